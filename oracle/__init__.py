@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for exact softmax attention -- test infrastructure only.
+
+Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; the product path never touches it.
+"""
+from .attention import (  # noqa: F401
+    attention_batched,
+    attention_bwd,
+    attention_from_scores,
+    combine_partials,
+    naive_attention,
+    scores,
+    split_kv_partials,
+    tiled_attention,
+)

@@ -1,0 +1,132 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module holds no attention arithmetic: it draws i.i.d. N(0, 1) values
+from counter-addressed NumPy PCG64 streams and rounds them to bfloat16
+(round to nearest, ties to even) when a config asks for bf16 inputs.  Both
+the fp64 oracle and the HIP path consume exactly the values produced here.
+
+Streams: one per (config, tensor, batch index, head index), seeded with the
+sequence [0xFA, config_id, tensor_id, b, h], so any single head can be
+regenerated without materialising the others.  Row samples use
+[0xFA, config_id, 99, salt].
+
+The workloads (sizes, causal flag, dtype) are the five attention problems
+the method is measured on:
+  1: B=1, H=1,  N=256,   d=64,  fp32, non-causal
+  2: B=1, H=16, N=2048,  d=64,  bf16, causal
+  3: B=8, H=32, N=8192,  d=128, bf16, causal   (the throughput workload)
+  4: B=1, H=16, N=32768, d=128, bf16, causal   (long context, batch 1)
+  5: B=2, H=16, N=4096,  d=128, bf16, causal   (forward plus backward)
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
+
+
+@dataclass(frozen=True)
+class Workload:
+    config_id: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+WORKLOADS = {
+    1: Workload(1, "single-head fp32 non-causal B1 H1 N256 d64", 1, 1, 256, 64, "f32", False),
+    2: Workload(2, "causal bf16 B1 H16 N2048 d64", 1, 16, 2048, 64, "bf16", True),
+    3: Workload(3, "causal bf16 B8 H32 N8192 d128", 8, 32, 8192, 128, "bf16", True),
+    4: Workload(4, "long-context causal bf16 B1 H16 N32768 d128", 1, 16, 32768, 128, "bf16", True),
+    5: Workload(5, "causal bf16 fwd+bwd B2 H16 N4096 d128", 2, 16, 4096, 128, "bf16", True),
+}
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Inputs are finite normal draws; no NaN handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> the exactly equal fp32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def head_stream(config_id: int, tensor: str, b: int, h: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64([0xFA, config_id, TENSOR_IDS[tensor], b, h]))
+
+
+def head_values(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dtype: str) -> np.ndarray:
+    """One head's (n, d) tensor as fp32 values (bf16-representable if dtype is bf16)."""
+    x = head_stream(config_id, tensor, b, h).standard_normal((n, d), dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bf16_round_bits(x))
+    return x
+
+
+def head_storage(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dtype: str) -> np.ndarray:
+    """One head's (n, d) tensor in storage form: uint16 bf16 bits or float32."""
+    x = head_stream(config_id, tensor, b, h).standard_normal((n, d), dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_round_bits(x)
+    return x
+
+
+def full_storage(config_id: int, tensor: str, B: int, H: int, N: int, d: int, dtype: str,
+                 threads: int = 8) -> np.ndarray:
+    """The whole [B][H][N][d] tensor in storage form (uint16 bf16 bits or float32)."""
+    out = np.empty((B, H, N, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        out[b, h] = head_storage(config_id, tensor, b, h, N, d, dtype)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
+
+
+def workload_storage(w: Workload, tensors=("q", "k", "v"), threads: int = 8) -> dict:
+    return {t: full_storage(w.config_id, t, w.B, w.H, w.N, w.d, w.dtype, threads) for t in tensors}
+
+
+def sample_rows(config_id: int, n: int, count: int, salt: int = 0, edge_block: int = 128) -> np.ndarray:
+    """Sorted query-row sample: `count` seeded rows plus the edge rows
+    {0, 1, edge_block - 1, edge_block, n - 1} (those inside 0..n-1)."""
+    rng = np.random.Generator(np.random.PCG64([0xFA, config_id, 99, salt]))
+    count = min(count, n)
+    picked = rng.choice(n, size=count, replace=False)
+    edges = [r for r in (0, 1, edge_block - 1, edge_block, n - 1) if 0 <= r < n]
+    return np.unique(np.concatenate([picked, np.array(edges, dtype=np.int64)]))
+
+
+def sample_heads(config_id: int, B: int, H: int, count: int) -> list:
+    """`count` distinct seeded (b, h) pairs."""
+    rng = np.random.Generator(np.random.PCG64([0xFA, config_id, 98]))
+    flat = rng.choice(B * H, size=min(count, B * H), replace=False)
+    return [divmod(int(x), H) for x in sorted(flat)]
+
+
+def random_values(seed: int, shape, dtype: str = "f32") -> np.ndarray:
+    """Free-form seeded N(0, 1) draws (fp32 values, bf16-rounded if asked)."""
+    x = np.random.Generator(np.random.PCG64([0xFA, 7, seed])).standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bf16_round_bits(x))
+    return x

@@ -1,0 +1,382 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each pin checks the oracle against something other than itself: a closed
+form, an invariant of softmax attention, a library routine (torch's fp64 CPU
+attention and autograd, scipy's logsumexp), brute force on tiny inputs, the
+page's own tiled-versus-naive experiment, or finite differences.  The
+mutation tests at the end plant plausible mistakes in copies of the naive
+oracle and check that at least one pin catches each of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from synthetic import random_values
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, shape):
+    return random_values(seed, shape).astype(np.float64)
+
+
+def qkv(seed, n, d, n_k=None):
+    n_k = n if n_k is None else n_k
+    return rnd(seed, (n, d)), rnd(seed + 1, (n_k, d)), rnd(seed + 2, (n_k, d))
+
+
+# ---------------------------------------------------------------- pins
+# Each pin takes an attention callable with the signature of
+# oracle.naive_attention and raises AssertionError when it is violated.
+
+
+def pin_rows_sum_to_one(attn):
+    for causal in (False, True):
+        q, k, v = qkv(10, 33, 8)
+        _, _, p = attn(q, k, v, causal, 0.7, return_p=True)
+        assert np.all(p >= 0)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-14
+
+
+def pin_scale_zero_means(attn):
+    """scale = 0 makes every visible score equal: O is the mean of the
+    visible V rows and L = log(#visible)."""
+    n, d = 17, 5
+    q, k, v = qkv(20, n, d)
+    o, lse = attn(q, k, v, False, 0.0)
+    assert np.max(np.abs(o - v.mean(axis=0)[None, :])) < 1e-14
+    assert np.max(np.abs(lse - math.log(n))) < 1e-14
+    o, lse = attn(q, k, v, True, 0.0)
+    prefix_mean = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.max(np.abs(o - prefix_mean)) < 1e-14
+    assert np.max(np.abs(lse - np.log(np.arange(1, n + 1)))) < 1e-14
+
+
+def pin_shift_invariance(attn):
+    """Adding c_i to every score of row i leaves O unchanged and shifts L by
+    c_i.  Realised by appending a column c_i / scale to Q and 1 to K."""
+    n, d, scale = 23, 6, 0.4
+    q, k, v = qkv(30, n, d)
+    c = rnd(33, (n,)) * 3.0
+    q2 = np.concatenate([q, (c / scale)[:, None]], axis=1)
+    k2 = np.concatenate([k, np.ones((n, 1))], axis=1)
+    for causal in (False, True):
+        o1, l1 = attn(q, k, v, causal, scale)
+        o2, l2 = attn(q2, k2, v, causal, scale)
+        assert np.max(np.abs(o1 - o2)) < 1e-12
+        assert np.max(np.abs((l1 + c) - l2)) < 1e-12
+
+
+def pin_causal_first_row(attn):
+    """Causal query 0 sees only key 0: O_0 = V_0 and L_0 = scale q_0 . k_0."""
+    q, k, v = qkv(40, 9, 4)
+    o, lse = attn(q, k, v, True, 0.3)
+    assert np.max(np.abs(o[0] - v[0])) < 1e-15
+    assert abs(lse[0] - 0.3 * float(q[0] @ k[0])) < 1e-14
+
+
+def pin_single_key(attn):
+    q, k, v = qkv(50, 1, 7)
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, 1.3)
+        assert np.max(np.abs(o - v)) < 1e-15
+        assert abs(lse[0] - 1.3 * float(q[0] @ k[0])) < 1e-14
+
+
+def pin_hardmax_limit(attn):
+    """With a huge scale and a unique largest score, softmax becomes one-hot
+    on the argmax: O_i = V_argmax, L_i = scale * max_j s_ij."""
+    n, d = 12, 4
+    q, k, v = qkv(60, n, d)
+    scale = 1e4
+    o, lse = attn(q, k, v, False, scale)
+    s = q @ k.T
+    am = np.argmax(s, axis=1)
+    assert np.max(np.abs(o - v[am])) < 1e-9
+    assert np.max(np.abs(lse - scale * s.max(axis=1))) < 1e-6
+
+
+def pin_permutation(attn):
+    """Non-causal: permuting the key/value rows together leaves O, L
+    unchanged; permuting query rows permutes O and L."""
+    n, d = 19, 5
+    q, k, v = qkv(70, n, d)
+    o, lse = attn(q, k, v, False, 0.5)
+    perm = np.random.default_rng(3).permutation(n)
+    o2, l2 = attn(q, k[perm], v[perm], False, 0.5)
+    assert np.max(np.abs(o - o2)) < 1e-13 and np.max(np.abs(lse - l2)) < 1e-13
+    o3, l3 = attn(q[perm], k, v, False, 0.5)
+    assert np.max(np.abs(o[perm] - o3)) < 1e-13 and np.max(np.abs(lse[perm] - l3)) < 1e-13
+
+
+def pin_lse_consistency(attn):
+    """exp(S_ij - L_i) = P_ij, with S the scaled masked scores."""
+    q, k, v = qkv(80, 15, 3)
+    for causal in (False, True):
+        _, lse, p = attn(q, k, v, causal, 0.9, return_p=True)
+        s = 0.9 * (q @ k.T)
+        if causal:
+            s = np.where(np.triu(np.ones_like(s, dtype=bool), 1), -np.inf, s)
+        assert np.max(np.abs(np.exp(s - lse[:, None]) - p)) < 1e-14
+        assert np.max(np.abs(lse - scipy.special.logsumexp(s, axis=1))) < 1e-13
+
+
+def pin_torch_sdpa(attn):
+    """Library cross-check: torch's math attention in fp64 on the CPU."""
+    for n, n_k, d, causal, scale in [(31, 31, 16, False, 0.25), (40, 40, 8, True, 0.35), (7, 29, 3, False, 1.1)]:
+        q, k, v = qkv(90 + n, n, d, n_k)
+        o, lse = attn(q, k, v, causal, scale)
+        tq, tk, tv = (torch.from_numpy(x)[None] for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)[0].numpy()
+        assert np.max(np.abs(o - ref)) < 1e-13
+        s = scale * (tq[0] @ tk[0].T)
+        if causal:
+            s = s.masked_fill(torch.triu(torch.ones_like(s, dtype=torch.bool), 1), -math.inf)
+        assert np.max(np.abs(lse - torch.logsumexp(s, dim=1).numpy())) < 1e-13
+
+
+def pin_brute_force(attn):
+    """Scalar loops with math.exp on a tiny problem, no arrays."""
+    n, d, scale = 5, 3, 0.8
+    q, k, v = qkv(100, n, d)
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, scale)
+        for i in range(n):
+            keys = range(i + 1) if causal else range(n)
+            w = {j: math.exp(scale * sum(q[i][c] * k[j][c] for c in range(d))) for j in keys}
+            z = sum(w.values())
+            for c in range(d):
+                assert abs(o[i][c] - sum(w[j] * v[j][c] for j in keys) / z) < 1e-14
+            assert abs(lse[i] - math.log(z)) < 1e-14
+
+
+PINS = [
+    pin_rows_sum_to_one,
+    pin_scale_zero_means,
+    pin_shift_invariance,
+    pin_causal_first_row,
+    pin_single_key,
+    pin_hardmax_limit,
+    pin_permutation,
+    pin_lse_consistency,
+    pin_torch_sdpa,
+    pin_brute_force,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_naive_oracle_pins(pin):
+    pin(oracle.naive_attention)
+
+
+def test_attention_from_scores_shift():
+    """The score-level entry point: S + c_i per row leaves P, O unchanged."""
+    s = rnd(110, (6, 9)) * 2
+    v = rnd(111, (9, 4))
+    c = rnd(112, (6,))
+    o1, l1, p1 = oracle.attention_from_scores(s, v, return_p=True)
+    o2, l2, p2 = oracle.attention_from_scores(s + c[:, None], v, return_p=True)
+    assert np.max(np.abs(p1 - p2)) < 1e-15
+    assert np.max(np.abs(o1 - o2)) < 1e-14
+    assert np.max(np.abs(l1 + c - l2)) < 1e-14
+    assert np.max(np.abs(p1 - scipy.special.softmax(s, axis=1))) < 1e-15
+
+
+def test_fully_masked_row_reading():
+    s = np.array([[-np.inf, -np.inf], [0.0, 1.0]])
+    o, lse = oracle.attention_from_scores(s, np.ones((2, 3)))
+    assert np.all(o[0] == 0) and lse[0] == -np.inf
+    assert np.allclose(o[1], 1.0)
+
+
+# ---------------------------------------------------------------- tiled
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 257])
+@pytest.mark.parametrize("d", [1, 8, 64])
+@pytest.mark.parametrize("blocks", [(1, 1), (7, 5), (64, 64), (128, 32)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_matches_naive(n, d, blocks, causal):
+    q, k, v = qkv(200 + n + d, n, d)
+    scale = 1.0 / math.sqrt(d)
+    o1, l1 = oracle.naive_attention(q, k, v, causal, scale)
+    o2, l2 = oracle.tiled_attention(q, k, v, causal, scale, *blocks)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+    assert np.max(np.abs(l1 - l2)) <= 1e-12
+
+
+def test_tiled_page_experiment():
+    """The page's check: blocked versus textbook at 2048x64, blocks 128,
+    causal, scale 1/sqrt(d), prints a max-abs difference of about 1e-15."""
+    with open(os.path.join(GOLDEN, "page_tiled_vs_naive.json")) as f:
+        g = json.load(f)
+    n, d = g["N"], g["d"]
+    q, k, v = qkv(300, n, d)
+    scale = 1.0 / math.sqrt(d)
+    o1, _ = oracle.naive_attention(q, k, v, g["causal"], scale)
+    o2, _ = oracle.tiled_attention(q, k, v, g["causal"], scale, g["block_q"], g["block_k"])
+    diff = float(np.max(np.abs(o1 - o2)))
+    # same order of magnitude as the printed value (rounding-order noise only)
+    assert diff < 100 * g["printed_max_abs_diff"]
+
+
+def test_tiled_hardmax_and_large_scores():
+    """Scores far beyond exp's range: the running max keeps every exp finite."""
+    q, k, v = qkv(310, 50, 4)
+    o1, l1 = oracle.naive_attention(q, k, v, True, 300.0)
+    o2, l2 = oracle.tiled_attention(q, k, v, True, 300.0, 8, 3)
+    assert np.all(np.isfinite(o2)) and np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(l1 - l2)) / np.max(np.abs(l1)) < 1e-13
+
+
+# ---------------------------------------------------------------- split-K merge
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_partials_combine(causal):
+    n, d = 37, 6
+    q, k, v = qkv(400, n, d)
+    o_ref, l_ref = oracle.naive_attention(q, k, v, causal, 0.45)
+    for bounds in ([(0, n)], [(0, 10), (10, 11), (11, n)], [(j, min(j + 4, n)) for j in range(0, n, 4)]):
+        m, l, o = oracle.split_kv_partials(q, k, v, causal, 0.45, bounds)
+        o2, l2 = oracle.combine_partials(m, l, o)
+        assert np.max(np.abs(o2 - o_ref)) < 1e-13
+        assert np.max(np.abs(l2 - l_ref)) < 1e-13
+
+
+def test_combine_two_halves_by_hand():
+    """Two partials with maxima 0 and 2: weights exp(-2) and 1."""
+    m = np.array([[0.0], [2.0]])
+    l = np.array([[3.0], [1.5]])
+    o = np.array([[[3.0]], [[6.0]]])
+    out, lse = oracle.combine_partials(m, l, o)
+    w0 = math.exp(-2.0)
+    assert abs(out[0, 0] - (w0 * 3.0 + 6.0) / (w0 * 3.0 + 1.5)) < 1e-15
+    assert abs(lse[0] - (2.0 + math.log(w0 * 3.0 + 1.5))) < 1e-15
+
+
+# ---------------------------------------------------------------- backward
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_finite_differences(causal):
+    """Central differences of f = <O, dO> at N=16, d=8 (fp64, step 1e-6)."""
+    n, d = 16, 8
+    q, k, v = qkv(500, n, d)
+    do = rnd(504, (n, d))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+
+    def f(qq, kk, vv):
+        o, _ = oracle.naive_attention(qq, kk, vv, causal, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        num = np.zeros_like(grad)
+        for i in range(n):
+            for c in range(d):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][i, c] += h
+                fp = f(*args)
+                args[which][i, c] -= 2 * h
+                fm = f(*args)
+                num[i, c] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - grad)) < 1e-7
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_torch_autograd(causal):
+    n, d = 24, 8
+    q, k, v = qkv(510, n, d)
+    do = rnd(514, (n, d))
+    scale = 0.3
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], is_causal=causal, scale=scale)[0]
+    out.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_invariants(causal):
+    """sum_j dV_j = sum_i dO_i (P rows sum to 1) and sum_j dK_j = 0
+    (rows of dS sum to 0)."""
+    n, d = 21, 5
+    q, k, v = qkv(520, n, d)
+    do = rnd(524, (n, d))
+    _, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 0.6)
+    assert np.max(np.abs(dv.sum(axis=0) - do.sum(axis=0))) < 1e-13
+    assert np.max(np.abs(dk.sum(axis=0))) < 1e-13
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+
+def _mutant(kind):
+    """A copy of the naive oracle with one planted mistake."""
+
+    def attn(q, k, v, causal, scale, rows=None, return_p=False):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+        sc = 1.0 if kind == "scale_dropped" else scale
+        s = sc * ((k @ q.T)[rows] if kind == "transposed_scores" and q.shape[0] == k.shape[0] else q[rows] @ k.T)
+        if causal:
+            kj = np.arange(k.shape[0])[None, :]
+            ri = rows[:, None]
+            bad = {"mask_flipped": kj < ri, "mask_off_by_one": kj >= ri}.get(kind, kj > ri)
+            s = np.where(bad, -np.inf, s)
+        m = np.max(s, axis=1, keepdims=True)
+        if kind == "max_not_subtracted":
+            m = np.zeros_like(m)
+        m = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(m - s) if kind == "exp_sign" else np.exp(s - m)
+        e = np.where(np.isnan(e), 0.0, e)
+        lsum = e.sum(axis=1, keepdims=True)
+        p = e if kind == "no_normalisation" else e / lsum
+        o = (p.T @ v) if kind == "pv_transposed" and p.shape[0] == p.shape[1] else p @ v
+        lse = m[:, 0] + (np.log2(lsum[:, 0]) if kind == "lse_log2" else np.log(lsum[:, 0]))
+        return (o, lse, p) if return_p else (o, lse)
+
+    return attn
+
+
+MUTANTS = [
+    "scale_dropped",
+    "transposed_scores",
+    "mask_flipped",
+    "mask_off_by_one",
+    "max_not_subtracted",
+    "exp_sign",
+    "no_normalisation",
+    "pv_transposed",
+    "lse_log2",
+]
+
+
+def test_unmutated_copy_passes_pins():
+    attn = _mutant("none")
+    for pin in PINS:
+        pin(attn)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_pins_catch_planted_mistake(kind):
+    attn = _mutant(kind)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(attn)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {kind}"
