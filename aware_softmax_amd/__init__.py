@@ -1,0 +1,135 @@
+"""Python binding of libfa.so, the gfx950 fused exact-attention library.
+
+Argument marshalling only: every step of the forward runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  torch supplies device
+memory and the current stream.  There is no fallback: if libfa.so is
+missing or fails to load, importing this package raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FaError",
+    "fwd",
+    "fa_fwd",
+    "tile_config",
+    "version",
+    "status_string",
+    "library",
+    "LIB_PATH",
+    "DTYPE_F32",
+    "DTYPE_BF16",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+FA_OK = 0
+
+
+class FaError(RuntimeError):
+    """A nonzero fa_status_t from the C library."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(message)
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m aware_softmax_amd.build` "
+            "(there is no non-HIP fallback)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_fwd.restype = ci
+    lib.fa_status_string.argtypes = [ci]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd_tile.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    lib.fa_fwd_tile.restype = ci
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    return lib
+
+
+_LIB = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _LIB
+
+
+def status_string(code: int) -> str:
+    return _LIB.fa_status_string(int(code)).decode()
+
+
+def version() -> str:
+    return _LIB.fa_version().decode()
+
+
+def _check(code: int) -> None:
+    if code != FA_OK:
+        raise FaError(code, status_string(code))
+
+
+def tile_config(d: int, dtype: int) -> tuple:
+    """(block_q, block_k, waves) that fa_fwd uses for head dim d and dtype."""
+    bq, bk, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_LIB.fa_fwd_tile(int(d), int(dtype), ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(w)))
+    return bq.value, bk.value, w.value
+
+
+def fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, scale, dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses; returns
+    the fa_status_t code."""
+    return _LIB.fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(N), int(d),
+                       int(bool(causal)), float(scale), int(dtype), stream)
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, stream=None):
+    """O, L = attention forward of [B, H, N, d] device tensors (bf16 or fp32).
+
+    Returns (o, lse): o like q, lse float32 [B, H, N] (natural-log
+    logsumexp of each scaled, masked score row).  out / lse may be passed to
+    reuse buffers.  Runs on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dtype = DTYPE_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}; use torch.bfloat16 or torch.float32")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q in dtype and shape")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  B, H, N, d, causal, scale, dtype, stream.cuda_stream))
+    return out, lse

@@ -1,0 +1,97 @@
+// C-ABI entry points of libfa.so: argument validation, kernel selection,
+// launch on the caller's stream.  Declarations and contracts: include/fa.h.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+size_t elem_size(fa_dtype_t dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
+
+fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N and d must be positive and the sizes must fit";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+    case FA_ERR_UNSUPPORTED_HEADDIM: return "FA_ERR_UNSUPPORTED_HEADDIM: d must be 64 or 128";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte and lse 4-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP kernel launch failed";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o and lse must not overlap the inputs or each other";
+  }
+  return "unknown fa_status_t";
+}
+
+const char* fa_version(void) { return "0.1.0 gfx950"; }
+
+fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves) {
+  if (!block_q || !block_k || !waves) return FA_ERR_NULL;
+  const fa_status_t st = check_dtype_headdim(d, dtype);
+  if (st != FA_OK) return st;
+  const fa::TileConfig t = dtype == FA_DTYPE_BF16 ? fa::bf16_tile(d) : fa::f32_tile(d);
+  *block_q = t.block_q;
+  *block_k = t.block_k;
+  *waves = t.waves;
+  return FA_OK;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_SHAPE;
+  const fa_status_t st = check_dtype_headdim(d, dtype);
+  if (st != FA_OK) return st;
+  // Sizes: element offsets are 64-bit in the kernels; the grid is one int.
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t elems = bh * N * d;
+  if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const fa::TileConfig tile = dtype == FA_DTYPE_BF16 ? fa::bf16_tile(d) : fa::f32_tile(d);
+  const int64_t nqb = ((int64_t)N + tile.block_q - 1) / tile.block_q;
+  if (bh * nqb > INT_MAX) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t tbytes = (size_t)elems * elem_size(dtype);
+  const size_t lbytes = (size_t)bh * N * sizeof(float);
+  if (ranges_overlap(o, tbytes, q, tbytes) || ranges_overlap(o, tbytes, k, tbytes) ||
+      ranges_overlap(o, tbytes, v, tbytes) || ranges_overlap(o, tbytes, lse, lbytes) ||
+      ranges_overlap(lse, lbytes, q, tbytes) || ranges_overlap(lse, lbytes, k, tbytes) ||
+      ranges_overlap(lse, lbytes, v, tbytes))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)bh;
+  p.N = N;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,255 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+
+A step is one fa_fwd over the whole causal bf16 workload B=8, H=32,
+N=8192, d=128 (scale 1/sqrt(d)), inputs resident in HBM before timing.
+Prints one JSON line with the throughput in TFLOP/s (2*N^2*d FLOP per head
+for the causal mask, i.e. 4*N^2*d halved), the roofline of the kernel
+against the dense bf16 MFMA peak, and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+--profile-run: the run used under rocprofv3 counters: one 1 GiB device
+copy (the byte-count calibration kernel) followed by --steps launches.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "aware_softmax_amd", "csrc", "fa_fwd_bf16.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_B8H32N8192d128_counters.txt")
+METRIC = "causal bf16 attention fwd TFLOPS at N=8k,d=128; % of MI355X MFMA peak"
+
+
+def attention_flops(B, H, N, d, causal):
+    """Algorithmic FLOPs: 4*N^2*d per head (two N x N x d products), halved
+    for the causal mask."""
+    f = 4.0 * N * N * d * B * H
+    return f / 2 if causal else f
+
+
+def causal_row_flops(rows, d):
+    """FLOPs of the causal rows actually visible: row i sees i + 1 keys."""
+    return float(sum(4.0 * d * (int(i) + 1) for i in rows))
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if
+    the summary is missing or the kernel source changed since."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(w, threads=16):
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    out = []
+    for t in ("q", "k", "v"):
+        st = synthetic.full_storage(w.config_id, t, w.B, w.H, w.N, w.d, w.dtype, threads=threads)
+        out.append(torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).to(dev))
+        del st
+    return out
+
+
+def time_launches(fa, q, k, v, o, lse, causal, scale, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for i in range(steps):
+        starts[i].record()
+        fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+        ends[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return t_begin.elapsed_time(t_end) / steps, sum(per) / len(per), min(per), max(per), wall
+
+
+def cpu_baseline(w, budget_s=12.0, rows_per_head=512):
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    workload: seeded (b, h) heads, 512 seeded query rows each, until the
+    time budget is spent (at least one head)."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = synthetic.sample_heads(w.config_id, w.B, w.H, w.B * w.H)
+    rows = synthetic.sample_rows(w.config_id, w.N, rows_per_head)
+    flops = 0.0
+    spent = 0.0
+    done = 0
+    for b, h in heads:
+        q, k, v = (synthetic.head_values(w.config_id, t, b, h, w.N, w.d, w.dtype) for t in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oracle.naive_attention(q, k, v, w.causal, w.scale, rows=rows)
+        spent += time.perf_counter() - t0
+        flops += causal_row_flops(rows, w.d) if w.causal else 4.0 * w.d * w.N * len(rows)
+        done += 1
+        if spent >= budget_s:
+            break
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} seeded heads x {len(rows)} seeded query rows of B={w.B} H={w.H} N={w.N} "
+                  f"d={w.d} causal (naive fp64 NumPy, materialised score rows); {spent:.1f} s",
+        "seconds": spent,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--extra", action="store_true", help="also time the other workloads and non-causal")
+    ap.add_argument("--profile-run", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the attention forward is sharded over heads with no "
+              f"communication, and this build runs on a single MI355X; --gpus {args.gpus} is not "
+              f"supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import aware_softmax_amd as fa
+    import synthetic
+
+    w = synthetic.WORKLOADS[3]
+    q, k, v = make_inputs(w)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=q.device)
+
+    if args.profile_run:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=q.device)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        print(f"profile-run: 1 GiB copy + {args.steps} fa_fwd launches done", flush=True)
+        return
+
+    ms_step, ms_kernel, ms_min, ms_max, wall = time_launches(
+        fa, q, k, v, o, lse, True, w.scale, args.steps, args.warmup)
+    flops = attention_flops(w.B, w.H, w.N, w.d, True)
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    bq, bk, waves = fa.tile_config(w.d, fa.DTYPE_BF16)
+    traffic = read_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal bf16 attention forward B=8 H=32 N=8192 d=128 scale=1/sqrt(d)",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+            "tile": {"block_q": bq, "block_k": bk, "waves": waves},
+            "inputs": "i.i.d. N(0,1) fp32 rounded to bf16, seeded per head",
+        },
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": {"mean": round(ms_kernel, 4), "min": round(ms_min, 4), "max": round(ms_max, 4)},
+            "flops_per_launch": flops,
+        },
+    }
+    if args.extra:
+        extra = {}
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+        for cid in (2, 4, 5):
+            ww = synthetic.WORKLOADS[cid]
+            qq, kk, vv = make_inputs(ww)
+            oo = torch.empty_like(qq)
+            ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
+            ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, True, ww.scale, 20, 3)
+            f = attention_flops(ww.B, ww.H, ww.N, ww.d, True)
+            extra[ww.name] = {"ms": round(msk, 4), "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2)}
+            if cid == 2:
+                pass
+            del qq, kk, vv, oo, ll
+            torch.cuda.empty_cache()
+        qq, kk, vv = make_inputs(w)
+        oo = torch.empty_like(qq)
+        ll = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=qq.device)
+        ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, False, w.scale, 10, 2)
+        f = attention_flops(w.B, w.H, w.N, w.d, False)
+        extra["non-causal bf16 B8 H32 N8192 d128"] = {
+            "ms": round(msk, 4), "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2),
+            "causal_speedup_time_ratio": round(msk / ms_kernel, 3)}
+        result["other_workloads"] = extra
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

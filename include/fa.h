@@ -1,0 +1,101 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention library (libfa.so, gfx950).
+ *
+ * The library computes, for every (batch b, head h),
+ *     O = softmax(scale * Q K^T + mask) V     and     L = rowwise logsumexp
+ * with the FlashAttention-2 forward: tiled over query blocks, keys and
+ * values streamed through on-chip memory, running max m, running sum l and
+ * an unnormalised accumulator rescaled by alpha = exp(m - m'), one division
+ * by l at the end, and the N x N score matrix never written to memory.
+ * Sources (page title and section):
+ *   "FlashAttention-2: Why the Attention Bottleneck Wasn't Where Everyone
+ *    Was Looking" -- "The hook" (the computed quantity), "FA2 change #1"
+ *    (deferred division, L = m + log l), "FA2 change #2" (parallel over
+ *    query blocks), "The causal masking freebie" (block classification);
+ *   "FlashAttention: Move Less, Not Compute Less" -- "Tiling Is Easy;
+ *    Softmax Couples the Entire Row" (online recurrences);
+ *   "PidokuInfra 10 -- FlashAttention" -- section 4 (causal: query i sees
+ *    keys 0..i; scale 1/sqrt(d) applied to QK^T before the softmax).
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, o are device pointers to contiguous row-major [B][H][N][d]
+ *     tensors of the given dtype; lse is a device pointer to a contiguous
+ *     [B][H][N] float32 tensor for both dtypes.
+ *   - L is the natural-log logsumexp of the scaled, masked score row
+ *     (L_i = m_i + ln l_i).
+ *   - The causal mask is top-left aligned: query i attends to keys 0..i.
+ *   - The caller owns all memory.  Nothing is allocated or freed, no state
+ *     is kept between calls (calls are thread-safe and re-entrant), and no
+ *     call synchronises: work is enqueued on `stream` (0 = the null stream)
+ *     and the call returns.  Device-side faults surface at the caller's
+ *     next synchronisation.
+ *   - Arguments are validated before any HIP call; on a nonzero status no
+ *     work has been enqueued.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* float32 in, float32 out, fp32 arithmetic */
+  FA_DTYPE_BF16 = 1  /* bfloat16 in/out, fp32 accumulation and softmax */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,                 /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,                /* B, H, N or d <= 0, or sizes overflow */
+  FA_ERR_DTYPE = 3,                /* dtype is not a fa_dtype_t value */
+  FA_ERR_UNSUPPORTED_HEADDIM = 4,  /* d is not 64 or 128 */
+  FA_ERR_ALIGN = 5,                /* q/k/v/o not 16-byte or lse not 4-byte aligned */
+  FA_ERR_SCALE = 6,                /* scale is NaN or infinite */
+  FA_ERR_HIP = 7,                  /* the HIP launch reported an error */
+  FA_ERR_ALIAS = 8                 /* o or lse overlaps an input or each other */
+} fa_status_t;
+
+/*
+ * fa_fwd -- attention forward for all B*H heads.
+ *
+ *   q, k, v  [in]  device, [B][H][N][d] of dtype, 16-byte aligned.
+ *   o        [out] device, [B][H][N][d] of dtype, 16-byte aligned; must not
+ *                  overlap q, k, v or lse.
+ *   lse      [out] device, [B][H][N] float32, 4-byte aligned.
+ *   B, H, N  sizes (> 0); any N >= 1 (ragged tails are masked).
+ *   d        head dimension: 64 or 128.
+ *   causal   0: every query sees all N keys; nonzero: query i sees 0..i.
+ *   scale    multiplies Q K^T before mask and softmax (finite; 1/sqrt(d)
+ *            in the usual case; 0 and negative values are allowed).
+ *   dtype    FA_DTYPE_BF16 (MFMA path) or FA_DTYPE_F32 (fp32 path).
+ *   stream   HIP stream the kernel is enqueued on.
+ * Returns FA_OK or the first failed check (see fa_status_t).  The output
+ * is deterministic: the same inputs give bitwise identical o and lse.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   fa_dtype_t dtype, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fa_status_string(fa_status_t status);
+
+/*
+ * fa_fwd_tile -- the tile configuration fa_fwd uses for (d, dtype):
+ * query rows per workgroup, keys per streamed tile and wavefronts per
+ * workgroup.  Host-only; makes no HIP call.  Returns FA_OK or
+ * FA_ERR_NULL / FA_ERR_DTYPE / FA_ERR_UNSUPPORTED_HEADDIM.
+ */
+fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves);
+
+/* Library version string, e.g. "0.1.0 gfx950" (static storage). */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,210 @@
+"""GPU parity of fa_fwd against the fp64 oracle (element by element).
+
+Every case draws seeded inputs from synthetic.py, runs the HIP path through
+the C ABI (aware_softmax_amd.fwd -> fa_fwd) and compares O and L with
+oracle.naive_attention on the same bf16/fp32 values upcast to fp64.
+Tolerances (max-abs over every checked element): fp32 1e-5 on O and L;
+bf16 2e-2 on O and 1e-2 on L (fp32 accumulation).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2)}
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import aware_softmax_amd
+
+    return aware_softmax_amd
+
+
+def to_device(storage, dtype):
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(storage.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(storage).cuda()
+
+
+def values(storage, dtype):
+    if dtype == "bf16":
+        return synthetic.bf16_bits_to_f32(storage)
+    return storage
+
+
+def run_case(fa, config_id, B, H, N, d, dtype, causal, scale=None, heads=None, rows=None,
+             tensors=None):
+    """Runs fa.fwd and returns (max |dO|, max |dL|) against the oracle."""
+    import torch
+
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if tensors is None:
+        tensors = {t: synthetic.full_storage(config_id, t, B, H, N, d, dtype) for t in ("q", "k", "v")}
+    q, k, v = (to_device(tensors[t], dtype) for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    err_o = err_l = 0.0
+    for b, h in heads:
+        ob = o[b, h].float().cpu().numpy().astype(np.float64)
+        lb = lse[b, h].cpu().numpy().astype(np.float64)
+        ref_o, ref_l = oracle.naive_attention(values(tensors["q"][b, h], dtype), values(tensors["k"][b, h], dtype),
+                                              values(tensors["v"][b, h], dtype), causal, scale, rows=rows)
+        sel = slice(None) if rows is None else rows
+        err_o = max(err_o, float(np.max(np.abs(ob[sel] - ref_o))))
+        err_l = max(err_l, float(np.max(np.abs(lb[sel] - ref_l))))
+    return err_o, err_l
+
+
+def assert_close(errs, dtype, scale_factor=1.0):
+    """scale_factor widens the fp32 bound for scores larger than the
+    workloads' scale = 1/sqrt(d) gives: an fp32 score carries an absolute
+    rounding error proportional to |scale| * |q| * |k| ~ |scale| * sqrt(d)
+    (times d unit roundoffs), and O moves by at most that error times
+    max|v - O|.  At scale = 1/sqrt(d) the factor is 1."""
+    to, tl = TOL[dtype]
+    if dtype == "f32":
+        to, tl = to * scale_factor, tl * scale_factor
+    assert errs[0] <= to, f"max |O - oracle| = {errs[0]:.3e} > {to}"
+    assert errs[1] <= tl, f"max |L - oracle| = {errs[1]:.3e} > {tl}"
+
+
+# ------------------------------------------------------------ the five workloads
+
+
+def test_workload1_fp32_noncausal(fa):
+    w = synthetic.WORKLOADS[1]
+    assert_close(run_case(fa, 1, w.B, w.H, w.N, w.d, w.dtype, w.causal), w.dtype)
+
+
+def test_workload2_bf16_causal_d64(fa):
+    w = synthetic.WORKLOADS[2]
+    assert_close(run_case(fa, 2, w.B, w.H, w.N, w.d, w.dtype, w.causal), w.dtype)
+
+
+def test_workload3_sampled(fa):
+    """B=8, H=32, N=8192, d=128 causal: 4 seeded heads x 512 seeded rows
+    (plus edge rows), in the launch configuration the bench times."""
+    w = synthetic.WORKLOADS[3]
+    heads = synthetic.sample_heads(3, w.B, w.H, 4)
+    rows = synthetic.sample_rows(3, w.N, 512)
+    assert_close(run_case(fa, 3, w.B, w.H, w.N, w.d, w.dtype, w.causal, heads=heads, rows=rows), w.dtype)
+
+
+def test_workload4_long_context_sampled(fa):
+    """B=1, H=16, N=32768, d=128 causal: 256 seeded rows of every head."""
+    w = synthetic.WORKLOADS[4]
+    rows = synthetic.sample_rows(4, w.N, 256)
+    assert_close(run_case(fa, 4, w.B, w.H, w.N, w.d, w.dtype, w.causal, rows=rows), w.dtype)
+
+
+def test_workload5_forward_all_rows(fa):
+    w = synthetic.WORKLOADS[5]
+    assert_close(run_case(fa, 5, w.B, w.H, w.N, w.d, w.dtype, w.causal), w.dtype)
+
+
+# ------------------------------------------------------------ shapes and edges
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 127, 128, 129, 200, 333, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_bf16(fa, n, d, causal):
+    cid = 1000 + n * 4 + (d == 128) * 2 + causal
+    assert_close(run_case(fa, cid, 2, 3, n, d, "bf16", causal), "bf16")
+
+
+@pytest.mark.parametrize("n", [1, 5, 64, 100, 257])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_fp32(fa, n, d, causal):
+    cid = 3000 + n * 4 + (d == 128) * 2 + causal
+    assert_close(run_case(fa, cid, 1, 2, n, d, "f32", causal), "f32")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.2, 0.9, 3.0])
+def test_other_scales(fa, dtype, scale):
+    d = 64
+    assert_close(run_case(fa, 4000 + int(scale * 10), 1, 2, 300, d, dtype, True, scale=scale), dtype,
+                 scale_factor=max(1.0, abs(scale) * math.sqrt(d)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_gives_prefix_means(fa, dtype, causal):
+    """Closed form, no oracle: scale 0 makes O the mean of the visible V
+    rows and L = log(#visible)."""
+    import torch
+
+    n, d = 257, 128
+    st = {t: synthetic.full_storage(5000, t, 1, 2, n, d, dtype) for t in ("q", "k", "v")}
+    q, k, v = (to_device(st[t], dtype) for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=0.0)
+    torch.cuda.synchronize()
+    vv = values(st["v"], dtype).astype(np.float64)
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    ref = np.cumsum(vv, axis=2) / cnt[None, None, :, None] if causal else np.repeat(
+        vv.mean(axis=2, keepdims=True), n, axis=2)
+    tol_o = 2e-2 if dtype == "bf16" else 1e-5
+    assert np.max(np.abs(o.float().cpu().numpy() - ref)) <= tol_o
+    assert np.max(np.abs(lse.cpu().numpy() - np.log(cnt)[None, None, :])) <= 1e-5
+
+
+def test_v_all_ones(fa):
+    """V = 1 gives O = 1 exactly up to the bf16 rounding of P (2^-8)."""
+    import torch
+
+    n, d = 1000, 128
+    st = {t: synthetic.full_storage(5100, t, 1, 4, n, d, "bf16") for t in ("q", "k")}
+    q, k = (to_device(st[t], "bf16") for t in ("q", "k"))
+    v = torch.ones_like(q)
+    o, _ = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert float((o.float() - 1.0).abs().max()) <= 2.0 ** -8
+
+
+def test_deterministic_and_stream(fa):
+    """No atomics in the forward: two runs are bitwise identical, also on a
+    side stream with caller-provided output buffers."""
+    import torch
+
+    st = {t: synthetic.full_storage(5200, t, 2, 4, 777, 128, "bf16") for t in ("q", "k", "v")}
+    q, k, v = (to_device(st[t], "bf16") for t in ("q", "k", "v"))
+    o1, l1 = fa.fwd(q, k, v, causal=True)
+    s = torch.cuda.Stream()
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fa.fwd(q, k, v, causal=True, out=o2, lse=l2, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_outputs_untouched_outside_bounds(fa):
+    """The kernel writes exactly B*H*N rows: a sentinel past the end of the
+    output buffers survives."""
+    import torch
+
+    B, H, n, d = 1, 3, 129, 64
+    st = {t: synthetic.full_storage(5300, t, B, H, n, d, "bf16") for t in ("q", "k", "v")}
+    q, k, v = (to_device(st[t], "bf16") for t in ("q", "k", "v"))
+    obuf = torch.full((B * H * n * d + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((B * H * n + 16,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[: B * H * n * d].view(B, H, n, d)
+    lse = lbuf[: B * H * n].view(B, H, n)
+    fa.fwd(q, k, v, causal=False, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[B * H * n * d:] == 7.0) and torch.all(lbuf[B * H * n:] == 7.0)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
