@@ -22,6 +22,10 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
+# Per-source flags.  The bf16 kernels never see NaN scores from finite
+# inputs; without NaN semantics fmaxf needs no quieting of its operands,
+# which keeps the row max at one v_max3 per two scores.
+SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -64,7 +68,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

@@ -60,7 +60,8 @@ def test_status_strings(fa):
 
 
 def test_tile_config(fa):
-    assert fa.tile_config(128, fa.DTYPE_BF16) == (128, 64, 4)
+    bq, bk, w = fa.tile_config(128, fa.DTYPE_BF16)
+    assert bk == 64 and bq == 32 * w and w in (4, 8)
     assert fa.tile_config(64, fa.DTYPE_BF16)[0] > 0
     assert fa.tile_config(64, fa.DTYPE_F32)[0] > 0
     with pytest.raises(fa.FaError) as e:
