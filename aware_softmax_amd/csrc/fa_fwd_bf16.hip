@@ -17,7 +17,7 @@
 //     on MFMA; one reciprocal of l per row at the end, L = ln2*(m + log2 l);
 //   * tiles entirely above a wave's diagonal are never computed.
 //
-// MI355X mapping:
+// MI355X mapping (both kernels):
 //   * scores are computed transposed (keys x queries) with
 //     v_mfma_f32_32x32x16_bf16, so each lane holds 32 scores of ONE query:
 //     row max and row sum are in-lane plus one permlane32 swap;
@@ -27,15 +27,23 @@
 //   * V^T operands come from the row-major V tile through ds_read_b64_tr_b16
 //     (the gfx950 transposing LDS read), so V is stored in LDS as it sits in
 //     HBM;
-//   * K/V tiles are double-buffered in LDS, next tile's global loads are in
-//     flight while the current tile computes; LDS rows are padded so the
-//     MFMA operand reads are bank-conflict free;
 //   * exp is the hardware exp2 with scale*log2(e) folded into one FMA.
+// Two kernels:
+//   * d = 64: 4 waves, 128 query rows per workgroup, K/V tiles staged
+//     through registers into padded, double-buffered LDS rows;
+//   * d = 128 ("duo"): 8 waves (two per SIMD), 256 query rows, K/V tiles
+//     copied HBM -> LDS by LDS-DMA into XOR-swizzled rings, every MFMA
+//     followed by a slot of softmax VALU work, the two waves of a SIMD
+//     staggered by half an iteration, lazy rescaling of O.
 #include <math.h>
+#include <stdlib.h>
 
 #include "fa_internal.h"
 #include "fa_schedule.h"
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 namespace fa {
 namespace {
@@ -91,12 +99,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-__device__ inline bf16x8 lds_read_b128(unsigned addr) { return *(const lds_bf16x8*)(uintptr_t)addr; }
-__device__ inline bf16x8 lds_read_vt(unsigned addr, unsigned addr8) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr8);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Offset, within a 64-key tile, of score i of a lane (i = 16*kb + r for the
@@ -342,70 +344,194 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant: 8 waves per workgroup (two per SIMD), 256 query rows.
-//
-// Each wave alternates an MFMA phase M_j = {O^T += V_{j-1}^T P_{j-1}^T;
-// S_j^T = K_j Q^T} and a softmax phase S_j (mask, max, alpha, exp, row sum,
-// O rescale, pack P_j to bf16).  The two waves that share a SIMD run one
-// phase apart (workgroup barriers separate the phases), so while one issues
-// MFMAs the other runs the exp/max/sum VALU work: the matrix unit is kept
-// busy while softmax runs ("FlashAttention-3" pipelining principle in
-// "FlashAttention: Move Less, Not Compute Less", "FA1 to FA3", rebuilt for
-// CDNA4 wave scheduling instead of Hopper warpgroups).  K/V tiles rotate
-// through three LDS stages; a tile is fetched into registers two phases
-// before it is stored to LDS.
-// Compile-time scheduling pattern for a run of N MFMAs whose operand
-// fragment f needs 2 LDS reads if f < NV, else 1: the first LEAD fragments
-// are read up front, then each MFMA is followed by the reads of the
-// fragment LEAD steps later (instruction-group masks: 0x008 MFMA, 0x100 DS
-// read).
-template <int F, int LEAD, int NV, int N>
-struct SchedPrologue {
-  static __device__ __forceinline__ void run() {
-    if constexpr (F < LEAD && F < N) {
-      __builtin_amdgcn_sched_group_barrier(0x100, F < NV ? 2 : 1, 0);
-      SchedPrologue<F + 1, LEAD, NV, N>::run();
-    }
-  }
-};
-template <int I, int LEAD, int NV, int N>
-struct SchedSteady {
-  static __device__ __forceinline__ void run() {
-    if constexpr (I < N) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if constexpr (I + LEAD < N) __builtin_amdgcn_sched_group_barrier(0x100, I + LEAD < NV ? 2 : 1, 0);
-      SchedSteady<I + 1, LEAD, NV, N>::run();
-    }
-  }
-};
-template <int LEAD, int NV, int N>
-__device__ __forceinline__ void sched_mfma_run() {
-  SchedPrologue<0, LEAD, NV, N>::run();
-  SchedSteady<0, LEAD, NV, N>::run();
+// Helpers of the d = 128 kernel.
+
+constexpr float kRaise = 8.f;  // reference-max slack, log2 units (P <= 2^8)
+
+// Calls fn(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
+template <class Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, I...>) {
+  (fn(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
 }
 
-namespace pp {
+// One V^T fragment (two transposing 8-byte reads) or K fragment (one
+// 16-byte read) by inline asm, so completion is tracked only by the
+// explicit waits below (hipcc's own wait insertion drops to lgkmcnt(0)
+// while LDS-DMA loads are in flight).
+template <int OFF_LO, int OFF_HI>
+__device__ __forceinline__ void read_v(s16x4& lo, s16x4& hi, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(OFF_LO));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(OFF_HI));
+}
+template <int OFF>
+__device__ __forceinline__ void read_k(bf16x8& f, unsigned addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+
+// Online softmax of one unmasked 32-row block split into 32 slots, one per
+// MFMA.  Inputs of every slot were produced at least one slot earlier, so a
+// slot issues without waiting on its own results:
+//   0-3   partial row max over 8 scores each
+//   4     row max across the lane pair (permlane32 swap)
+//   5     reference max m (raised only by more than kRaise), alpha
+//   6-21  t = s*c - m for score pair k = slot - 6
+//   7-22  p = 2^t for pair slot - 7
+//   8-23  pack pair slot - 8 to bf16, add to a partial row sum
+//   24-25 row sum l = alpha*l + sum
+struct Softmax {
+  float mx[4];
+  float mrow;
+  float m_use, alpha;
+  float t[2], p[2];
+  float ps[4];
+  unsigned w[16];
+};
+
+template <int K>
+__device__ __forceinline__ void softmax_slot(Softmax& st, const f32x16 (&s)[2], float c, float& m_run,
+                                             float& l_part) {
+  auto sv = [&](int i) { return s[i >> 4][i & 15]; };
+  if constexpr (K < 4) {
+    st.mx[K] = fmaxf(fmaxf(fmaxf(sv(8 * K), sv(8 * K + 1)), fmaxf(sv(8 * K + 2), sv(8 * K + 3))),
+                     fmaxf(fmaxf(sv(8 * K + 4), sv(8 * K + 5)), fmaxf(sv(8 * K + 6), sv(8 * K + 7))));
+    asm volatile("" ::"v"(st.mx[K]));
+  } else if constexpr (K == 4) {
+    st.mrow = swap_halves(fmaxf(fmaxf(st.mx[0], st.mx[1]), fmaxf(st.mx[2], st.mx[3])), true);
+    asm volatile("" ::"v"(st.mrow));
+  } else if constexpr (K == 5) {
+    const float m_tile = st.mrow * c;
+    const bool raise = m_tile > m_run + kRaise;
+    st.m_use = raise ? m_tile : m_run;
+    st.alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+    m_run = st.m_use;
+    st.ps[0] = st.ps[1] = st.ps[2] = st.ps[3] = 0.f;
+    asm volatile("" ::"v"(st.m_use), "v"(st.alpha));
+  } else if constexpr (K >= 6 && K <= 25) {
+    // pack first (oldest pair), then exponentiate, then scale-and-shift the
+    // next pair, so the three steps in one slot are independent.
+    if constexpr (K >= 8 && K <= 23) {
+      constexpr int k = K - 8;
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      const bf16x2 pr = __builtin_convertvector((f32x2){st.p[0], st.p[1]}, bf16x2);
+      st.ps[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.ps[k & 3], false);
+      st.w[k] = __builtin_bit_cast(unsigned, pr);
+      asm volatile("" ::"v"(st.w[k]), "v"(st.ps[k & 3]));
+    }
+    if constexpr (K >= 7 && K <= 22) {
+      st.p[0] = __builtin_amdgcn_exp2f(st.t[0]);
+      st.p[1] = __builtin_amdgcn_exp2f(st.t[1]);
+      asm volatile("" ::"v"(st.p[0]), "v"(st.p[1]));
+    }
+    if constexpr (K >= 6 && K <= 21) {
+      constexpr int k = K - 6;
+      st.t[0] = fmaf(sv(2 * k), c, -st.m_use);
+      st.t[1] = fmaf(sv(2 * k + 1), c, -st.m_use);
+      asm volatile("" ::"v"(st.t[0]), "v"(st.t[1]));
+    }
+    if constexpr (K == 24) {
+      l_part = l_part * st.alpha + ((st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]));
+      asm volatile("" ::"v"(l_part));
+    }
+  }
+}
+
+__device__ __forceinline__ void softmax_pack(const Softmax& st, bf16x8 (&pfrag)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){st.w[4 * u], st.w[4 * u + 1], st.w[4 * u + 2], st.w[4 * u + 3]});
+}
+
+// Masked tile update in place on the score accumulator.  A score is
+// visible when its key offset (within the lane's keys of the tile) is below
+// lim; hidden scores become -inf through a sign-mask bit select (integer
+// ALU only, so no per-score lane masks occupy scalar registers).  With c > 0,
+// 2^(-inf) = 0 drops them from P; a row with no visible key keeps its state.
+__device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim, float& m_run, float& l_part,
+                                               bf16x8 (&pfrag)[4]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const unsigned keep = (unsigned)((score_key_offset(i) - lim) >> 31);
+    const unsigned u = __float_as_uint(s[i >> 4][i & 15]);
+    s[i >> 4][i & 15] = __uint_as_float((u & keep) | (0xff800000u & ~keep));
+    mx = fmaxf(mx, s[i >> 4][i & 15]);
+  }
+  const float mrow = swap_halves(mx, true);
+  const float m_tile = mrow * c;
+  const bool raise = m_tile > m_run + kRaise;  // false when m_tile = -inf
+  const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+  if (raise) m_run = m_tile;
+  const float m_use = m_run == -INFINITY ? 0.f : m_run;
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    unsigned w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int i = u * 8 + e;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 4][i & 15], c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m_use));
+      const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+      ps[e >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[e >> 1], false);
+      w[e >> 1] = __builtin_bit_cast(unsigned, pr);
+    }
+    pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+  }
+  l_part = l_part * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+  return alpha;
+}
+
+// ---------------------------------------------------------------------------
+// duo (d = 128): 8 waves per workgroup, two per SIMD, 32 query rows per
+// wave, 256 per workgroup, one workgroup per CU.
+//
+// Each wave software-pipelines its own tiles: within one barrier interval it
+// runs the 16 P.V MFMAs of one tile and the 16 Q.K MFMAs of another, and
+// the 32 slots of the online softmax of the tile in between ride on those
+// MFMAs, one slot of VALU work after each (the matrix unit computes while
+// the exponentials issue).  The two waves of a SIMD are staggered by half an
+// interval, so that one reads V^T fragments while the other reads K ones.
+// The HBM -> LDS copies (LDS-DMA, 1 KiB per wave instruction) are spread
+// over the same MFMAs two intervals ahead of use, into rings of four K and
+// three V tiles; one workgroup barrier per interval.
+//
+// Lazy rescaling: the reference max m of a row moves only when a tile's max
+// exceeds it by more than kRaise (log2 units), so O is rescaled a handful of
+// times per row instead of at every new maximum; in between P = 2^(s*c - m)
+// is at most 2^kRaise.  O = O~/l and L = m + log l do not depend on which
+// reference m was used (the online-softmax identity of "FlashAttention: Move
+// Less, Not Compute Less", "Tiling Is Easy"), so this changes rounding only.
+namespace duo {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 256;
-constexpr int kBK = 64;
-constexpr int kStages = 3;
+constexpr int kLead = 3;
+constexpr int kRingK = 4;  // K ring: tiles read by the two wave groups, one landing, one being written
+constexpr int kRingV = 3;  // V ring: tile being read, one landing, one being written
 
-// K and V tiles sit unpadded in LDS (rows of D bf16) because the
-// HBM->LDS DMA writes 1 KiB per wave instruction contiguously.  Bank
-// conflicts are removed by XOR-swizzling the 16-byte chunks of each row:
-//   K: chunk c of row r is stored at c ^ (r mod CPR)  -- the MFMA A-operand
-//      reads (16 consecutive rows, same chunk) hit 16 distinct chunks;
-//   V: chunk c of row r is stored at c ^ 2(r mod 4)   -- each 16-lane group
-//      of a transposing read touches 4 consecutive rows x 2 chunks, which
-//      land on 8 distinct chunks.
+// K and V tiles sit unpadded in LDS (rows of D bf16) because the LDS-DMA
+// writes 1 KiB per wave instruction contiguously.  Bank conflicts of the
+// MFMA operand reads are removed by XOR-swizzling the 16-byte chunks of
+// each row:
+//   K: chunk c of row r is stored at c ^ (r mod CPR) -- the 16 lanes reading
+//      one logical chunk of 16 consecutive rows hit 16 distinct chunks;
+//   V: chunk c of row r is stored at c ^ 2(r mod 4) -- a 16-lane group of a
+//      transposing read touches 4 consecutive rows x 2 chunks, which land
+//      on 8 distinct chunks.
 template <int D>
 struct Layout {
-  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int TILE = kBK * D;                 // elements per K (or V) tile
-  static constexpr int STAGE = 2 * TILE;
-  static constexpr int ROWS_PER_INSTR = 64 / CPR;      // rows one DMA instruction fills
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = kBK * D;
+  static constexpr int K0 = 0;
+  static constexpr int V0 = kRingK * TILE;
+  static constexpr int TOTAL = (kRingK + kRingV) * TILE;
+  static constexpr int ROWS_PER_INSTR = 64 / CPR;
   static constexpr int INSTR_PER_TILE = kBK / ROWS_PER_INSTR;
   static constexpr int INSTR_PER_WAVE = INSTR_PER_TILE / kWaves;
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
@@ -419,17 +545,17 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
   constexpr int CPR = Ly::CPR;
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[kStages * Ly::STAGE];
+  constexpr int NV = (kBK / 16) * DB;
+  constexpr int NK = 2 * DT;
+  constexpr int IPW = Ly::INSTR_PER_WAVE;
+  static_assert(NV == 16 && NK == 16, "32 MFMA slots per iteration");
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
-  // Waves w and w + 4 share a SIMD; they form the two phase groups.  Rows
-  // are interleaved so both groups meet the causal diagonal equally.
-  const int group = wave >> 2;
-  const int rowbase = ((wave & 3) * 2 + group) * 32;
 
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
@@ -439,7 +565,12 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   const __bf16* Kh = Kg + head;
   const __bf16* Vh = Vg + head;
 
-  const int qw = q0 + rowbase;
+  // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
+  // -inf * c stays -inf for hidden keys.
+  c = fmaxf(c, 1e-30f);
+  // Waves w and w + 4 share a SIMD; give them rows 64(w%4) + 32(w/4) so the
+  // two waves of a SIMD meet the causal diagonal at the same tile.
+  const int qw = q0 + (wave & 3) * 64 + (wave >> 2) * 32;
   const int qi = qw + col;
   bf16x8 qf[DT];
   if (qi < N) {
@@ -450,7 +581,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 #pragma unroll
     for (int t = 0; t < DT; ++t) qf[t] = bf16x8{};
   }
-  if (negate) {
+  if (negate) {  // scale < 0: use -Q and |scale| (negation is exact)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4 u = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
@@ -460,171 +591,239 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 
   int nkt = (N + kBK - 1) / kBK;
   if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / kBK + 1);
-  int wave_nt = nkt;  // tiles this wave computes
+  int wave_nt = nkt;
   if (CAUSAL) wave_nt = min(nkt, (qw + 31) / kBK + 1);
   if (qw >= N) wave_nt = 0;
+  int nfull = N / kBK;
+  if (CAUSAL) nfull = min(nfull, q0 / kBK);
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
   f32x16 sacc[2];
-  sacc[0] = f32x16{};
-  sacc[1] = f32x16{};
-  bf16x8 pfrag[kBK / 16];
+  sacc[0] = sacc[1] = f32x16{};
+  bf16x8 pfrag[4];
 #pragma unroll
-  for (int u = 0; u < kBK / 16; ++u) pfrag[u] = bf16x8{};
+  for (int u = 0; u < 4; ++u) pfrag[u] = bf16x8{};
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // ---- HBM -> LDS DMA of key/value tile t into stage t % kStages.  Each wave
-  // fills INSTR_PER_WAVE 1 KiB row groups of K and of V; lane l lands at
-  // chunk l % CPR of row l / CPR and fetches the chunk the swizzle puts there.
-  // Rows past N re-read row N - 1 (finite data; those keys are masked).
   const int dma_row = lane / CPR;
   const int dma_chunk = lane % CPR;
-  auto issue_tile = [&](int t) {
-    __bf16* Kl = smem + (t % kStages) * Ly::STAGE;
-    __bf16* Vl = Kl + Ly::TILE;
+  auto dma_one = [&](const __bf16* Xh, int buf, int t, int i, auto is_v) {
+    t = min(t, nkt - 1);
     const int kt0 = t * kBK;
-#pragma unroll
-    for (int i = 0; i < Ly::INSTR_PER_WAVE; ++i) {
-      const int r0 = (wave * Ly::INSTR_PER_WAVE + i) * Ly::ROWS_PER_INSTR;
-      const int row = r0 + dma_row;
-      const size_t key = (size_t)min(kt0 + row, N - 1);
-      const int ck = dma_chunk ^ (row % CPR);
-      const int cv = dma_chunk ^ (2 * (row & 3));
-      __builtin_amdgcn_global_load_lds((const void*)(Kh + key * D + ck * 8),
-                                       (__attribute__((address_space(3))) void*)(Kl + r0 * D), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(Vh + key * D + cv * 8),
-                                       (__attribute__((address_space(3))) void*)(Vl + r0 * D), 16, 0, 0);
-    }
+    const char* src = (const char*)(Xh + (size_t)kt0 * D);
+    const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
+    const int row = r0 + dma_row;
+    const int chunk = decltype(is_v)::value ? (dma_chunk ^ (2 * (row & 3))) : (dma_chunk ^ (row % CPR));
+    const unsigned off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
+    __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                     (__attribute__((address_space(3))) void*)(smem + buf + r0 * D), 16, 0, 0);
+  };
+  auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::TILE; };
+  auto vbuf = [](int t) { return Ly::V0 + (t % kRingV) * Ly::TILE; };
+  auto iteration_barrier = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(2 * IPW) : "memory");
   };
 
-  // ---- per-lane LDS byte offsets of the MFMA operands within a stage
-  // K: row kb*32 + col, logical chunk 2t + half (kb adds 32 rows).
   unsigned k_off[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * D + (((2 * t + half) ^ (col % CPR)) * 8)) * 2u;
-  // V (transposing reads): 16-lane group g = (half, tr_cg); lane (tr_e, tr_t)
-  // reads 8 bytes of key row u*16 + half*4 + tr_e (and +8), logical chunk
-  // 4b + 2*tr_cg + tr_t/2, 8-byte half tr_t & 1.
   const int tr_e = (lane & 15) >> 2;
   const int tr_t = lane & 3;
   const int tr_cg = (lane >> 4) & 1;
   unsigned v_off[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
-    v_off[b] = (unsigned)(Ly::TILE + (half * 4 + tr_e) * D +
-                          (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (2 * tr_e)) * 8) + (tr_t & 1) * 4) * 2u;
+    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (2 * tr_e)) * 8) +
+                          (tr_t & 1) * 4) * 2u;
   const unsigned smem_base = lds_addr(smem);
+  auto buf_addr = [&](int elem_off) {
+    unsigned a = smem_base + (unsigned)(elem_off * 2);
+    asm volatile("" : "+s"(a));
+    return a;
+  };
 
-  // The scheduling hints below keep LDS operand reads a few MFMAs ahead of
-  // their use instead of hoisting a whole phase's reads (which would need
-  // ~128 more VGPRs): kLead fragments are in flight, then each MFMA is
-  // followed by the read of the fragment kLead steps later.
-  constexpr int kLead = 3;
-  auto stage_base = [&](int j) {
-    unsigned base = smem_base + (unsigned)((j % kStages) * Ly::STAGE * 2);
-    asm volatile("" : "+s"(base));  // one add per operand per phase, not per read
-    return base;
+  Softmax st;
+  f32x16 sb[2];  // scores of the tile being normalised (Q.K overwrites sacc)
+
+  // S^T = K Q^T from K buffer kb.  With SM, softmax slots S0..S0+15 of the
+  // scores sc ride along; with DMA, the V DMA of tile dma_t into buffer
+  // dma_b.
+  auto qk = [&](int kb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
+    constexpr bool SM = decltype(with_sm)::value;
+    constexpr bool DMA = decltype(with_dma)::value;
+    constexpr int S0 = decltype(slot0)::value;
+    const unsigned base = buf_addr(kb);
+    bf16x8 fr[kLead];
+    auto issue = [&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      read_k<(F % 2) * 32 * D * 2>(fr[F % kLead], base + k_off[F / 2]);
+    };
+    static_for<kLead>(issue);
+    static_for<NK>([&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
+      asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fr[F % kLead]) : "i"(last - F));
+      if constexpr (F < 2)
+        sacc[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], f32x16{}, 0, 0, 0);
+      else
+        sacc[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], sacc[F % 2], 0, 0, 0);
+      if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
+      if constexpr (SM) softmax_slot<S0 + F>(st, sc, c, m_run, l_part);
+      if constexpr (DMA && F % 8 == 3) dma_one(Vh, dma_b, dma_t, F / 8, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
-  auto pv_body = [&](int j) {  // O^T += V_j^T P_j^T
-    const unsigned base = stage_base(j);
-    unsigned va[DB];
-#pragma unroll
-    for (int b = 0; b < DB; ++b) va[b] = base + v_off[b];
-#pragma unroll
-    for (int u = 0; u < kBK / 16; ++u) {
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const bf16x8 vf = lds_read_vt(va[b] + u * 16 * D * 2, va[b] + (u * 16 + 8) * D * 2);
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[u], oacc[b], 0, 0, 0);
-      }
-    }
+
+  // O^T += V^T P^T from V buffer vb.  With SM, softmax slots S0..S0+15 of
+  // the scores sc ride along; with DMA, the K DMA of tile dma_t into buffer
+  // dma_b.
+  auto pv = [&](int vb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
+    constexpr bool SM = decltype(with_sm)::value;
+    constexpr bool DMA = decltype(with_dma)::value;
+    constexpr int S0 = decltype(slot0)::value;
+    const unsigned base = buf_addr(vb);
+    s16x4 lo[kLead], hi[kLead];
+    auto issue = [&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      constexpr int u = F / DB, b = F % DB;
+      read_v<u * 16 * D * 2, (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], base + v_off[b]);
+    };
+    static_for<kLead>(issue);
+    static_for<NV>([&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      constexpr int u = F / DB, b = F % DB;
+      constexpr int last = (F + kLead - 1 < NV - 1) ? F + kLead - 1 : NV - 1;
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo[F % kLead]), "+v"(hi[F % kLead]) : "i"(2 * (last - F)));
+      const bf16x8 vf =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[F % kLead], hi[F % kLead], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[u], oacc[b], 0, 0, 0);
+      if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
+      if constexpr (SM) softmax_slot<S0 + F>(st, sc, c, m_run, l_part);
+      if constexpr (DMA && F % 8 == 3) dma_one(Kh, dma_b, dma_t, F / 8, std::false_type{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
-  auto qk_body = [&](int j) {  // S_j^T = K_j Q^T
-    const unsigned base = stage_base(j);
-    sacc[0] = f32x16{};
-    sacc[1] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      const unsigned ka = base + k_off[t];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 kf = lds_read_b128(ka + kb * 32 * D * 2);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sacc[kb], 0, 0, 0);
-      }
-    }
-  };
-  constexpr int kPvMfma = (kBK / 16) * DB;
-  constexpr int kQkMfma = 2 * DT;
-  // MFMA phase M_j: P_{j-1} V_{j-1} (if active) then Q K_j (if active).
-  auto mphase = [&](bool do_pv, bool do_qk, int j) {
-    if (do_pv) {
-      pv_body(j - 1);
-      sched_mfma_run<kLead, kPvMfma, kPvMfma>();
-    }
-    if (do_qk) {
-      qk_body(j);
-      sched_mfma_run<kLead, 0, kQkMfma>();
-    }
-  };
-  // Softmax phase: online update for tile j; P_j packed for the next MFMA phase.
-  auto softmax = [&](int j) {
-    float sv[32];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sv[r] = sacc[0][r];
-      sv[16 + r] = sacc[1][r];
-    }
-    const int kt0 = j * kBK;
-    const bool need_mask = (CAUSAL && kt0 + kBK - 1 > qw) || (kt0 + kBK > N);
-    const int lim_causal = qi - kt0 - half * 4;
-    const int lim_n = N - kt0 - half * 4;
-    const float alpha = need_mask
-                            ? tile_softmax<true, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag)
-                            : tile_softmax<false, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag);
-    // Rescale only when some row's max moved (alpha is exactly 1 otherwise).
+
+  auto rescale = [&](float alpha) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int b = 0; b < DB; ++b) oacc[b] *= alpha;
     }
   };
 
-  issue_tile(0);
-  if (nkt > 1) issue_tile(1);
-  __syncthreads();
-
-  // Global slot s: group 0 runs M_j in slot 2j and S_j in slot 2j + 1;
-  // group 1 runs them one slot later.  Every slot ends with one s_barrier
-  // for all 8 waves.  Tile t is DMA'd in slot 2t - 2 (into the stage that
-  // tile t - 3 used, last read in slot 2t - 3); the barrier ending each odd
-  // slot waits for the wave's DMA and LDS traffic (vmcnt/lgkmcnt = 0), so
-  // tile t is complete and visible from slot 2t on.  Even-slot barriers
-  // only keep the two groups in step.
-  auto end_slot = [&](int slot) {
-    if (slot & 1) {
-      __syncthreads();
+  // Interval j (between two workgroup barriers) loads K_{j+3} into the
+  // buffer K_{j-1} left and V_{j+1} into the buffer V_{j-2} left.  The two
+  // waves of a SIMD are staggered by half an interval so that one streams
+  // V^T through the transposing LDS reads while the other streams K:
+  //   waves 0-3, interval j: P_{j-1}V_{j-1} || softmax slots 0-15 of tile j,
+  //                          S_{j+1} = Q K_{j+1}^T || slots 16-31 of tile j
+  //   waves 4-7, interval j: S_j = Q K_j^T || slots 16-31 of tile j-1,
+  //                          P_{j-1}V_{j-1} || slots 0-15 of tile j
+  // (K_{j-1} was last read in interval j-1 by waves 4-7, V_{j-2} in
+  // interval j-1 by both groups).  Slots 0-15 read the scores where Q.K
+  // left them; slots 16-31 a copy, since the next Q.K overwrites them.
+  using S_lo = std::integral_constant<int, 0>;
+  using S_hi = std::integral_constant<int, 16>;
+  using On = std::true_type;
+  using Off = std::false_type;
+  const bool lead = wave < 4;
+  bool pending = false;  // waves 4-7: slots 16-31 of the previous tile still to run
+  auto masked_softmax = [&](int j) {
+    const int kt0 = j * kBK;
+    int lim = N - kt0 - half * 4;
+    if (CAUSAL) lim = min(lim, qi - kt0 - half * 4 + 1);
+    const float m_before = m_run;
+    const float alpha = softmax_masked_inplace(sacc, c, lim, m_run, l_part, pfrag);
+    rescale(m_before == -INFINITY ? 1.f : alpha);
+  };
+  auto finish_pending = [&]() {
+    static_for<16>([&](auto kc) { softmax_slot<16 + decltype(kc)::value>(st, sb, c, m_run, l_part); });
+    softmax_pack(st, pfrag);
+    pending = false;
+  };
+  // Steady interval: tile j unmasked for every row, 1 <= j, j + 1 < nkt.
+  // The two wave groups run separate loops, so the state waves 4-7 carry
+  // across barriers is not live in the loop of waves 0-3.
+  auto steady_lead = [&](int j) {
+    pv(vbuf(j - 1), On{}, On{}, j + 3, kbuf(j + 3), S_lo{}, sacc);
+    rescale(st.alpha);
+    sb[0] = sacc[0];
+    sb[1] = sacc[1];
+    qk(kbuf(j + 1), On{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
+    softmax_pack(st, pfrag);
+    iteration_barrier();
+  };
+  auto steady_follow = [&](int j, auto first) {
+    if constexpr (decltype(first)::value) {
+      qk(kbuf(j), Off{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
     } else {
-      __builtin_amdgcn_s_barrier();
+      sb[0] = sacc[0];
+      sb[1] = sacc[1];
+      qk(kbuf(j), On{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
+      softmax_pack(st, pfrag);
+    }
+    pv(vbuf(j - 1), On{}, On{}, j + 3, kbuf(j + 3), S_lo{}, sacc);
+    rescale(st.alpha);
+    iteration_barrier();
+  };
+  auto dma_all = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      dma_one(Kh, kbuf(j + 3), j + 3, i, Off{});
+      dma_one(Vh, vbuf(j + 1), j + 1, i, On{});
     }
   };
-  if (group == 1) end_slot(0);
-  for (int j = 0; j <= nkt; ++j) {
-    const int slot_m = 2 * j + group;
-    mphase(j >= 1 && j - 1 < wave_nt, j < wave_nt, j);
-    // DMA of tile slot/2 + 1 in even slots 2, 4, ..., issued after this
-    // phase's LDS reads so they need not wait for it.
-    if ((slot_m & 1) == 0 && slot_m >= 2 && slot_m / 2 + 1 < nkt) issue_tile(slot_m / 2 + 1);
-    end_slot(slot_m);
-    if (j < nkt) {
-      const int slot_s = slot_m + 1;
-      if ((slot_s & 1) == 0 && slot_s / 2 + 1 < nkt) issue_tile(slot_s / 2 + 1);
-      if (j < wave_nt) softmax(j);
-      end_slot(slot_s);
+  // Any interval (first, masked or last tiles; per-wave tile counts).
+  auto general_lead = [&](int j) {
+    dma_all(j);
+    if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    if (j < wave_nt) masked_softmax(j);
+    if (j + 1 < wave_nt) qk(kbuf(j + 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    iteration_barrier();
+  };
+  auto general_follow = [&](int j) {
+    dma_all(j);
+    if (pending) {
+      sb[0] = sacc[0];
+      sb[1] = sacc[1];
     }
+    if (j < wave_nt) qk(kbuf(j), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    if (pending) finish_pending();
+    if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    if (j < wave_nt) masked_softmax(j);
+    iteration_barrier();
+  };
+
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    dma_one(Kh, kbuf(0), 0, i, Off{});
+    dma_one(Kh, kbuf(1), 1, i, Off{});
+    dma_one(Kh, kbuf(2), 2, i, Off{});
+    dma_one(Vh, vbuf(0), 0, i, On{});
   }
-  if (group == 0) end_slot(2 * nkt + 1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  const int jend = min(nfull, nkt - 1);
+  if (lead) {
+    if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    general_lead(0);
+    int j = 1;
+    for (; j < jend; ++j) steady_lead(j);
+    for (; j < nkt; ++j) general_lead(j);
+  } else {
+    general_follow(0);
+    int j = 1;
+    if (j < jend) {
+      steady_follow(j, std::true_type{});
+      for (++j; j < jend; ++j) steady_follow(j, std::false_type{});
+      pending = true;
+    }
+    for (; j < nkt; ++j) general_follow(j);
+  }
+  if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float l_tot = swap_halves(l_part, false);
   if (qi < N) {
@@ -643,21 +842,20 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   }
 }
 
-}  // namespace pp
+}  // namespace duo
 
-// Kernel choice per head dim: the ping-pong kernel for d = 128 (MFMA phase
-// long enough to cover a softmax phase), the 4-wave kernel for d = 64.
-bool use_pp(int d) { return d == 128; }
-
+// Kernel per head dim: the staggered two-waves-per-SIMD kernel for d = 128,
+// the 4-wave kernel for d = 64 (whose 8 + 8 MFMAs per tile leave too few
+// slots to hide the softmax of a 64-key tile).
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const bool pingpong = use_pp(D);
-  const int bq = pingpong ? pp::kBQ : kBQ;
+  constexpr bool kDuo = D == 128;
+  const int bq = kDuo ? duo::kBQ : kBQ;
   const int nqb = (p.N + bq - 1) / bq;
   const float c_signed = p.scale * 1.44269504088896340736f;
   const int negate = p.scale < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
-  dim3 grid(p.BH * nqb), block(pingpong ? pp::kThreads : kThreads);
+  dim3 grid(p.BH * nqb), block(kDuo ? duo::kThreads : kThreads);
   const __bf16* q = (const __bf16*)p.q;
   const __bf16* k = (const __bf16*)p.k;
   const __bf16* v = (const __bf16*)p.v;
@@ -665,14 +863,18 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   float* lse = p.lse;
   int bh = p.BH, n = p.N;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate};
-  const void* fn = pingpong ? (const void*)pp::fwd_kernel<D, CAUSAL> : (const void*)fwd_bf16_kernel<D, CAUSAL>;
+  const void* fn;
+  if constexpr (kDuo)
+    fn = (const void*)duo::fwd_kernel<D, CAUSAL>;
+  else
+    fn = (const void*)fwd_bf16_kernel<D, CAUSAL>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace
 
 TileConfig bf16_tile(int d) {
-  return use_pp(d) ? TileConfig{pp::kBQ, pp::kBK, pp::kWaves} : TileConfig{kBQ, kBK, kWaves};
+  return d == 128 ? TileConfig{duo::kBQ, kBK, duo::kWaves} : TileConfig{kBQ, kBK, kWaves};
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
