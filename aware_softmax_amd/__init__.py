@@ -1,6 +1,6 @@
 """Python binding of libfa.so, the gfx950 fused exact-attention library.
 
-Argument marshalling only: every step of the forward runs in the HIP
+Argument marshalling only: every step of the forward and backward runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  torch supplies device
 memory and the current stream.  There is no fallback: if libfa.so is
 missing or fails to load, importing this package raises ImportError.
@@ -15,6 +15,10 @@ __all__ = [
     "FaError",
     "fwd",
     "fa_fwd",
+    "bwd",
+    "fa_bwd",
+    "bwd_workspace_bytes",
+    "bwd_tile_config",
     "tile_config",
     "version",
     "status_string",
@@ -42,7 +46,7 @@ class FaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m aware_softmax_amd.build` "
+            f"{LIB_PATH} is not built; run `python aware_softmax_amd/build.py` "
             "(there is no non-HIP fallback)"
         )
     lib = ctypes.CDLL(LIB_PATH)
@@ -53,6 +57,13 @@ def _load() -> ctypes.CDLL:
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd_tile.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
     lib.fa_fwd_tile.restype = ci
+    sz = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_bwd.restype = ci
+    lib.fa_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_tile.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    lib.fa_bwd_tile.restype = ci
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
     return lib
@@ -133,3 +144,70 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                   B, H, N, d, causal, scale, dtype, stream.cuda_stream))
     return out, lse
+
+
+def bwd_workspace_bytes(B, H, N, d) -> int:
+    """Device workspace bytes fa_bwd needs (0 for unsupported sizes)."""
+    return int(_LIB.fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def bwd_tile_config(d: int) -> tuple:
+    """(keys per workgroup, queries per streamed tile) of the backward."""
+    bk, bq = ctypes.c_int(), ctypes.c_int()
+    _check(_LIB.fa_bwd_tile(int(d), ctypes.byref(bk), ctypes.byref(bq)))
+    return bk.value, bq.value
+
+
+def fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, ws_bytes,
+           B, H, N, d, causal, scale, dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses; returns
+    the fa_status_t code."""
+    return _LIB.fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                       int(ws_bytes), int(B), int(H), int(N), int(d), int(bool(causal)), float(scale),
+                       int(dtype), stream)
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """dQ, dK, dV of attention for [B, H, N, d] bf16 device tensors.
+
+    o and lse are the outputs of fwd() for the same q, k, v, causal and
+    scale; do is the upstream gradient of o.  dq / dk / dv / workspace may
+    be passed to reuse buffers (workspace: a uint8 device tensor of at least
+    bwd_workspace_bytes(B, H, N, d) bytes).  Runs on `stream` (default:
+    torch's current stream).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"unsupported dtype {q.dtype} for the backward; use torch.bfloat16")
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q in dtype and shape")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                  workspace.numel() * workspace.element_size(), B, H, N, d, causal, scale, DTYPE_BF16,
+                  stream.cuda_stream))
+    return dq, dk, dv

@@ -1,6 +1,8 @@
 """Build libfa.so (gfx950) in-tree with hipcc.
 
-    python -m aware_softmax_amd.build        # or aware_softmax_amd.build.build()
+    python aware_softmax_amd/build.py        # or __graft_entry__.build()
+
+(Run by path: importing the package loads the library this script builds.)
 
 Each HIP source is compiled to an object in parallel, then linked into
 aware_softmax_amd/libfa.so.  The library is written to a temporary name and
@@ -21,11 +23,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
 # Per-source flags.  The bf16 kernels never see NaN scores from finite
 # inputs; without NaN semantics fmaxf needs no quieting of its operands,
 # which keeps the row max at one v_max3 per two scores.
-SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"], "fa_bwd_bf16.hip": ["-munsafe-fp-atomics"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

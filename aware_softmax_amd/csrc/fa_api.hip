@@ -36,12 +36,13 @@ const char* fa_status_string(fa_status_t status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte and lse 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP kernel launch failed";
-    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: o and lse must not overlap the inputs or each other";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or smaller than fa_bwd_workspace_bytes";
   }
   return "unknown fa_status_t";
 }
 
-const char* fa_version(void) { return "0.1.0 gfx950"; }
+const char* fa_version(void) { return "0.2.0 gfx950"; }
 
 fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves) {
   if (!block_q || !block_k || !waves) return FA_ERR_NULL;
@@ -92,6 +93,72 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.scale = scale;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX || bh * N * d > ((int64_t)1 << 40)) return 0;
+  return fa::bwd_workspace_bytes((int)bh, N, d);
+}
+
+fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q) {
+  if (!block_k || !block_q) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  *block_k = fa::bwd_block_k();
+  *block_q = fa::bwd_block_q();
+  return FA_OK;
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t elems = bh * N * d;
+  if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const int64_t nkb = ((int64_t)N + fa::bwd_block_k() - 1) / fa::bwd_block_k();
+  if (bh * nkb > INT_MAX) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+        (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_workspace_bytes((int)bh, N, d);
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = (size_t)elems * 2;
+  const size_t lb = (size_t)bh * N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_bytes[4] = {tb, tb, tb, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.workspace = workspace;
+  p.BH = (int)bh;
+  p.N = N;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

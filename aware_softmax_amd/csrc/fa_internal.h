@@ -31,8 +31,35 @@ struct TileConfig {
 TileConfig bf16_tile(int d);
 TileConfig f32_tile(int d);
 
-// Launchers: enqueue the kernel on `stream`; return the launch's hipError_t.
+// Everything a backward launch needs (device pointers, layouts of fa.h).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* workspace;  // bwd_workspace_bytes(BH, N, d) bytes
+  int BH;
+  int N;
+  int d;
+  int causal;
+  float scale;
+};
+
+// Launchers: enqueue the kernel(s) on `stream`; return the first
+// hipError_t a launch reported.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
+// Backward workspace: fp32 dQ accumulator [BH][Npad][d], then L (log2
+// units) and D, [BH][Npad] each; Npad = N rounded up to the query tile.
+size_t bwd_workspace_bytes(int BH, int N, int d);
+int bwd_block_k();  // keys per backward workgroup
+int bwd_block_q();  // queries per streamed backward tile
 
 }  // namespace fa

@@ -107,6 +107,39 @@ def time_launches(fa, q, k, v, o, lse, causal, scale, steps, warmup):
     return t_begin.elapsed_time(t_end) / steps, sum(per) / len(per), min(per), max(per), wall
 
 
+def time_backward(fa, w, q, k, v, o, lse, steps, warmup):
+    """fa_bwd (its three kernels) on one workload, inputs and the forward's
+    outputs resident; FLOPs 2.5x the forward's (five N x N x d products
+    instead of two), halved for the causal mask like the forward."""
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    st = synthetic.full_storage(w.config_id, "do", w.B, w.H, w.N, w.d, w.dtype)
+    do = torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).to(q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=q.device)
+    fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+    def step():
+        fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    f = 2.5 * attention_flops(w.B, w.H, w.N, w.d, w.causal)
+    return {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2),
+            "flops_per_call": f, "kernels": "bwd_pre + bwd_main + bwd_post"}
+
+
 def cpu_baseline(w, budget_s=12.0, rows_per_head=512):
     """The fp64 oracle on the host cores over a bounded sample of the same
     workload: seeded (b, h) heads, 512 seeded query rows each, until the
@@ -232,9 +265,11 @@ def main():
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
             ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, True, ww.scale, 20, 3)
             f = attention_flops(ww.B, ww.H, ww.N, ww.d, True)
-            extra[ww.name] = {"ms": round(msk, 4), "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2)}
-            if cid == 2:
-                pass
+            label = f"causal bf16 fwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"
+            extra[label] = {"ms": round(msk, 4), "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2)}
+            if cid == 5:
+                extra[f"causal bf16 bwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"] = time_backward(
+                    fa, ww, qq, kk, vv, oo, ll, 20, 3)
             del qq, kk, vv, oo, ll
             torch.cuda.empty_cache()
         qq, kk, vv = make_inputs(w)

@@ -56,7 +56,8 @@ typedef enum {
   FA_ERR_ALIGN = 5,                /* q/k/v/o not 16-byte or lse not 4-byte aligned */
   FA_ERR_SCALE = 6,                /* scale is NaN or infinite */
   FA_ERR_HIP = 7,                  /* the HIP launch reported an error */
-  FA_ERR_ALIAS = 8                 /* o or lse overlaps an input or each other */
+  FA_ERR_ALIAS = 8,                /* an output overlaps an input or another output */
+  FA_ERR_WORKSPACE = 9             /* workspace missing, misaligned or too small */
 } fa_status_t;
 
 /*
@@ -90,6 +91,57 @@ const char* fa_status_string(fa_status_t status);
  * FA_ERR_NULL / FA_ERR_DTYPE / FA_ERR_UNSUPPORTED_HEADDIM.
  */
 fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves);
+
+/*
+ * fa_bwd_workspace_bytes -- size of the device workspace fa_bwd needs for
+ * these sizes: an fp32 dQ accumulator of [B][H][Npad][d] plus two fp32
+ * [B][H][Npad] row vectors, Npad = N rounded up to a multiple of 64.
+ * Host-only; makes no HIP call.  Returns 0 for non-positive sizes or an
+ * unsupported head dimension.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- attention backward for all B*H heads: given the upstream
+ * gradient dO of O, writes dQ, dK and dV.
+ *
+ * "FlashAttention: Move Less, Not Compute Less", "Why More Arithmetic Can
+ * Finish Sooner": the backward does not read a stored S or P; it rebuilds
+ * P = exp(scale Q K^T + mask - L) tile by tile on chip from Q, K and the
+ * row statistic L of the forward ("FlashAttention-2: ...", "FA2 change #1").
+ * "FA2 change #2", last paragraph: the work is split over key columns, each
+ * worker owning dK_j and dV_j, and the dQ rows shared by all workers are
+ * accumulated with atomic adds (here into the fp32 workspace, converted to
+ * dQ at the end).  With D_i = dO_i . O_i and dS = P * (dO V^T - D):
+ *     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
+ *
+ *   q, k, v, o, dout  [in]  device, [B][H][N][d] bf16, 16-byte aligned; o is
+ *                     the forward output for the same q, k, v, causal, scale.
+ *   lse       [in]  device, [B][H][N] float32 (the forward's L), 4-byte aligned.
+ *   dq, dk, dv [out] device, [B][H][N][d] bf16, 16-byte aligned; must not
+ *                     overlap each other, the inputs or the workspace.
+ *   workspace [scratch] device, at least fa_bwd_workspace_bytes(B, H, N, d)
+ *                     bytes (passed as workspace_bytes), 256-byte aligned,
+ *                     owned by the caller; overwritten, contents undefined
+ *                     afterwards.  It is cleared by the call itself, so it
+ *                     needs no initialisation.
+ *   B, H, N, d, causal, scale   as for fa_fwd.
+ *   dtype     FA_DTYPE_BF16 only (FA_DTYPE_F32 returns FA_ERR_DTYPE).
+ *   stream    HIP stream; three kernels are enqueued in order on it.
+ * Returns FA_OK or the first failed check.  Accumulation order of dQ
+ * depends on the order of the atomic adds, so dQ may differ in the last
+ * bits between runs; dK and dV are deterministic.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, int causal, float scale, fa_dtype_t dtype,
+                   hipStream_t stream);
+
+/*
+ * fa_bwd_tile -- keys per backward workgroup and queries per streamed tile.
+ * Host-only.  Returns FA_OK or FA_ERR_NULL / FA_ERR_UNSUPPORTED_HEADDIM.
+ */
+fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q);
 
 /* Library version string, e.g. "0.1.0 gfx950" (static storage). */
 const char* fa_version(void);

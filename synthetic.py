@@ -50,7 +50,7 @@ WORKLOADS = {
     2: Workload(2, "causal bf16 B1 H16 N2048 d64", 1, 16, 2048, 64, "bf16", True),
     3: Workload(3, "causal bf16 B8 H32 N8192 d128", 8, 32, 8192, 128, "bf16", True),
     4: Workload(4, "long-context causal bf16 B1 H16 N32768 d128", 1, 16, 32768, 128, "bf16", True),
-    5: Workload(5, "causal bf16 fwd+bwd B2 H16 N4096 d128", 2, 16, 4096, 128, "bf16", True),
+    5: Workload(5, "causal bf16 forward and backward B2 H16 N4096 d128", 2, 16, 4096, 128, "bf16", True),
 }
 
 

@@ -34,7 +34,8 @@ def fa():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version"):
+    for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version", "fa_bwd",
+                     "fa_bwd_workspace_bytes", "fa_bwd_tile"):
         assert required in names
 
 
@@ -52,7 +53,7 @@ def test_library_carries_gfx950_code_object(fa):
 
 
 def test_status_strings(fa):
-    for code in range(9):
+    for code in range(10):
         s = fa.status_string(code)
         assert s.startswith("FA_")
     assert fa.status_string(99) == "unknown fa_status_t"
@@ -145,3 +146,57 @@ int main() {
     subprocess.run(["g++", "-std=c++17", "-O1", "-I", csrc, str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+# ------------------------------------------------------------ fa_bwd
+
+W = A + 0x8000000  # fake workspace address (256-byte aligned)
+BGOOD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000,
+             do=A + 0x5000000, dq=A + 0x6000000, dk=A + 0x7000000, dv=A + 0x7800000, ws=W,
+             ws_bytes=1 << 26, B=1, H=2, N=64, d=64, causal=1, scale=0.125, dtype=1, stream=None)
+
+
+def bcall(fa, **over):
+    a = dict(BGOOD)
+    a.update(over)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["ws"],
+                     a["ws_bytes"], a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"],
+                     a["stream"])
+
+
+def test_bwd_workspace_bytes(fa):
+    # fp32 dQ accumulator over N rounded up to 64 rows, plus two fp32 row vectors
+    assert fa.bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * (128 + 2) * 4
+    assert fa.bwd_workspace_bytes(1, 2, 65, 64) == 2 * 128 * (64 + 2) * 4
+    assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 64 * 130 * 4
+    for bad in ((0, 1, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96), (1, -1, 64, 128)):
+        assert fa.bwd_workspace_bytes(*bad) == 0
+    bk, bq = fa.bwd_tile_config(128)
+    assert bk > 0 and bq > 0 and bk % 32 == 0
+    with pytest.raises(fa.FaError):
+        fa.bwd_tile_config(80)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(do=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dv=0), 1),
+    (dict(B=0), 2), (dict(N=-3), 2), (dict(B=1 << 20, H=1 << 12, N=1 << 20), 2),
+    (dict(dtype=0), 3), (dict(dtype=5), 3),
+    (dict(d=96), 4), (dict(d=32), 4),
+    (dict(do=A + 0x5000008), 5), (dict(dk=A + 0x7000002), 5), (dict(lse=A + 0x4000001), 5),
+    (dict(scale=float("nan")), 6), (dict(scale=float("-inf")), 6),
+    (dict(dq=A), 8), (dict(dv=A + 0x7000100), 8), (dict(ws=A + 0x6000000), 8), (dict(dk=W + 0x100), 8),
+    (dict(ws=0), 9), (dict(ws=W + 16), 9), (dict(ws_bytes=1000), 9),
+])
+def test_bwd_validation_rejects_before_launch(fa, over, code):
+    assert bcall(fa, **over) == code
+
+
+def test_bwd_binding_rejects_bad_tensors(fa):
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError):
+        fa.bwd(q, q, q, q, lse, q)
+    with pytest.raises(TypeError):
+        fa.bwd(q.float(), q.float(), q.float(), q.float(), lse, q.float())

@@ -1,0 +1,162 @@
+"""GPU parity of fa_bwd against the fp64 analytic backward of the oracle.
+
+Every case draws seeded Q, K, V, dO from synthetic.py, runs the HIP forward
+and backward through the C ABI (aware_softmax_amd.fwd / .bwd -> fa_fwd /
+fa_bwd) and compares dQ, dK and dV element by element with
+oracle.attention_bwd on the same bf16 values upcast to fp64.
+
+Tolerance (per gradient tensor, over every checked element):
+  max |got - ref| <= 2e-2 * max(1, max |ref|)   and
+  rms(got - ref)  <= 1e-2 * rms(ref) + 1e-4
+(the absolute floor covers gradients that are exactly 0, e.g. dQ of a
+causal row that sees a single key).
+Derivation: the kernels round P and dS to bf16 for the MFMAs (relative
+2^-9 each), take D_i = dO_i . O_i from the bf16 output O, accumulate in
+fp32 and round each gradient to bf16 once (half an ulp: 2^-9 relative).
+Replaying exactly those roundings in fp64 NumPy on the B2 H16 N4096 d128
+workload gives max-abs errors of 0.007-0.011 against max |ref| of 2-5 and
+a relative rms error of 2.4e-3; the bounds leave a 2-4x margin over that
+model while a wrong term (a dropped D, a missing scale, a transposed
+operand) moves the gradients by O(max |ref|).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import aware_softmax_amd
+
+    return aware_softmax_amd
+
+
+def to_device(storage):
+    import torch
+
+    return torch.from_numpy(storage.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def assert_grad_close(name, got, ref):
+    max_abs = float(np.abs(got - ref).max())
+    bound = 2e-2 * max(1.0, float(np.abs(ref).max()))
+    assert max_abs <= bound, f"{name}: max |got - ref| = {max_abs:.3e} > {bound:.3e}"
+    rms_err = float(np.sqrt(np.mean((got - ref) ** 2)))
+    rms_bound = 1e-2 * float(np.sqrt(np.mean(ref ** 2))) + 1e-4
+    assert rms_err <= rms_bound, f"{name}: rms error {rms_err:.3e} > {rms_bound:.3e}"
+
+
+def run_bwd(fa, config_id, B, H, N, d, causal, scale=None, heads=None, tensors=None):
+    """Runs fwd + bwd on the GPU and checks dQ, dK, dV of the given heads."""
+    import torch
+
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if tensors is None:
+        tensors = {t: synthetic.full_storage(config_id, t, B, H, N, d, "bf16") for t in ("q", "k", "v", "do")}
+    q, k, v, do = (to_device(tensors[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in heads:
+        vals = [synthetic.bf16_bits_to_f32(tensors[t][b, h]) for t in ("q", "k", "v", "do")]
+        ref = oracle.attention_bwd(*vals, causal, scale)
+        for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            assert_grad_close(f"{name}[{b},{h}]", got[b, h].float().cpu().numpy().astype(np.float64), r)
+    return dq, dk, dv
+
+
+# ------------------------------------------------------------ the workload
+
+
+def test_workload5_backward_sampled_heads(fa):
+    """B=2, H=16, N=4096, d=128 causal: 4 seeded heads, every row of dQ,
+    dK, dV, in the launch configuration the bench times."""
+    w = synthetic.WORKLOADS[5]
+    heads = synthetic.sample_heads(5, w.B, w.H, 4)
+    run_bwd(fa, 5, w.B, w.H, w.N, w.d, w.causal, heads=heads)
+
+
+# ------------------------------------------------------------ shapes and edges
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 127, 128, 129, 200, 333, 513])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_bwd(fa, n, d, causal):
+    cid = 6000 + n * 4 + (d == 128) * 2 + causal
+    run_bwd(fa, cid, 1, 2, n, d, causal)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.35])
+def test_other_scales_bwd(fa, scale):
+    run_bwd(fa, 6500 + int(scale * 100), 1, 2, 300, 64, True, scale=scale)
+
+
+def test_noncausal_multi_block(fa):
+    run_bwd(fa, 6600, 2, 2, 1000, 128, False)
+
+
+def test_closed_form_sums(fa):
+    """No oracle: every row of P sums to 1, so the dV rows sum to the dO
+    rows' sum; the rows of dS sum to 0, so the dK rows sum to 0."""
+    import torch
+
+    B, H, N, d = 1, 3, 2048, 128
+    st = {t: synthetic.full_storage(6700, t, B, H, N, d, "bf16") for t in ("q", "k", "v", "do")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    dov = synthetic.bf16_bits_to_f32(st["do"]).astype(np.float64)
+    sum_dv = dv.double().sum(dim=2).cpu().numpy()
+    sum_do = dov.sum(axis=2)
+    # each of the N bf16 entries carries <= 2^-9 relative rounding
+    bound = 2.0 ** -8 * dv.double().abs().sum(dim=2).cpu().numpy() + 1e-3
+    assert np.all(np.abs(sum_dv - sum_do) <= bound)
+    sum_dk = dk.double().sum(dim=2).cpu().numpy()
+    assert np.all(np.abs(sum_dk) <= 2.0 ** -7 * dk.double().abs().sum(dim=2).cpu().numpy() + 1e-3)
+
+
+def test_deterministic_dk_dv_and_dirty_workspace(fa):
+    """dK and dV have no atomics: bitwise identical across runs.  The
+    workspace is cleared by the call, so garbage in it changes nothing
+    beyond the atomic-order rounding of dQ."""
+    import torch
+
+    B, H, N, d = 2, 2, 777, 128
+    st = {t: synthetic.full_storage(6800, t, B, H, N, d, "bf16") for t in ("q", "k", "v", "do")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    ws = torch.full((fa.bwd_workspace_bytes(B, H, N, d) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    dq1, dk1, dv1 = fa.bwd(q, k, v, o, lse, do, causal=True, workspace=ws.view(torch.uint8))
+    dq2, dk2, dv2 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk1.view(torch.int16), dk2.view(torch.int16))
+    assert torch.equal(dv1.view(torch.int16), dv2.view(torch.int16))
+    assert torch.isfinite(dq1.float()).all()
+    assert float((dq1.float() - dq2.float()).abs().max()) <= 2.0 ** -6 * max(1.0, float(dq2.float().abs().max()))
+
+
+def test_outputs_untouched_outside_bounds(fa):
+    """fa_bwd writes exactly B*H*N rows of dQ, dK and dV."""
+    import torch
+
+    B, H, n, d = 1, 2, 129, 64
+    st = {t: synthetic.full_storage(6900, t, B, H, n, d, "bf16") for t in ("q", "k", "v", "do")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    size = B * H * n * d
+    bufs = [torch.full((size + 64,), 7.0, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    outs = [b[:size].view(B, H, n, d) for b in bufs]
+    fa.bwd(q, k, v, o, lse, do, causal=True, dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert torch.all(b[size:] == 7.0)
+        assert torch.isfinite(b[:size].float()).all()
