@@ -27,7 +27,7 @@ SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip"]
 # Per-source flags.  The bf16 kernels never see NaN scores from finite
 # inputs; without NaN semantics fmaxf needs no quieting of its operands,
 # which keeps the row max at one v_max3 per two scores.
-SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"], "fa_bwd_bf16.hip": ["-munsafe-fp-atomics"]}
+SOURCE_FLAGS = {"fa_fwd_bf16.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

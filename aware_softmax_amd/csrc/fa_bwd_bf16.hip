@@ -9,35 +9,51 @@
 //   P  = exp(scale * Q K^T - L)          (0 where masked)
 //   dV = P^T dO,   dP = dO V^T,   D_i = dO_i . O_i,   dS = P * (dP - D)
 //   dK = scale * dS^T Q,   dQ = scale * dS K
-// How ("FA2 change #2", last paragraph): the backward is parallel over key
-// columns.  Each workgroup owns one block of 128 keys and keeps dK and dV of
-// those keys in registers for the whole sweep over query tiles, so dK and dV
-// need no atomics; the dQ rows, which every key block touches, are
-// accumulated in an fp32 buffer with atomic adds.
+//
+// How.  "FA2 change #2" (last paragraph) parallelises the backward over key
+// columns: each worker owns dK_j and dV_j, and the dQ rows that every
+// worker touches are accumulated with atomic adds.  The key-column part is
+// kept; the dQ atomics are not: on MI355X fp32 atomic adds of one 64 x d
+// partial dQ per (key block, query tile) took as long as all five matrix
+// products together (about one lane per clock per CU).  dQ is instead
+// formed by a second, query-parallel kernel that rebuilds S, P and dP for
+// its rows -- two more matrix products in place of the atomics, the pages'
+// trade of recomputation for memory traffic once more -- which also makes
+// dQ deterministic.
 //
 // Three kernels:
-//   bwd_pre   D_i = dO_i . O_i (fp32), L in log2 units, dQ accumulator = 0;
-//   bwd_main  one workgroup per (head, 128-key block), 4 wave64s with 32
+//   bwd_pre   D_i = dO_i . O_i (fp32) and L_i / scale, stored negated: the
+//             initial values of the dP and S accumulators below;
+//   bwd_dkdv  one workgroup per (head, 128-key block), 4 wave64s with 32
 //             keys each; 64-query tiles of Q and dO (plus L, D) streamed
-//             through double-buffered LDS;
-//   bwd_post  dQ = scale * accumulator, rounded to bf16.
+//             through triple-buffered LDS; dK, dV in registers;
+//   bwd_dq    one workgroup per (head, 128-query block), 4 wave64s with 32
+//             queries each; 64-key tiles of K and V streamed through
+//             triple-buffered LDS; dQ in registers.
 //
-// MI355X mapping of bwd_main (v_mfma_f32_32x32x16_bf16 throughout):
-//   * S = Q K^T and dP = dO V^T are computed with queries as MFMA rows and
-//     the wave's 32 keys as columns, K and V fragments resident in VGPRs:
-//     each lane owns one key and 16 query rows of each 32-query block;
-//   * that accumulator layout, packed to bf16, is directly the B operand of
-//     dV^T += dO^T P and dK^T += Q^T dS (the query order inside a 16-query
-//     step is permuted identically on both operands); the dO^T and Q^T
-//     fragments come from the row-major tiles through ds_read_b64_tr_b16;
-//   * dS^T (keys x queries) is written to LDS and dQ = dS K is formed per
-//     workgroup over all 128 keys (both operands through transposing reads),
-//     one tile behind, so a single barrier per tile suffices;
+// MI355X mapping (v_mfma_f32_32x32x16_bf16 throughout, one wave per SIMD):
+//   * the MFMA accumulator layout that computes scores is directly the B
+//     operand of the next product: in bwd_dkdv S and dP have queries as rows
+//     and the wave's 32 keys as columns, so P and dS packed to bf16 feed
+//     dV^T += dO^T P and dK^T += Q^T dS; in bwd_dq S^T and dP^T have keys as
+//     rows and the wave's 32 queries as columns, so dS^T feeds
+//     dQ^T += K^T dS^T (the order of the 16 contraction indices of a step
+//     is permuted identically on both operands);
+//   * the transposed operands (dO^T, Q^T, K^T) come from the row-major LDS
+//     tiles through ds_read_b64_tr_b16;
 //   * LDS tiles are XOR-swizzled per 16-byte chunk so that both the
 //     row-fragment reads (ds_read_b128) and the transposing reads are free
-//     of bank conflicts.
+//     of bank conflicts, and are filled by LDS-DMA (global_load_lds) two
+//     tiles ahead;
+//   * each tile is software-pipelined: the MFMAs that compute the next
+//     tile's scores run while the current tile's P and dS are exponentiated
+//     and packed on the VALU, then the current tile's gradient MFMAs run.
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "fa_internal.h"
 #include "fa_schedule.h"
@@ -52,18 +68,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBKV = 128;  // keys per workgroup (32 per wave)
-constexpr int kBQ = 64;    // queries per streamed tile
+constexpr int kBKV = 128;     // bwd_dkdv: keys per workgroup (32 per wave)
+constexpr int kBQ = 64;       // bwd_dkdv: queries per streamed tile
+constexpr int kBQdq = 128;    // bwd_dq: queries per workgroup (32 per wave)
+constexpr int kBKdq = 64;     // bwd_dq: keys per streamed tile
+constexpr int kRing = 3;      // LDS buffers per streamed tensor
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Physical 16-byte chunk of logical chunk c in row r of an LDS tile whose
-// rows are ROWB bytes.  Conflict-free for
+// Calls fn(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
+template <class Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, I...>) {
+  (fn(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  static_for_impl(fn, std::make_integer_sequence<int, N>{});
+}
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+// Physical 16-byte chunk mask of row r of an LDS tile whose rows are ROWB
+// bytes (chunk c is stored at c ^ mask).  Conflict-free for
 //   * 16 lanes reading one chunk of 16 consecutive rows (ds_read_b128), and
 //   * 32 lanes reading 4 chunks of 4 consecutive rows (transposing reads).
 template <int ROWB>
@@ -75,23 +104,72 @@ __device__ __forceinline__ int swz_mask(int r) {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-__device__ __forceinline__ bf16x8 tr_frag(const char* p_lo, const char* p_hi) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p_lo));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p_hi));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+__device__ inline unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// LDS operand reads by inline asm: completion is tracked only by the
+// explicit lgkmcnt waits that precede each use, so several fragments stay in
+// flight while the MFMAs run (hipcc's own wait insertion would drain the
+// queue before every read).  LDS reads complete in order, so a wait that
+// counts only the reads issued after a fragment is exact for it.  The loops
+// below issue no other LDS operation.
+template <int OFF>
+__device__ __forceinline__ void ds_b128(bf16x8& f, unsigned addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_b128f(f32x4& f, unsigned addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_tr64(s16x4& f, unsigned addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
+}
+__device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Waits until this wave's LDS-DMA copies and LDS operations are complete,
+// then the workgroup barrier.
+__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copies rows [r0, r0 + kRows) of a row-major [N][D] bf16 matrix into a
+// swizzled LDS tile (rows past N - 1 are clamped; their values are never
+// used unmasked).  One wave instruction writes 1 KiB of LDS contiguously
+// (lane l at byte 16 l); the swizzle is applied by choosing which logical
+// chunk each lane fetches.  Wave w issues instructions [w IPW, (w + 1) IPW).
+template <int D, int kRows>
+__device__ __forceinline__ void dma_rows(const __bf16* X, int r0, int N, char* tile, int wave, int lane) {
+  constexpr int ROWB = 2 * D, CPR = D / 8, RPI = 1024 / ROWB;
+  constexpr int IPW = kRows * ROWB / 1024 / kWaves;
+  static_assert(kRows * ROWB % (1024 * kWaves) == 0, "DMA splits evenly over waves");
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int inst = wave * IPW + i;
+    const int row = inst * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz_mask<ROWB>(row);
+    const size_t off = (size_t)min(r0 + row, N - 1) * D + chunk * 8;
+    __builtin_amdgcn_global_load_lds((const void*)(X + off), (lds_void*)(tile + inst * 1024), 16, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // bwd_pre: one row per LPR lanes (one 16-byte chunk of dO and O each).
+// Writes -D_i and -L_i / scale (in the units of the raw score q.k): the
+// initial values of the dP and S accumulators of the two main kernels, so
+// that their MFMAs produce dP - D and q.k - L / scale directly.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ Og, const __bf16* __restrict__ dOg,
-                                                      const float* __restrict__ Lg, float* __restrict__ dqacc,
-                                                      float* __restrict__ L2g, float* __restrict__ Dg, int N,
-                                                      int Npad) {
+                                                      const float* __restrict__ Lg, float* __restrict__ Lsg,
+                                                      float* __restrict__ Dng, int N, int Npad, float l_to_score) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
@@ -109,71 +187,48 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   }
 #pragma unroll
   for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  f32x4* z = (f32x4*)(dqacc + row * D + c * 8);
-  z[0] = f32x4{};
-  z[1] = f32x4{};
   if (c == 0) {
-    Dg[row] = acc;
-    L2g[row] = i < N ? Lg[(size_t)bh * N + i] * kLog2e : 0.f;
+    Dng[row] = -acc;
+    Lsg[row] = i < N ? -Lg[(size_t)bh * N + i] * l_to_score : 0.f;
   }
-}
-
-// bwd_post: dQ = scale * accumulator -> bf16, 8 elements per thread.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_post_kernel(const float* __restrict__ dqacc, __bf16* __restrict__ dQg,
-                                                       int N, int Npad, size_t total8, float scale) {
-  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= total8) return;
-  const size_t e = g * 8;  // element index in [B][H][N][D]
-  const size_t row = e / D;
-  const int cd = (int)(e % D);
-  const size_t bh = row / N;
-  const int i = (int)(row % N);
-  const f32x4* src = (const f32x4*)(dqacc + (bh * Npad + i) * D + cd);
-  const f32x4 a = src[0], b = src[1];
-  bf16x8 out;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    out[k] = (__bf16)(a[k] * scale);
-    out[4 + k] = (__bf16)(b[k] * scale);
-  }
-  *(bf16x8*)(dQg + e) = out;
 }
 
 // ---------------------------------------------------------------------------
-// bwd_main.
+// bwd_dkdv.
 template <int D>
-struct BwdLayout {
-  static constexpr int ROWB = 2 * D;            // bytes per Q / dO / K row
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int QTILE = kBQ * ROWB;      // one Q or dO tile
-  static constexpr int KTILE = kBKV * ROWB;     // the workgroup's K block
-  static constexpr int DSROWB = 2 * kBQ;        // dS^T row: 64 queries
-  static constexpr int DSTILE = kBKV * DSROWB;  // dS^T tile
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_Q = OFF_K + KTILE;
-  static constexpr int OFF_DO = OFF_Q + 2 * QTILE;
-  static constexpr int OFF_DS = OFF_DO + 2 * QTILE;
-  static constexpr int OFF_LD = OFF_DS + 2 * DSTILE;  // per buffer: L2[64], D[64]
-  static constexpr int LDTILE = 2 * kBQ * 4;
-  static constexpr int TOTAL = OFF_LD + 2 * LDTILE;
-  static constexpr int CH = QTILE / 16 / kThreads;  // staged chunks per thread per tile
-  static_assert(QTILE % (16 * kThreads) == 0 && KTILE % (16 * kThreads) == 0, "tiles split over threads");
+struct DkdvLayout {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int QTILE = kBQ * ROWB;    // one Q or dO tile
+  static constexpr int STTILE = 2 * kBQ * 4;  // -L/scale[64], -D[64]
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_DO = OFF_Q + kRing * QTILE;
+  static constexpr int OFF_ST = OFF_DO + kRing * QTILE;
+  static constexpr int TOTAL = OFF_ST + kRing * STTILE;
   static_assert(TOTAL <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
+// Per 64-query tile and wave (32 keys):
+//   A  S = Q K^T - L/scale and dP = dO V^T - D  (4 DT MFMAs; row fragments
+//      of the Q and dO tiles, several in flight);
+//   V  P = 2^(c S), dS = P dP, both packed to bf16 (VALU only);
+//   B  dV^T += dO^T P and dK^T += Q^T dS        (8 DB MFMAs, transposing reads).
+// Iteration t runs A(t + 1) with V(t) riding on its MFMAs, then B(t); the
+// DMA of tile t + 2 is in flight meanwhile; one barrier per iteration.
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void bwd_main_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                     const __bf16* __restrict__ dOg, const float* __restrict__ L2g, const float* __restrict__ Dg,
-                     float* __restrict__ dqacc, __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int BH, int N,
-                     int Npad, int nkb, float c, float scale) {
-  using Ly = BwdLayout<D>;
-  constexpr int DT = D / 16;  // 16-wide d steps (S and dP contractions)
-  constexpr int DB = D / 32;  // 32-wide d blocks (dK, dV, dQ outputs)
+void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
+                     const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
+                     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int BH, int N, int Npad, int nkb, float c,
+                     float scale) {
+  using Ly = DkdvLayout<D>;
+  constexpr int DT = D / 16;
+  constexpr int DB = D / 32;
   constexpr int ROWB = Ly::ROWB;
-  constexpr int CPR = Ly::CPR;
-  constexpr int DQB = DB / 2;  // dQ blocks per wave: 2 query blocks x DB d blocks over 4 waves
+  constexpr int NA = 4 * DT;  // phase A MFMAs
+  constexpr int LA = 4;       // phase A fragments in flight
+  constexpr int NB = 8 * DB;  // phase B MFMAs
+  constexpr int LB = 4;       // phase B fragments in flight
+  static_assert(NA % 8 == 0, "eight VALU groups ride on the phase A MFMAs");
   __shared__ __attribute__((aligned(1024))) char smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
@@ -192,13 +247,11 @@ void bwd_main_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const __bf16* Kh = Kg + head;
   const __bf16* Vh = Vg + head;
   const __bf16* dOh = dOg + head;
-  const float* L2h = L2g + (size_t)bh * Npad;
-  const float* Dh = Dg + (size_t)bh * Npad;
-  float* dqh = dqacc + (size_t)bh * Npad * D;
+  const float* Lsh = Lsg + (size_t)bh * Npad;
+  const float* Dnh = Dng + (size_t)bh * Npad;
 
   // K and V fragments of the wave's keys: B operands of S = Q K^T and
-  // dP = dO V^T (lane: key `col`, d = 16t + 8 half .. + 7).  Rows past the
-  // end are clamped (finite values; their scores are masked).
+  // dP = dO V^T (lane: key `col`, d = 16t + 8 half .. + 7).
   bf16x8 kf[DT], vf[DT];
   {
     const size_t r = (size_t)min(key, N - 1) * D + half * 8;
@@ -208,109 +261,44 @@ void bwd_main_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       vf[t] = *(const bf16x8*)(Vh + r + 16 * t);
     }
   }
-  // The workgroup's K block into LDS (B operand of dQ = dS K).
-#pragma unroll
-  for (int i = 0; i < Ly::KTILE / 16 / kThreads; ++i) {
-    const int ci = tid + kThreads * i;
-    const int row = ci / CPR, ch = ci % CPR;
-    const bf16x8 x = *(const bf16x8*)(Kh + (size_t)min(kb0 + row, N - 1) * D + ch * 8);
-    *(bf16x8*)(smem + Ly::OFF_K + row * ROWB + ((ch ^ swz_mask<ROWB>(row)) << 4)) = x;
-  }
 
   const int nqt = Npad / kBQ;
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
-
-  // ---- Q / dO / L2 / D tiles: global -> registers -> swizzled LDS rows.
-  bf16x8 qreg[Ly::CH], doreg[Ly::CH];
-  float ldreg = 0.f;
-  auto gload = [&](int it) {
-    const int q0 = it * kBQ;
-#pragma unroll
-    for (int i = 0; i < Ly::CH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / CPR, ch = ci % CPR;
-      const size_t off = (size_t)min(q0 + row, N - 1) * D + ch * 8;
-      qreg[i] = *(const bf16x8*)(Qh + off);
-      doreg[i] = *(const bf16x8*)(dOh + off);
-    }
-    if (tid < 2 * kBQ) ldreg = tid < kBQ ? L2h[q0 + tid] : Dh[q0 + tid - kBQ];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < Ly::CH; ++i) {
-      const int ci = tid + kThreads * i;
-      const int row = ci / CPR, ch = ci % CPR;
-      const int off = row * ROWB + ((ch ^ swz_mask<ROWB>(row)) << 4);
-      *(bf16x8*)(smem + Ly::OFF_Q + buf * Ly::QTILE + off) = qreg[i];
-      *(bf16x8*)(smem + Ly::OFF_DO + buf * Ly::QTILE + off) = doreg[i];
-    }
-    if (tid < 2 * kBQ) *(float*)(smem + Ly::OFF_LD + buf * Ly::LDTILE + tid * 4) = ldreg;
+  auto ring = [&](int it) { return __builtin_amdgcn_readfirstlane((it - it0) % kRing); };
+  auto dma_tile = [&](int it) {
+    const int b = ring(it);
+    if (wave < 2)  // the tile's 64 statistics: -L/scale by wave 0, -D by wave 1
+      __builtin_amdgcn_global_load_lds((const void*)((wave == 0 ? Lsh : Dnh) + it * kBQ + lane),
+                                       (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + wave * 4 * kBQ), 4, 0, 0);
+    dma_rows<D, kBQ>(Qh, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
+    dma_rows<D, kBQ>(dOh, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
   };
 
-  // ---- lane-constant LDS offsets
-  // Row fragments (A operand of S and dP): row 32 qb + col, chunk 2t + half.
-  int rf_off[2];
+  // Lane-constant LDS byte offsets within a tile.
+  // Row fragments: row 32 qb + col, logical chunk 2t + half, stored at
+  // (2t) ^ (half ^ mask): t enters as a XOR of bits 5.. of the offset.
+  unsigned rf_lane[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = 32 * qb + col;
-    rf_off[qb] = r * ROWB + ((half ^ swz_mask<ROWB>(r)) << 4);  // chunk 2t + half = 2t ^ (half)
+    rf_lane[qb] = (unsigned)(r * ROWB + ((half ^ swz_mask<ROWB>(r)) << 4));
   }
-  // Transposing reads of a row-major tile X (rows = contraction index):
-  // lane gets column 32b + col of rows 16u + 4 half + {0..3} (lo) and
-  // 16u + 8 + 4 half + {0..3} (hi).  The swizzle does not depend on u.
-  const int tr_e = (lane & 15) >> 2;
-  const int tr_t = lane & 3;
-  const int tr_cg = (lane >> 4) & 1;
-  auto tr_off = [&](int rowb_is_256, int hi, int chunk) {
-    const int r = 4 * half + tr_e + 8 * hi;
-    const int m = rowb_is_256 ? swz_mask<256>(r) : swz_mask<128>(r);
-    return r * (rowb_is_256 ? 256 : 128) + ((chunk ^ m) << 4) + (tr_t & 1) * 8;
-  };
-  int trq_off[DB][2];  // Q / dO / K tiles
+  // Transposing reads: lane gets column 32b + col of rows 16u + 4 half +
+  // {0..3} (lo) and 16u + 8 + 4 half + {0..3} (hi); the swizzle does not
+  // depend on u, which enters as an immediate offset.
+  unsigned trq[DB][2];
+  {
+    const int tr_e = (lane & 15) >> 2, tr_t = lane & 3, tr_cg = (lane >> 4) & 1;
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DB; ++b)
 #pragma unroll
-    for (int hi = 0; hi < 2; ++hi) trq_off[b][hi] = tr_off(ROWB == 256, hi, 4 * b + 2 * tr_cg + (tr_t >> 1));
-  int trs_off[2][2];  // dS^T tile (rows of 64 queries), query block qb
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) trs_off[qb][hi] = tr_off(0, hi, 4 * qb + 2 * tr_cg + (tr_t >> 1));
-  // dS^T writes: row = local key 32 wave + col, queries 32 qb + 8 g + 4 half.
-  const int ds_row = 32 * wave + col;
-  const int ds_mask = swz_mask<128>(ds_row);
-
-  const int dq_qb = wave >> 1;
-  const int dq_db0 = (wave & 1) * DQB;
-
-  // dQ(tile) += dS K over the workgroup's 128 keys, from dS^T buffer `buf`.
-  auto dq_step = [&](int it, int buf) {
-    const char* dst = smem + Ly::OFF_DS + buf * Ly::DSTILE;
-    const char* kt = smem + Ly::OFF_K;
-    f32x16 acc[DQB];
-#pragma unroll
-    for (int j = 0; j < DQB; ++j) acc[j] = f32x16{};
-    int usteps = kBKV / 16;
-    if (CAUSAL) usteps = min(usteps, max(0, (it * kBQ + kBQ - 1 - kb0) / 16 + 1));
-    for (int u = 0; u < usteps; ++u) {
-      const bf16x8 a = tr_frag(dst + u * 16 * Ly::DSROWB + trs_off[dq_qb][0],
-                               dst + u * 16 * Ly::DSROWB + trs_off[dq_qb][1]);
-#pragma unroll
-      for (int j = 0; j < DQB; ++j) {
-        const bf16x8 b = tr_frag(kt + u * 16 * ROWB + trq_off[dq_db0 + j][0], kt + u * 16 * ROWB + trq_off[dq_db0 + j][1]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * half + tr_e + 8 * hi;
+        const int chunk = 4 * b + 2 * tr_cg + (tr_t >> 1);
+        trq[b][hi] = (unsigned)(r * ROWB + ((chunk ^ swz_mask<ROWB>(r)) << 4) + (tr_t & 1) * 8);
       }
-    }
-    // rows of the padded accumulator past N receive zeros (dS = 0 there)
-    float* base = dqh + (size_t)(it * kBQ + 32 * dq_qb + 4 * half) * D + col;
-#pragma unroll
-    for (int j = 0; j < DQB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float* p = base + (size_t)(8 * (r >> 2) + (r & 3)) * D + 32 * (dq_db0 + j);
-        unsafeAtomicAdd(p, acc[j][r]);
-      }
-  };
+  }
+  const unsigned sbase = lds_addr(smem);
 
   f32x16 dkT[DB], dvT[DB];
 #pragma unroll
@@ -318,101 +306,138 @@ void bwd_main_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     dkT[b] = f32x16{};
     dvT[b] = f32x16{};
   }
+  f32x16 S[2], dP[2];  // [query block]
+  unsigned pw[2][8], dw[2][8];
 
-  gload(it0);
-  lstore(0);
-  __syncthreads();
+  // visible iff key <= query (causal), query < N and key < N: with lo = the
+  // smallest visible query index, query q is visible iff lo <= q < N.
+  const int lo = key >= N ? INT_MAX / 2 : (CAUSAL ? key : 0);
 
-  for (int it = it0; it < nqt; ++it) {
-    const int buf = (it - it0) & 1;
-    if (it + 1 < nqt) gload(it + 1);
-    const int q0 = it * kBQ;
-    const char* qt = smem + Ly::OFF_Q + buf * Ly::QTILE;
-    const char* dot = smem + Ly::OFF_DO + buf * Ly::QTILE;
-
-    // S = Q K^T and dP = dO V^T for the two 32-query blocks.
-    f32x16 s[2], dp[2];
+  // VALU group k: P and dS of query block k / 4, rows 8 (k % 4) + 4 half +
+  // {0..3}, i.e. the bf16 pairs of 16-query step k / 2 of phase B.
+  auto vgroup = [&](auto kc, auto mask_c, int it) {
+    constexpr int k = decltype(kc)::value, qb = k / 4, g = k % 4;
+    constexpr bool MASK = decltype(mask_c)::value;
+    float p[4], ds[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const bf16x8 a = *(const bf16x8*)(qt + (rf_off[qb] ^ (t << 5)));
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[t], s[qb], 0, 0, 0);
+    for (int e = 0; e < 4; ++e) {
+      float pe = __builtin_amdgcn_exp2f(S[qb][4 * g + e] * c);
+      if constexpr (MASK) {
+        const int qi = it * kBQ + 32 * qb + 8 * g + 4 * half + e;
+        const unsigned keep = ~(unsigned)(((qi - lo) | (N - 1 - qi)) >> 31);
+        pe = __uint_as_float(__float_as_uint(pe) & keep);
       }
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const bf16x8 a = *(const bf16x8*)(dot + (rf_off[qb] ^ (t << 5)));
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[t], dp[qb], 0, 0, 0);
-      }
+      p[e] = pe;
+      ds[e] = pe * dP[qb][4 * g + e];
     }
+    pw[qb][2 * g] = pack_bf16(p[0], p[1]);
+    pw[qb][2 * g + 1] = pack_bf16(p[2], p[3]);
+    dw[qb][2 * g] = pack_bf16(ds[0], ds[1]);
+    dw[qb][2 * g + 1] = pack_bf16(ds[2], ds[3]);
+  };
 
-    // dQ of the previous tile (its dS^T was completed before the barrier).
-    if (it > it0) dq_step(it - 1, buf ^ 1);
-
-    // P = 2^(s c - L2), dS = P (dP - D); lane: key `key`, queries
-    // q0 + 32 qb + 8 g + 4 half + e for accumulator register 4 g + e.
-    const float* l2t = (const float*)(smem + Ly::OFF_LD + buf * Ly::LDTILE);
-    const float* dt = l2t + kBQ;
-    const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + kBQ > N) || (kw0 + 32 > N);
-    bf16x8 pf[4], dsf[4];
-    char* dsw = smem + Ly::OFF_DS + buf * Ly::DSTILE + ds_row * Ly::DSROWB + half * 8;  // + chunk * 16
+  // One tile: phase A, then phase B with the VALU groups of step u + 1
+  // riding on the MFMAs of step u (groups 0 and 1 run before step 0).
+  auto iteration = [&](int it, auto mask_c) {
+    const int b = ring(it);
+    if (it + 2 < nqt) dma_tile(it + 2);
+    const unsigned aq = sbase + Ly::OFF_Q + b * Ly::QTILE;
+    const unsigned ado = sbase + Ly::OFF_DO + b * Ly::QTILE;
+    {
+      const unsigned ast = sbase + Ly::OFF_ST + b * Ly::STTILE + 16 * half;
+      // initial accumulators: register 4 g + e of query block qb holds query
+      // 32 qb + 8 g + 4 half + e
+      f32x4 init[2][2][4];  // [S or dP][qb][g]
+      static_for<8>([&](auto kc) {
+        constexpr int k = decltype(kc)::value, qb = k / 4, g = k % 4;
+        ds_b128f<(32 * qb + 8 * g) * 4>(init[0][qb][g], ast);
+        ds_b128f<(kBQ + 32 * qb + 8 * g) * 4>(init[1][qb][g], ast);
+      });
+      bf16x8 fa[LA];
+      auto issue = [&](auto fc) {
+        constexpr int F = decltype(fc)::value, qb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
+        ds_b128<0>(fa[F % LA], (X ? ado : aq) + (rf_lane[qb] ^ (unsigned)(t << 5)));
+      };
+      static_for<LA>(issue);
+      asm volatile("s_waitcnt lgkmcnt(%16)"
+                   : "+v"(init[0][0][0]), "+v"(init[0][0][1]), "+v"(init[0][0][2]), "+v"(init[0][0][3]),
+                     "+v"(init[0][1][0]), "+v"(init[0][1][1]), "+v"(init[0][1][2]), "+v"(init[0][1][3]),
+                     "+v"(init[1][0][0]), "+v"(init[1][0][1]), "+v"(init[1][0][2]), "+v"(init[1][0][3]),
+                     "+v"(init[1][1][0]), "+v"(init[1][1][1]), "+v"(init[1][1][2]), "+v"(init[1][1][3])
+                   : "i"(LA));
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      unsigned pw[8], dw[8];
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *(const f32x4*)(l2t + 32 * qb + 8 * g + 4 * half);
-        const f32x4 d4 = *(const f32x4*)(dt + 32 * qb + 8 * g + 4 * half);
-        float p[4], ds[4];
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float pe = __builtin_amdgcn_exp2f(fmaf(s[qb][r], c, -l4[e]));
-          if (need_mask) {
-            const int qi = q0 + 32 * qb + 8 * g + 4 * half + e;
-            const bool vis = qi < N && key < N && (!CAUSAL || key <= qi);
-            pe = vis ? pe : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            S[qb][4 * g + e] = init[0][qb][g][e];
+            dP[qb][4 * g + e] = init[1][qb][g][e];
           }
-          p[e] = pe;
-          ds[e] = pe * (dp[qb][r] - d4[e]);
+      static_for<NA>([&](auto fc) {
+        constexpr int F = decltype(fc)::value, qb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
+        constexpr int last = (F + LA - 1 < NA - 1) ? F + LA - 1 : NA - 1;
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fa[F % LA]) : "i"(last - F));
+        if constexpr (X == 0)
+          S[qb] = mfma(fa[F % LA], kf[t], S[qb]);
+        else
+          dP[qb] = mfma(fa[F % LA], vf[t], dP[qb]);
+        if constexpr (F + LA < NA) issue(ic<F + LA>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    vgroup(ic<0>{}, mask_c, it);
+    vgroup(ic<1>{}, mask_c, it);
+    {
+      s16x4 lo_[LB], hi_[LB];
+      auto issue = [&](auto fc) {
+        constexpr int F = decltype(fc)::value, u = F / (2 * DB), bb = (F / 2) % DB, X = F % 2;
+        const unsigned a = X ? aq : ado;
+        ds_tr64<u * 16 * ROWB>(lo_[F % LB], a + trq[bb][0]);
+        ds_tr64<u * 16 * ROWB>(hi_[F % LB], a + trq[bb][1]);
+      };
+      static_for<LB>(issue);
+      static_for<NB>([&](auto fc) {
+        constexpr int F = decltype(fc)::value, u = F / (2 * DB), bb = (F / 2) % DB, X = F % 2;
+        constexpr int last = (F + LB - 1 < NB - 1) ? F + LB - 1 : NB - 1;
+        constexpr int qb = u / 2, h2 = u % 2;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo_[F % LB]), "+v"(hi_[F % LB]) : "i"(2 * (last - F)));
+        if constexpr (X == 0) {
+          const bf16x8 pf = __builtin_bit_cast(
+              bf16x8, (u32x4){pw[qb][4 * h2], pw[qb][4 * h2 + 1], pw[qb][4 * h2 + 2], pw[qb][4 * h2 + 3]});
+          dvT[bb] = mfma(join(lo_[F % LB], hi_[F % LB]), pf, dvT[bb]);
+        } else {
+          const bf16x8 dsf = __builtin_bit_cast(
+              bf16x8, (u32x4){dw[qb][4 * h2], dw[qb][4 * h2 + 1], dw[qb][4 * h2 + 2], dw[qb][4 * h2 + 3]});
+          dkT[bb] = mfma(join(lo_[F % LB], hi_[F % LB]), dsf, dkT[bb]);
         }
-        pw[2 * g] = pack_bf16(p[0], p[1]);
-        pw[2 * g + 1] = pack_bf16(p[2], p[3]);
-        dw[2 * g] = pack_bf16(ds[0], ds[1]);
-        dw[2 * g + 1] = pack_bf16(ds[2], ds[3]);
-        // dS^T row `ds_row`, queries 32 qb + 8 g + 4 half + {0..3}: chunk 4 qb + g
-        *(uint2*)(dsw + (((4 * qb + g) ^ ds_mask) << 4)) = make_uint2(dw[2 * g], dw[2 * g + 1]);
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        pf[2 * qb + h2] = __builtin_bit_cast(bf16x8, (u32x4){pw[4 * h2], pw[4 * h2 + 1], pw[4 * h2 + 2], pw[4 * h2 + 3]});
-        dsf[2 * qb + h2] = __builtin_bit_cast(bf16x8, (u32x4){dw[4 * h2], dw[4 * h2 + 1], dw[4 * h2 + 2], dw[4 * h2 + 3]});
-      }
+        if constexpr (F + LB < NB) issue(ic<F + LB>{});
+        // groups 2 (u + 1) and 2 (u + 1) + 1 after the first and second half
+        // of step u's MFMAs
+        constexpr int per = 2 * DB, f = F % per;
+        if constexpr (u < 3 && (f == per / 2 - 1 || f == per - 1))
+          vgroup(ic<2 * (u + 1) + (f == per - 1 ? 1 : 0)>{}, mask_c, it);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    dma_barrier();
+  };
 
-    // dV^T += dO^T P and dK^T += Q^T dS over four 16-query steps.
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const bf16x8 a = tr_frag(dot + u * 16 * ROWB + trq_off[b][0], dot + u * 16 * ROWB + trq_off[b][1]);
-        dvT[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], dvT[b], 0, 0, 0);
-      }
-#pragma unroll
-      for (int b = 0; b < DB; ++b) {
-        const bf16x8 a = tr_frag(qt + u * 16 * ROWB + trq_off[b][0], qt + u * 16 * ROWB + trq_off[b][1]);
-        dkT[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[u], dkT[b], 0, 0, 0);
-      }
-    }
+  // Tiles [it0, it_s) and [it_e, nqt) may hide scores (the causal diagonal,
+  // the ragged end); tiles in between need no mask for any wave.
+  const int it_s = CAUSAL ? min(it0 + 2, nqt) : 0;
+  int it_e = kb0 + kBKV <= N ? N / kBQ : 0;
+  it_e = max(it_e, it_s);
 
-    if (it + 1 < nqt) lstore(buf ^ 1);
-    __syncthreads();
-  }
-  dq_step(nqt - 1, (nqt - 1 - it0) & 1);
+  dma_tile(it0);
+  if (it0 + 1 < nqt) dma_tile(it0 + 1);
+  dma_barrier();
+  int it = it0;
+  for (; it < it_s; ++it) iteration(it, std::true_type{});
+  for (; it < it_e; ++it) iteration(it, std::false_type{});
+  for (; it < nqt; ++it) iteration(it, std::true_type{});
 
-  // ---- dK = scale * dK^T^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
+  // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
   if (key < N) {
     __bf16* dkrow = dKg + head + (size_t)key * D + 4 * half;
     __bf16* dvrow = dVg + head + (size_t)key * D + 4 * half;
@@ -432,39 +457,265 @@ void bwd_main_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   }
 }
 
+// ---------------------------------------------------------------------------
+// bwd_dq.
+template <int D>
+struct DqLayout {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int KTILE = kBKdq * ROWB;  // one K or V tile
+  static constexpr int OFF_K = 0;
+  static constexpr int OFF_V = OFF_K + kRing * KTILE;
+  static constexpr int TOTAL = OFF_V + kRing * KTILE;
+  static_assert(TOTAL <= 160 * 1024, "fits the 160 KiB LDS");
+};
+
+// Per 64-key tile and wave (32 queries; lane = query, registers = keys):
+//   A  S^T = K Q^T - L/scale and dP^T = V dO^T - D  (4 DT MFMAs; row
+//      fragments of the K and V tiles; Q and dO fragments resident);
+//   V  P = 2^(c S^T), dS^T = P dP^T, packed to bf16;
+//   C  dQ^T += K^T dS^T                               (4 DB MFMAs, transposing reads).
+// Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
+                   const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
+                   __bf16* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale) {
+  using Ly = DqLayout<D>;
+  constexpr int DT = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int ROWB = Ly::ROWB;
+  constexpr int NA = 4 * DT;  // phase A MFMAs
+  constexpr int LA = 4;
+  constexpr int NC = 4 * DB;  // phase C MFMAs
+  constexpr int LC = 4;
+  static_assert(NA % 8 == 0, "eight VALU groups ride on the phase A MFMAs");
+  __shared__ __attribute__((aligned(1024))) char smem[Ly::TOTAL];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int bh, qb;
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);  // causal: the longest blocks first
+  const int q0 = qb * kBQdq;
+  const int qw = q0 + 32 * wave;
+  const int qi = qw + col;  // this lane's query (MFMA column)
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const __bf16* Qh = Qg + head;
+  const __bf16* Kh = Kg + head;
+  const __bf16* Vh = Vg + head;
+  const __bf16* dOh = dOg + head;
+
+  // Q and dO fragments of the wave's queries: B operands of S^T = K Q^T and
+  // dP^T = V dO^T (lane: query `col`, d = 16t + 8 half .. + 7).
+  bf16x8 qf[DT], dof[DT];
+  {
+    const size_t r = (size_t)min(qi, N - 1) * D + half * 8;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      qf[t] = *(const bf16x8*)(Qh + r + 16 * t);
+      dof[t] = *(const bf16x8*)(dOh + r + 16 * t);
+    }
+  }
+  const int qs = min(qi, Npad - 1);
+  const float ls = Lsg[(size_t)bh * Npad + qs];  // -L / scale
+  const float dn = Dng[(size_t)bh * Npad + qs];  // -D
+
+  int nkt = (N + kBKdq - 1) / kBKdq;
+  if (CAUSAL) nkt = min(nkt, (q0 + kBQdq - 1) / kBKdq + 1);
+  auto ring = [&](int j) { return __builtin_amdgcn_readfirstlane(j % kRing); };
+  auto dma_tile = [&](int j) {
+    const int b = ring(j);
+    dma_rows<D, kBKdq>(Kh, j * kBKdq, N, smem + Ly::OFF_K + b * Ly::KTILE, wave, lane);
+    dma_rows<D, kBKdq>(Vh, j * kBKdq, N, smem + Ly::OFF_V + b * Ly::KTILE, wave, lane);
+  };
+
+  unsigned rf_lane[2];  // K / V row fragments: row 32 kb + col, chunk 2t + half
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = 32 * kb + col;
+    rf_lane[kb] = (unsigned)(r * ROWB + ((half ^ swz_mask<ROWB>(r)) << 4));
+  }
+  unsigned trk[DB][2];  // K^T transposing reads
+  {
+    const int tr_e = (lane & 15) >> 2, tr_t = lane & 3, tr_cg = (lane >> 4) & 1;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * half + tr_e + 8 * hi;
+        const int chunk = 4 * b + 2 * tr_cg + (tr_t >> 1);
+        trk[b][hi] = (unsigned)(r * ROWB + ((chunk ^ swz_mask<ROWB>(r)) << 4) + (tr_t & 1) * 8);
+      }
+  }
+  const unsigned sbase = lds_addr(smem);
+
+  f32x16 dqT[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) dqT[b] = f32x16{};
+  f32x16 S[2], dP[2];  // [32-key half]
+  unsigned dw[2][8];
+
+  // visible iff key <= qi (causal) and key < N: key <= hi_key
+  const int hi_key = CAUSAL ? min(qi, N - 1) : N - 1;
+
+  // VALU group k: dS^T of key half k / 4, rows 8 (k % 4) + 4 half + {0..3},
+  // i.e. the bf16 pairs of 16-key step k / 2 of phase C.
+  auto vgroup = [&](auto kc, auto mask_c, int j) {
+    constexpr int k = decltype(kc)::value, kb = k / 4, g = k % 4;
+    constexpr bool MASK = decltype(mask_c)::value;
+    float ds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float pe = __builtin_amdgcn_exp2f(S[kb][4 * g + e] * c);
+      if constexpr (MASK) {
+        const int kk = j * kBKdq + 32 * kb + 8 * g + 4 * half + e;
+        const unsigned keep = ~(unsigned)((hi_key - kk) >> 31);
+        pe = __uint_as_float(__float_as_uint(pe) & keep);
+      }
+      ds[e] = pe * dP[kb][4 * g + e];
+    }
+    dw[kb][2 * g] = pack_bf16(ds[0], ds[1]);
+    dw[kb][2 * g + 1] = pack_bf16(ds[2], ds[3]);
+  };
+
+  auto iteration = [&](int j, auto mask_c) {
+    const int b = ring(j);
+    if (j + 2 < nkt) dma_tile(j + 2);
+    const unsigned ak = sbase + Ly::OFF_K + b * Ly::KTILE;
+    const unsigned av = sbase + Ly::OFF_V + b * Ly::KTILE;
+    {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[kb][r] = ls;
+          dP[kb][r] = dn;
+        }
+      bf16x8 fa[LA];
+      auto issue = [&](auto fc) {
+        constexpr int F = decltype(fc)::value, kb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
+        ds_b128<0>(fa[F % LA], (X ? av : ak) + (rf_lane[kb] ^ (unsigned)(t << 5)));
+      };
+      static_for<LA>(issue);
+      static_for<NA>([&](auto fc) {
+        constexpr int F = decltype(fc)::value, kb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
+        constexpr int last = (F + LA - 1 < NA - 1) ? F + LA - 1 : NA - 1;
+        asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fa[F % LA]) : "i"(last - F));
+        if constexpr (X == 0)
+          S[kb] = mfma(fa[F % LA], qf[t], S[kb]);
+        else
+          dP[kb] = mfma(fa[F % LA], dof[t], dP[kb]);
+        if constexpr (F + LA < NA) issue(ic<F + LA>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    vgroup(ic<0>{}, mask_c, j);
+    vgroup(ic<1>{}, mask_c, j);
+    {
+      s16x4 lo_[LC], hi_[LC];
+      auto issue = [&](auto fc) {
+        constexpr int F = decltype(fc)::value, u = F / DB, bb = F % DB;
+        ds_tr64<u * 16 * ROWB>(lo_[F % LC], ak + trk[bb][0]);
+        ds_tr64<u * 16 * ROWB>(hi_[F % LC], ak + trk[bb][1]);
+      };
+      static_for<LC>(issue);
+      static_for<NC>([&](auto fc) {
+        constexpr int F = decltype(fc)::value, u = F / DB, bb = F % DB;
+        constexpr int last = (F + LC - 1 < NC - 1) ? F + LC - 1 : NC - 1;
+        constexpr int kb = u / 2, h2 = u % 2;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo_[F % LC]), "+v"(hi_[F % LC]) : "i"(2 * (last - F)));
+        const bf16x8 dsf = __builtin_bit_cast(
+            bf16x8, (u32x4){dw[kb][4 * h2], dw[kb][4 * h2 + 1], dw[kb][4 * h2 + 2], dw[kb][4 * h2 + 3]});
+        dqT[bb] = mfma(join(lo_[F % LC], hi_[F % LC]), dsf, dqT[bb]);
+        if constexpr (F + LC < NC) issue(ic<F + LC>{});
+        // groups 2 (u + 1) and 2 (u + 1) + 1 ride on step u's MFMAs
+        constexpr int f = F % DB;
+        if constexpr (u < 3 && DB >= 2 && (f == DB / 2 - 1 || f == DB - 1))
+          vgroup(ic<2 * (u + 1) + (f == DB - 1 ? 1 : 0)>{}, mask_c, j);
+        if constexpr (u < 3 && DB == 1) {
+          vgroup(ic<2 * (u + 1)>{}, mask_c, j);
+          vgroup(ic<2 * (u + 1) + 1>{}, mask_c, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    dma_barrier();
+  };
+
+  // Key tiles [0, j_e) need no mask for any wave: every key precedes every
+  // query of the workgroup (causal) and lies inside the sequence.
+  int j_e = N / kBKdq;
+  if (CAUSAL) j_e = min(j_e, q0 / kBKdq);
+  j_e = max(0, min(j_e, nkt));
+
+  dma_tile(0);
+  if (1 < nkt) dma_tile(1);
+  dma_barrier();
+  int j = 0;
+  for (; j < j_e; ++j) iteration(j, std::false_type{});
+  for (; j < nkt; ++j) iteration(j, std::true_type{});
+
+  // ---- dQ = scale * (dQ^T)^T: lane writes query qi, d = 32 b + 8 g + 4 half + {0..3}.
+  if (qi < N) {
+    __bf16* row = dQg + head + (size_t)qi * D + 4 * half;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(dqT[b][4 * g + e] * scale);
+        *(bf16x4*)(row + 32 * b + 8 * g) = o;
+      }
+  }
+}
+
 template <int D>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int npad = (p.N + kBQ - 1) / kBQ * kBQ;
-  float* dqacc = (float*)p.workspace;
-  float* l2 = dqacc + (size_t)p.BH * npad * D;
-  float* dv = l2 + (size_t)p.BH * npad;
+  // P = 2^(c (q.k - L / scale)) with c = scale log2(e).  |c| is kept at
+  // least 1e-30 so that L / scale stays finite; below that every
+  // c q.k rounds to 0 anyway and P = e^-L as for scale = 0.
+  float c = p.scale * kLog2e;
+  if (fabsf(c) < 1e-30f) c = c < 0.f ? -1e-30f : 1e-30f;
+  float* ls = (float*)p.workspace;
+  float* dn = ls + (size_t)p.BH * npad;
+  const __bf16* q = (const __bf16*)p.q;
+  const __bf16* k = (const __bf16*)p.k;
+  const __bf16* v = (const __bf16*)p.v;
+  const __bf16* dout = (const __bf16*)p.dout;
   {
     constexpr int RPB = 256 / (D / 8);
     const size_t rows = (size_t)p.BH * npad;  // a multiple of RPB
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(rows / RPB)), dim3(256), 0, stream,
-                       (const __bf16*)p.o, (const __bf16*)p.dout, p.lse, dqacc, l2, dv, p.N, npad);
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(rows / RPB)), dim3(256), 0, stream, (const __bf16*)p.o,
+                       dout, p.lse, ls, dn, p.N, npad, kLog2e / c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     const int nkb = (p.N + kBKV - 1) / kBKV;
-    const float c = p.scale * kLog2e;
     const dim3 grid((unsigned)(p.BH * nkb)), block(kThreads);
     if (p.causal)
-      hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, block, 0, stream, (const __bf16*)p.q, (const __bf16*)p.k,
-                         (const __bf16*)p.v, (const __bf16*)p.dout, l2, dv, dqacc, (__bf16*)p.dk, (__bf16*)p.dv,
-                         p.BH, p.N, npad, nkb, c, p.scale);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
+                         (__bf16*)p.dv, p.BH, p.N, npad, nkb, c, p.scale);
     else
-      hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, block, 0, stream, (const __bf16*)p.q, (const __bf16*)p.k,
-                         (const __bf16*)p.v, (const __bf16*)p.dout, l2, dv, dqacc, (__bf16*)p.dk, (__bf16*)p.dv,
-                         p.BH, p.N, npad, nkb, c, p.scale);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
+                         (__bf16*)p.dv, p.BH, p.N, npad, nkb, c, p.scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    const size_t total8 = (size_t)p.BH * p.N * D / 8;
-    hipLaunchKernelGGL(bwd_post_kernel<D>, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, stream, dqacc,
-                       (__bf16*)p.dq, p.N, npad, total8, p.scale);
+    const int nqb = (p.N + kBQdq - 1) / kBQdq;
+    const dim3 grid((unsigned)(p.BH * nqb)), block(kThreads);
+    if (p.causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
+                         p.BH, p.N, npad, nqb, c, p.scale);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
+                         p.BH, p.N, npad, nqb, c, p.scale);
     return hipGetLastError();
   }
 }
@@ -472,8 +723,9 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t bwd_workspace_bytes(int BH, int N, int d) {
+  (void)d;
   const size_t npad = ((size_t)N + kBQ - 1) / kBQ * kBQ;
-  return (size_t)BH * npad * ((size_t)d + 2) * sizeof(float);
+  return (size_t)BH * npad * 2 * sizeof(float);
 }
 
 int bwd_block_k() { return kBKV; }

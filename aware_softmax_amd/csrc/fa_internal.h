@@ -56,10 +56,10 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 
-// Backward workspace: fp32 dQ accumulator [BH][Npad][d], then L (log2
-// units) and D, [BH][Npad] each; Npad = N rounded up to the query tile.
+// Backward workspace: -L/scale and -D, fp32 [BH][Npad] each; Npad = N
+// rounded up to the query tile of the dK/dV pass.
 size_t bwd_workspace_bytes(int BH, int N, int d);
-int bwd_block_k();  // keys per backward workgroup
-int bwd_block_q();  // queries per streamed backward tile
+int bwd_block_k();  // keys per workgroup of the dK/dV pass
+int bwd_block_q();  // queries per streamed tile of the dK/dV pass
 
 }  // namespace fa

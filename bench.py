@@ -137,7 +137,7 @@ def time_backward(fa, w, q, k, v, o, lse, steps, warmup):
     ms = t0.elapsed_time(t1) / steps
     f = 2.5 * attention_flops(w.B, w.H, w.N, w.d, w.causal)
     return {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2),
-            "flops_per_call": f, "kernels": "bwd_pre + bwd_main + bwd_post"}
+            "flops_per_call": f, "kernels": "bwd_pre + bwd_dkdv + bwd_dq"}
 
 
 def cpu_baseline(w, budget_s=12.0, rows_per_head=512):

@@ -94,8 +94,8 @@ fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int
 
 /*
  * fa_bwd_workspace_bytes -- size of the device workspace fa_bwd needs for
- * these sizes: an fp32 dQ accumulator of [B][H][Npad][d] plus two fp32
- * [B][H][Npad] row vectors, Npad = N rounded up to a multiple of 64.
+ * these sizes: two fp32 [B][H][Npad] row vectors (the row statistics D and
+ * L / scale of every query), Npad = N rounded up to a multiple of 64.
  * Host-only; makes no HIP call.  Returns 0 for non-positive sizes or an
  * unsupported head dimension.
  */
@@ -109,11 +109,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * Finish Sooner": the backward does not read a stored S or P; it rebuilds
  * P = exp(scale Q K^T + mask - L) tile by tile on chip from Q, K and the
  * row statistic L of the forward ("FlashAttention-2: ...", "FA2 change #1").
- * "FA2 change #2", last paragraph: the work is split over key columns, each
- * worker owning dK_j and dV_j, and the dQ rows shared by all workers are
- * accumulated with atomic adds (here into the fp32 workspace, converted to
- * dQ at the end).  With D_i = dO_i . O_i and dS = P * (dO V^T - D):
+ * With D_i = dO_i . O_i and dS = P * (dO V^T - D):
  *     dV = P^T dO,   dK = scale dS^T Q,   dQ = scale dS K.
+ * "FA2 change #2", last paragraph, splits the work over key columns (each
+ * worker owning dK_j, dV_j) and accumulates dQ with atomic adds; here dK
+ * and dV are formed that way, and dQ by a second, query-parallel pass that
+ * rebuilds P and dP for its rows instead of atomics (no atomics at all).
  *
  *   q, k, v, o, dout  [in]  device, [B][H][N][d] bf16, 16-byte aligned; o is
  *                     the forward output for the same q, k, v, causal, scale.
@@ -123,14 +124,12 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   workspace [scratch] device, at least fa_bwd_workspace_bytes(B, H, N, d)
  *                     bytes (passed as workspace_bytes), 256-byte aligned,
  *                     owned by the caller; overwritten, contents undefined
- *                     afterwards.  It is cleared by the call itself, so it
- *                     needs no initialisation.
+ *                     afterwards.  It needs no initialisation.
  *   B, H, N, d, causal, scale   as for fa_fwd.
  *   dtype     FA_DTYPE_BF16 only (FA_DTYPE_F32 returns FA_ERR_DTYPE).
  *   stream    HIP stream; three kernels are enqueued in order on it.
- * Returns FA_OK or the first failed check.  Accumulation order of dQ
- * depends on the order of the atomic adds, so dQ may differ in the last
- * bits between runs; dK and dV are deterministic.
+ * Returns FA_OK or the first failed check.  The outputs are deterministic:
+ * the same inputs give bitwise identical dq, dk and dv.
  */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -138,8 +137,9 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    hipStream_t stream);
 
 /*
- * fa_bwd_tile -- keys per backward workgroup and queries per streamed tile.
- * Host-only.  Returns FA_OK or FA_ERR_NULL / FA_ERR_UNSUPPORTED_HEADDIM.
+ * fa_bwd_tile -- keys per workgroup of the dK/dV pass and queries per
+ * streamed tile of it.  Host-only.  Returns FA_OK or FA_ERR_NULL /
+ * FA_ERR_UNSUPPORTED_HEADDIM.
  */
 fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q);
 

@@ -153,7 +153,7 @@ int main() {
 W = A + 0x8000000  # fake workspace address (256-byte aligned)
 BGOOD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000,
              do=A + 0x5000000, dq=A + 0x6000000, dk=A + 0x7000000, dv=A + 0x7800000, ws=W,
-             ws_bytes=1 << 26, B=1, H=2, N=64, d=64, causal=1, scale=0.125, dtype=1, stream=None)
+             ws_bytes=1 << 20, B=1, H=2, N=64, d=64, causal=1, scale=0.125, dtype=1, stream=None)
 
 
 def bcall(fa, **over):
@@ -165,10 +165,10 @@ def bcall(fa, **over):
 
 
 def test_bwd_workspace_bytes(fa):
-    # fp32 dQ accumulator over N rounded up to 64 rows, plus two fp32 row vectors
-    assert fa.bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * (128 + 2) * 4
-    assert fa.bwd_workspace_bytes(1, 2, 65, 64) == 2 * 128 * (64 + 2) * 4
-    assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 64 * 130 * 4
+    # two fp32 row vectors over N rounded up to 64 rows
+    assert fa.bwd_workspace_bytes(2, 16, 4096, 128) == 2 * 16 * 4096 * 2 * 4
+    assert fa.bwd_workspace_bytes(1, 2, 65, 64) == 2 * 128 * 2 * 4
+    assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 64 * 2 * 4
     for bad in ((0, 1, 64, 64), (1, 1, 0, 64), (1, 1, 64, 96), (1, -1, 64, 128)):
         assert fa.bwd_workspace_bytes(*bad) == 0
     bk, bq = fa.bwd_tile_config(128)
@@ -185,7 +185,7 @@ def test_bwd_workspace_bytes(fa):
     (dict(do=A + 0x5000008), 5), (dict(dk=A + 0x7000002), 5), (dict(lse=A + 0x4000001), 5),
     (dict(scale=float("nan")), 6), (dict(scale=float("-inf")), 6),
     (dict(dq=A), 8), (dict(dv=A + 0x7000100), 8), (dict(ws=A + 0x6000000), 8), (dict(dk=W + 0x100), 8),
-    (dict(ws=0), 9), (dict(ws=W + 16), 9), (dict(ws_bytes=1000), 9),
+    (dict(ws=0), 9), (dict(ws=W + 16), 9), (dict(ws_bytes=1000), 9), (dict(ws_bytes=1023), 9),
 ])
 def test_bwd_validation_rejects_before_launch(fa, over, code):
     assert bcall(fa, **over) == code
