@@ -135,9 +135,14 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-// Waits until this wave's LDS-DMA copies and LDS operations are complete,
-// then the workgroup barrier.
-__device__ __forceinline__ void dma_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Waits until all but this wave's last KEEP vector memory operations (the
+// LDS-DMA copies of the tile after next, issued this iteration) and all its
+// LDS operations are complete, then the workgroup barrier.  Vector memory
+// operations of a wave complete in issue order.
+template <int KEEP>
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(KEEP) : "memory");
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -265,11 +270,14 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int nqt = Npad / kBQ;
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
   auto ring = [&](int it) { return __builtin_amdgcn_readfirstlane((it - it0) % kRing); };
+  constexpr int kDmaPerWave = 1 + 2 * (Ly::QTILE / 1024 / kWaves);  // statistics, Q, dO
   auto dma_tile = [&](int it) {
     const int b = ring(it);
-    if (wave < 2)  // the tile's 64 statistics: -L/scale by wave 0, -D by wave 1
-      __builtin_amdgcn_global_load_lds((const void*)((wave == 0 ? Lsh : Dnh) + it * kBQ + lane),
-                                       (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + wave * 4 * kBQ), 4, 0, 0);
+    // the tile's 64 statistics: -L/scale by waves 0 and 2, -D by waves 1
+    // and 3 (the duplicate copy writes the same bytes; it keeps the number
+    // of DMA instructions per wave uniform for the waits)
+    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dnh : Lsh) + it * kBQ + lane),
+                                     (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + (wave & 1) * 4 * kBQ), 4, 0, 0);
     dma_rows<D, kBQ>(Qh, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
     dma_rows<D, kBQ>(dOh, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
   };
@@ -420,7 +428,11 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    dma_barrier();
+    // tile it + 1 must be complete; the copies of tile it + 2 stay in flight
+    if (it + 2 < nqt)
+      dma_barrier<kDmaPerWave>();
+    else
+      dma_barrier<0>();
   };
 
   // Tiles [it0, it_s) and [it_e, nqt) may hide scores (the causal diagonal,
@@ -430,8 +442,12 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   it_e = max(it_e, it_s);
 
   dma_tile(it0);
-  if (it0 + 1 < nqt) dma_tile(it0 + 1);
-  dma_barrier();
+  if (it0 + 1 < nqt) {
+    dma_tile(it0 + 1);
+    dma_barrier<kDmaPerWave>();
+  } else {
+    dma_barrier<0>();
+  }
   int it = it0;
   for (; it < it_s; ++it) iteration(it, std::true_type{});
   for (; it < it_e; ++it) iteration(it, std::false_type{});
@@ -526,6 +542,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
   int nkt = (N + kBKdq - 1) / kBKdq;
   if (CAUSAL) nkt = min(nkt, (q0 + kBQdq - 1) / kBKdq + 1);
   auto ring = [&](int j) { return __builtin_amdgcn_readfirstlane(j % kRing); };
+  constexpr int kDmaPerWave = 2 * (Ly::KTILE / 1024 / kWaves);  // K, V
   auto dma_tile = [&](int j) {
     const int b = ring(j);
     dma_rows<D, kBKdq>(Kh, j * kBKdq, N, smem + Ly::OFF_K + b * Ly::KTILE, wave, lane);
@@ -642,7 +659,11 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    dma_barrier();
+    // tile j + 1 must be complete; the copies of tile j + 2 stay in flight
+    if (j + 2 < nkt)
+      dma_barrier<kDmaPerWave>();
+    else
+      dma_barrier<0>();
   };
 
   // Key tiles [0, j_e) need no mask for any wave: every key precedes every
@@ -652,8 +673,12 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
   j_e = max(0, min(j_e, nkt));
 
   dma_tile(0);
-  if (1 < nkt) dma_tile(1);
-  dma_barrier();
+  if (1 < nkt) {
+    dma_tile(1);
+    dma_barrier<kDmaPerWave>();
+  } else {
+    dma_barrier<0>();
+  }
   int j = 0;
   for (; j < j_e; ++j) iteration(j, std::false_type{});
   for (; j < nkt; ++j) iteration(j, std::true_type{});

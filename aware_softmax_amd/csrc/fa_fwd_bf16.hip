@@ -33,8 +33,8 @@
 //     through registers into padded, double-buffered LDS rows;
 //   * d = 128 ("duo"): 8 waves (two per SIMD), 256 query rows, K/V tiles
 //     copied HBM -> LDS by LDS-DMA into XOR-swizzled rings, every MFMA
-//     followed by a slot of softmax VALU work, the two waves of a SIMD
-//     staggered by half an iteration, lazy rescaling of O.
+//     followed by a slot of softmax VALU work; steady tiles skip the row
+//     max (fixed reference max with an overflow check, see below).
 #include <math.h>
 #include <stdlib.h>
 
@@ -372,78 +372,62 @@ __device__ __forceinline__ void read_k(bf16x8& f, unsigned addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
 
-// Online softmax of one unmasked 32-row block split into 32 slots, one per
-// MFMA.  Inputs of every slot were produced at least one slot earlier, so a
-// slot issues without waiting on its own results:
-//   0-3   partial row max over 8 scores each
-//   4     row max across the lane pair (permlane32 swap)
-//   5     reference max m (raised only by more than kRaise), alpha
-//   6-21  t = s*c - m for score pair k = slot - 6
-//   7-22  p = 2^t for pair slot - 7
-//   8-23  pack pair slot - 8 to bf16, add to a partial row sum
-//   24-25 row sum l = alpha*l + sum
-struct Softmax {
-  float mx[4];
-  float mrow;
-  float m_use, alpha;
+// Update of one unmasked tile against the current reference max m, with no
+// per-tile max at all.  O = O~/l and L = m + log l hold for any reference m
+// ("FlashAttention: Move Less, Not Compute Less", "Tiling Is Easy"); m only
+// has to keep 2^(s c - m) in range.  It is set from a real row max on the
+// row's first tile and raised only when a tile's probabilities overflow the
+// budget checked in fast_finish, so it never exceeds the running row max by
+// more than the raise slack and nothing underflows.  The 16 score pairs go
+// through three stages spread over the 32 MFMA slots of an interval:
+//   slot 2r:     t = s c - m of pair r, and pack + row-sum pair r - 1;
+//   slot 2r + 1: p = 2^t of pair r;
+// pair 15 is packed by fast_finish.
+struct FastSoftmax {
   float t[2], p[2];
   float ps[4];
   unsigned w[16];
 };
 
 template <int K>
-__device__ __forceinline__ void softmax_slot(Softmax& st, const f32x16 (&s)[2], float c, float& m_run,
-                                             float& l_part) {
+__device__ __forceinline__ void fast_slot(FastSoftmax& st, const f32x16 (&s)[2], float c, float m) {
   auto sv = [&](int i) { return s[i >> 4][i & 15]; };
-  if constexpr (K < 4) {
-    st.mx[K] = fmaxf(fmaxf(fmaxf(sv(8 * K), sv(8 * K + 1)), fmaxf(sv(8 * K + 2), sv(8 * K + 3))),
-                     fmaxf(fmaxf(sv(8 * K + 4), sv(8 * K + 5)), fmaxf(sv(8 * K + 6), sv(8 * K + 7))));
-    asm volatile("" ::"v"(st.mx[K]));
-  } else if constexpr (K == 4) {
-    st.mrow = swap_halves(fmaxf(fmaxf(st.mx[0], st.mx[1]), fmaxf(st.mx[2], st.mx[3])), true);
-    asm volatile("" ::"v"(st.mrow));
-  } else if constexpr (K == 5) {
-    const float m_tile = st.mrow * c;
-    const bool raise = m_tile > m_run + kRaise;
-    st.m_use = raise ? m_tile : m_run;
-    st.alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
-    m_run = st.m_use;
-    st.ps[0] = st.ps[1] = st.ps[2] = st.ps[3] = 0.f;
-    asm volatile("" ::"v"(st.m_use), "v"(st.alpha));
-  } else if constexpr (K >= 6 && K <= 25) {
-    // pack first (oldest pair), then exponentiate, then scale-and-shift the
-    // next pair, so the three steps in one slot are independent.
-    if constexpr (K >= 8 && K <= 23) {
-      constexpr int k = K - 8;
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  constexpr int r = K / 2;
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  if constexpr (K % 2 == 0) {
+    if constexpr (r >= 1) {
+      constexpr int q = r - 1;
       const bf16x2 pr = __builtin_convertvector((f32x2){st.p[0], st.p[1]}, bf16x2);
-      st.ps[k & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.ps[k & 3], false);
-      st.w[k] = __builtin_bit_cast(unsigned, pr);
-      asm volatile("" ::"v"(st.w[k]), "v"(st.ps[k & 3]));
+      st.ps[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, q < 4 ? 0.f : st.ps[q & 3], false);
+      st.w[q] = __builtin_bit_cast(unsigned, pr);
+      asm volatile("" ::"v"(st.w[q]), "v"(st.ps[q & 3]));
     }
-    if constexpr (K >= 7 && K <= 22) {
-      st.p[0] = __builtin_amdgcn_exp2f(st.t[0]);
-      st.p[1] = __builtin_amdgcn_exp2f(st.t[1]);
-      asm volatile("" ::"v"(st.p[0]), "v"(st.p[1]));
-    }
-    if constexpr (K >= 6 && K <= 21) {
-      constexpr int k = K - 6;
-      st.t[0] = fmaf(sv(2 * k), c, -st.m_use);
-      st.t[1] = fmaf(sv(2 * k + 1), c, -st.m_use);
-      asm volatile("" ::"v"(st.t[0]), "v"(st.t[1]));
-    }
-    if constexpr (K == 24) {
-      l_part = l_part * st.alpha + ((st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]));
-      asm volatile("" ::"v"(l_part));
-    }
+    st.t[0] = fmaf(sv(2 * r), c, -m);
+    st.t[1] = fmaf(sv(2 * r + 1), c, -m);
+    asm volatile("" ::"v"(st.t[0]), "v"(st.t[1]));
+  } else {
+    st.p[0] = __builtin_amdgcn_exp2f(st.t[0]);
+    st.p[1] = __builtin_amdgcn_exp2f(st.t[1]);
+    asm volatile("" ::"v"(st.p[0]), "v"(st.p[1]));
   }
 }
 
-__device__ __forceinline__ void softmax_pack(const Softmax& st, bf16x8 (&pfrag)[4]) {
+// Packs pair 15 and returns the lane's partial row sum of the tile.
+__device__ __forceinline__ float fast_finish(FastSoftmax& st, bf16x8 (&pfrag)[4]) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const bf16x2 pr = __builtin_convertvector((f32x2){st.p[0], st.p[1]}, bf16x2);
+  st.ps[3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.ps[3], false);
+  st.w[15] = __builtin_bit_cast(unsigned, pr);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
     pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){st.w[4 * u], st.w[4 * u + 1], st.w[4 * u + 2], st.w[4 * u + 3]});
+  return (st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]);
 }
+
+// Probability budget of a fast tile: a lane's partial row sum above 2^16
+// (or not finite) sends the tile through the exact update instead.  Below
+// it every probability is at most 2^16, so O stays far from fp32 overflow.
+constexpr float kFastBudget = 65536.f;
 
 // Masked tile update in place on the score accumulator.  A score is
 // visible when its key offset (within the lane's keys of the tile) is below
@@ -491,28 +475,31 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
 // wave, 256 per workgroup, one workgroup per CU.
 //
 // Each wave software-pipelines its own tiles: within one barrier interval it
-// runs the 16 P.V MFMAs of one tile and the 16 Q.K MFMAs of another, and
-// the 32 slots of the online softmax of the tile in between ride on those
+// runs the 16 P.V MFMAs of one tile and the 16 Q.K MFMAs of the next, and
+// the 32 slots of the softmax update of the tile in between ride on those
 // MFMAs, one slot of VALU work after each (the matrix unit computes while
-// the exponentials issue).  The two waves of a SIMD are staggered by half an
-// interval, so that one reads V^T fragments while the other reads K ones.
-// The HBM -> LDS copies (LDS-DMA, 1 KiB per wave instruction) are spread
-// over the same MFMAs two intervals ahead of use, into rings of four K and
-// three V tiles; one workgroup barrier per interval.
+// the exponentials issue; the other wave of the SIMD fills the gaps).  The
+// HBM -> LDS copies (LDS-DMA, 1 KiB per wave instruction) are spread over
+// the same MFMAs two intervals ahead of use, into rings of four K and three
+// V tiles; one workgroup barrier per interval.
 //
-// Lazy rescaling: the reference max m of a row moves only when a tile's max
-// exceeds it by more than kRaise (log2 units), so O is rescaled a handful of
-// times per row instead of at every new maximum; in between P = 2^(s*c - m)
-// is at most 2^kRaise.  O = O~/l and L = m + log l do not depend on which
-// reference m was used (the online-softmax identity of "FlashAttention: Move
-// Less, Not Compute Less", "Tiling Is Easy"), so this changes rounding only.
+// The reference max m of a row is not the running max.  O = O~/l and
+// L = m + log l do not depend on which reference m is used (the
+// online-softmax identity of "FlashAttention: Move Less, Not Compute Less",
+// "Tiling Is Easy"); m only has to keep P = 2^(s*c - m) in range.  It is set
+// from the real row max on the first and on masked tiles (raised only when
+// a tile's max exceeds it by more than kRaise), and steady tiles use it as
+// it stands, with no per-tile max: their probabilities are checked after the
+// fact (fast_check) and the rare tile whose row sum exceeds the budget is
+// redone against its real max (fast_redo).  The choice of m changes rounding
+// only.
 namespace duo {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 256;
 constexpr int kLead = 3;
-constexpr int kRingK = 4;  // K ring: tiles read by the two wave groups, one landing, one being written
+constexpr int kRingK = 4;  // K ring: tile being read, one landing, one being written, one spare
 constexpr int kRingV = 3;  // V ring: tile being read, one landing, one being written
 
 // K and V tiles sit unpadded in LDS (rows of D bf16) because the LDS-DMA
@@ -569,7 +556,8 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // -inf * c stays -inf for hidden keys.
   c = fmaxf(c, 1e-30f);
   // Waves w and w + 4 share a SIMD; give them rows 64(w%4) + 32(w/4) so the
-  // two waves of a SIMD meet the causal diagonal at the same tile.
+  // two waves of a SIMD meet the causal diagonal at the same tile (their
+  // numbers of visible tiles differ by at most one).
   const int qw = q0 + (wave & 3) * 64 + (wave >> 2) * 32;
   const int qi = qw + col;
   bf16x8 qf[DT];
@@ -645,12 +633,12 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     return a;
   };
 
-  Softmax st;
+  FastSoftmax fs;
   f32x16 sb[2];  // scores of the tile being normalised (Q.K overwrites sacc)
 
-  // S^T = K Q^T from K buffer kb.  With SM, softmax slots S0..S0+15 of the
-  // scores sc ride along; with DMA, the V DMA of tile dma_t into buffer
-  // dma_b.
+  // S^T = K Q^T from K buffer kb.  With SM, slots S0..S0+15 of the fast
+  // update of the scores sc ride along; with DMA, the V DMA of tile dma_t
+  // into buffer dma_b.
   auto qk = [&](int kb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
     constexpr bool SM = decltype(with_sm)::value;
     constexpr bool DMA = decltype(with_dma)::value;
@@ -671,15 +659,15 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
       else
         sacc[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], sacc[F % 2], 0, 0, 0);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) softmax_slot<S0 + F>(st, sc, c, m_run, l_part);
+      if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_one(Vh, dma_b, dma_t, F / 8, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
-  // O^T += V^T P^T from V buffer vb.  With SM, softmax slots S0..S0+15 of
-  // the scores sc ride along; with DMA, the K DMA of tile dma_t into buffer
-  // dma_b.
+  // O^T += V^T P^T from V buffer vb.  With SM, slots S0..S0+15 of the fast
+  // update of the scores sc ride along; with DMA, the K DMA of tile dma_t
+  // into buffer dma_b.
   auto pv = [&](int vb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
     constexpr bool SM = decltype(with_sm)::value;
     constexpr bool DMA = decltype(with_dma)::value;
@@ -701,7 +689,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
           __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[F % kLead], hi[F % kLead], 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[u], oacc[b], 0, 0, 0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) softmax_slot<S0 + F>(st, sc, c, m_run, l_part);
+      if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_one(Kh, dma_b, dma_t, F / 8, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -715,22 +703,17 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   };
 
   // Interval j (between two workgroup barriers) loads K_{j+3} into the
-  // buffer K_{j-1} left and V_{j+1} into the buffer V_{j-2} left.  The two
-  // waves of a SIMD are staggered by half an interval so that one streams
-  // V^T through the transposing LDS reads while the other streams K:
-  //   waves 0-3, interval j: P_{j-1}V_{j-1} || softmax slots 0-15 of tile j,
-  //                          S_{j+1} = Q K_{j+1}^T || slots 16-31 of tile j
-  //   waves 4-7, interval j: S_j = Q K_j^T || slots 16-31 of tile j-1,
-  //                          P_{j-1}V_{j-1} || slots 0-15 of tile j
-  // (K_{j-1} was last read in interval j-1 by waves 4-7, V_{j-2} in
-  // interval j-1 by both groups).  Slots 0-15 read the scores where Q.K
-  // left them; slots 16-31 a copy, since the next Q.K overwrites them.
+  // buffer K_{j-1} left and V_{j+1} into the buffer V_{j-2} left, and every
+  // wave runs
+  //   P_{j-1} V_{j-1}       || slots 0-15 of the fast update of tile j,
+  //   S_{j+1} = Q K_{j+1}^T || slots 16-31 of tile j.
+  // (K_{j-1} was last read in interval j-2, V_{j-2} in interval j-1.)
+  // Slots 0-15 read the scores where Q.K left them; slots 16-31 a copy,
+  // since the next Q.K overwrites them.
   using S_lo = std::integral_constant<int, 0>;
   using S_hi = std::integral_constant<int, 16>;
   using On = std::true_type;
   using Off = std::false_type;
-  const bool lead = wave < 4;
-  bool pending = false;  // waves 4-7: slots 16-31 of the previous tile still to run
   auto masked_softmax = [&](int j) {
     const int kt0 = j * kBK;
     int lim = N - kt0 - half * 4;
@@ -739,36 +722,58 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     const float alpha = softmax_masked_inplace(sacc, c, lim, m_run, l_part, pfrag);
     rescale(m_before == -INFINITY ? 1.f : alpha);
   };
-  auto finish_pending = [&]() {
-    static_for<16>([&](auto kc) { softmax_slot<16 + decltype(kc)::value>(st, sb, c, m_run, l_part); });
-    softmax_pack(st, pfrag);
-    pending = false;
+  // End of a fast tile whose scores are in sb: P fragments, and the tile's
+  // row sum joins l -- unless a lane's partial sum exceeds the budget (or is
+  // not finite); then fast_check returns true and the caller runs fast_redo
+  // before the tile's P.V.  The redo sits outside the steady loops (they
+  // only exit on it), which keeps their register allocation unchanged.
+  auto fast_check = [&]() -> bool {
+    const float part = fast_finish(fs, pfrag);
+    const bool ovf = __builtin_amdgcn_ballot_w64(!(part <= kFastBudget)) != 0;
+    if (!ovf) l_part += part;
+    return ovf;
+  };
+  // Exact update of the tile in sb: m raised to the row max, P recomputed,
+  // O and l rescaled.
+  auto fast_redo = [&]() {
+    float mx = sb[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sb[i >> 4][i & 15]);
+    const float m_new = fmaxf(m_run, swap_halves(mx, true) * c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float ps[2] = {0.f, 0.f};
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      unsigned w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int i = u * 8 + e;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[i >> 4][i & 15], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[(i + 1) >> 4][(i + 1) & 15], c, -m_run));
+        const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        ps[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[e >> 2], false);
+        w[e >> 1] = __builtin_bit_cast(unsigned, pr);
+      }
+      pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+    }
+    l_part = l_part * alpha + (ps[0] + ps[1]);
+    rescale(alpha);
   };
   // Steady interval: tile j unmasked for every row, 1 <= j, j + 1 < nkt.
-  // The two wave groups run separate loops, so the state waves 4-7 carry
-  // across barriers is not live in the loop of waves 0-3.
-  auto steady_lead = [&](int j) {
+  // Returns true when tile j's probabilities overflowed the budget (P_j
+  // then needs fast_redo before the next interval's P.V).
+  auto steady = [&](int j) -> bool {
     pv(vbuf(j - 1), On{}, On{}, j + 3, kbuf(j + 3), S_lo{}, sacc);
-    rescale(st.alpha);
     sb[0] = sacc[0];
     sb[1] = sacc[1];
     qk(kbuf(j + 1), On{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
-    softmax_pack(st, pfrag);
+    const bool ovf = fast_check();
     iteration_barrier();
+    return ovf;
   };
-  auto steady_follow = [&](int j, auto first) {
-    if constexpr (decltype(first)::value) {
-      qk(kbuf(j), Off{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
-    } else {
-      sb[0] = sacc[0];
-      sb[1] = sacc[1];
-      qk(kbuf(j), On{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
-      softmax_pack(st, pfrag);
-    }
-    pv(vbuf(j - 1), On{}, On{}, j + 3, kbuf(j + 3), S_lo{}, sacc);
-    rescale(st.alpha);
-    iteration_barrier();
-  };
+
   auto dma_all = [&](int j) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
@@ -777,23 +782,11 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     }
   };
   // Any interval (first, masked or last tiles; per-wave tile counts).
-  auto general_lead = [&](int j) {
+  auto general = [&](int j) {
     dma_all(j);
     if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
     if (j < wave_nt) masked_softmax(j);
     if (j + 1 < wave_nt) qk(kbuf(j + 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
-    iteration_barrier();
-  };
-  auto general_follow = [&](int j) {
-    dma_all(j);
-    if (pending) {
-      sb[0] = sacc[0];
-      sb[1] = sacc[1];
-    }
-    if (j < wave_nt) qk(kbuf(j), Off{}, Off{}, 0, 0, S_lo{}, sacc);
-    if (pending) finish_pending();
-    if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
-    if (j < wave_nt) masked_softmax(j);
     iteration_barrier();
   };
 
@@ -806,22 +799,16 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   const int jend = min(nfull, nkt - 1);
-  if (lead) {
-    if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc);
-    general_lead(0);
-    int j = 1;
-    for (; j < jend; ++j) steady_lead(j);
-    for (; j < nkt; ++j) general_lead(j);
-  } else {
-    general_follow(0);
-    int j = 1;
-    if (j < jend) {
-      steady_follow(j, std::true_type{});
-      for (++j; j < jend; ++j) steady_follow(j, std::false_type{});
-      pending = true;
-    }
-    for (; j < nkt; ++j) general_follow(j);
+  if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+  general(0);
+  int j = 1;
+  for (;;) {  // steady tiles; a tile that overflowed the budget is redone outside the loop
+    bool ovf = false;
+    for (; j < jend && !ovf; ++j) ovf = steady(j);
+    if (!ovf) break;
+    fast_redo();
   }
+  for (; j < nkt; ++j) general(j);
   if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

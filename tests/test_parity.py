@@ -208,3 +208,26 @@ def test_outputs_untouched_outside_bounds(fa):
     torch.cuda.synchronize()
     assert torch.all(obuf[B * H * n * d:] == 7.0) and torch.all(lbuf[B * H * n:] == 7.0)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [2.0, -1.5])
+def test_large_scores_d128(fa, causal, scale):
+    """Scores that grow far beyond the row max of a row's first key tile
+    (scale * sqrt(d) ~ 23: later tiles exceed it by dozens of log2 units),
+    so the d = 128 kernel must raise its reference max mid-row many times."""
+    d = 128
+    assert_close(run_case(fa, 4100 + int(scale * 10) + causal, 1, 2, 1000, d, "bf16", causal, scale=scale),
+                 "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_magnitude_ramp_d128(fa, causal):
+    """Key j scaled by 1 + j/16: every new key tile has a larger score range
+    than all earlier ones (the worst case for a reference max fixed from
+    early tiles)."""
+    n, d = 1500, 128
+    st = {t: synthetic.full_storage(4200 + causal, t, 1, 2, n, d, "bf16") for t in ("q", "k", "v")}
+    kv = synthetic.bf16_bits_to_f32(st["k"]) * (1.0 + np.arange(n, dtype=np.float32) / 16.0)[None, None, :, None]
+    st["k"] = synthetic.bf16_round_bits(kv)
+    assert_close(run_case(fa, 0, 1, 2, n, d, "bf16", causal, tensors=st), "bf16")
