@@ -495,12 +495,17 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
 // only.
 namespace duo {
 
+template <class T>
+__device__ constexpr int kb_slot(T) {
+  return T::value;
+}
+
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBQ = 256;
 constexpr int kLead = 3;
 constexpr int kRingK = 4;  // K ring: tile being read, one landing, one being written, one spare
-constexpr int kRingV = 3;  // V ring: tile being read, one landing, one being written
+constexpr int kRingV = 4;  // V ring: as K (equal rings make the buffers of an interval depend on j mod 4 only)
 
 // K and V tiles sit unpadded in LDS (rows of D bf16) because the LDS-DMA
 // writes 1 KiB per wave instruction contiguously.  Bank conflicts of the
@@ -609,6 +614,17 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     __builtin_amdgcn_global_load_lds((const void*)(src + off),
                                      (__attribute__((address_space(3))) void*)(smem + buf + r0 * D), 16, 0, 0);
   };
+  // DMA of tile t into a ring slot given as an element offset (general
+  // path) or as integral_constant<int, slot> of the K (is_v false) or V
+  // ring.
+  auto dma_any = [&](const __bf16* Xh, auto buf, int t, int i, auto is_v) {
+    if constexpr (std::is_integral_v<decltype(buf)>) {
+      dma_one(Xh, buf, t, i, is_v);
+    } else {
+      constexpr int eoff = (decltype(is_v)::value ? Ly::V0 : Ly::K0) + kb_slot(buf) * Ly::TILE;
+      dma_one(Xh, eoff, t, i, is_v);
+    }
+  };
   auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::TILE; };
   auto vbuf = [](int t) { return Ly::V0 + (t % kRingV) * Ly::TILE; };
   auto iteration_barrier = [&]() {
@@ -627,8 +643,15 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (2 * tr_e)) * 8) +
                           (tr_t & 1) * 4) * 2u;
   const unsigned smem_base = lds_addr(smem);
-  auto buf_addr = [&](int elem_off) {
-    unsigned a = smem_base + (unsigned)(elem_off * 2);
+  // Absolute LDS addresses of buffer 0 of each ring; the buffer, the
+  // 32-key half and the 16-key step then enter as instruction immediates.
+  unsigned k_abs[DT], v_abs[DB];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) k_abs[t] = smem_base + Ly::K0 * 2 + k_off[t];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) v_abs[b] = smem_base + Ly::V0 * 2 + v_off[b];
+  auto buf_rel = [&](int elem_off) {
+    unsigned a = (unsigned)(elem_off * 2);
     asm volatile("" : "+s"(a));
     return a;
   };
@@ -639,15 +662,23 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // S^T = K Q^T from K buffer kb.  With SM, slots S0..S0+15 of the fast
   // update of the scores sc ride along; with DMA, the V DMA of tile dma_t
   // into buffer dma_b.
-  auto qk = [&](int kb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
+  auto qk = [&](auto kb, auto with_sm, auto with_dma, int dma_t, auto dma_b, auto slot0, const f32x16(&sc)[2],
+                f32x16(&dst)[2]) {
     constexpr bool SM = decltype(with_sm)::value;
     constexpr bool DMA = decltype(with_dma)::value;
     constexpr int S0 = decltype(slot0)::value;
-    const unsigned base = buf_addr(kb);
+    // kb: an element offset, or integral_constant<int, ring slot> (then the
+    // slot is an immediate of every read)
+    constexpr bool CT = !std::is_integral_v<decltype(kb)>;
+    unsigned base = 0;  // byte offset of the slot from slot 0
+    if constexpr (!CT) base = buf_rel(kb - Ly::K0);
     bf16x8 fr[kLead];
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
-      read_k<(F % 2) * 32 * D * 2>(fr[F % kLead], base + k_off[F / 2]);
+      if constexpr (CT)
+        read_k<kb_slot(kb) * Ly::TILE * 2 + (F % 2) * 32 * D * 2>(fr[F % kLead], k_abs[F / 2]);
+      else
+        read_k<(F % 2) * 32 * D * 2>(fr[F % kLead], base + k_abs[F / 2]);
     };
     static_for<kLead>(issue);
     static_for<NK>([&](auto fc) {
@@ -655,12 +686,12 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
       constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fr[F % kLead]) : "i"(last - F));
       if constexpr (F < 2)
-        sacc[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], f32x16{}, 0, 0, 0);
+        dst[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], f32x16{}, 0, 0, 0);
       else
-        sacc[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], sacc[F % 2], 0, 0, 0);
+        dst[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], dst[F % 2], 0, 0, 0);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
       if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
-      if constexpr (DMA && F % 8 == 3) dma_one(Vh, dma_b, dma_t, F / 8, std::true_type{});
+      if constexpr (DMA && F % 8 == 3) dma_any(Vh, dma_b, dma_t, F / 8, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -668,16 +699,23 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // O^T += V^T P^T from V buffer vb.  With SM, slots S0..S0+15 of the fast
   // update of the scores sc ride along; with DMA, the K DMA of tile dma_t
   // into buffer dma_b.
-  auto pv = [&](int vb, auto with_sm, auto with_dma, int dma_t, int dma_b, auto slot0, const f32x16(&sc)[2]) {
+  auto pv = [&](auto vb, auto with_sm, auto with_dma, int dma_t, auto dma_b, auto slot0, const f32x16(&sc)[2]) {
     constexpr bool SM = decltype(with_sm)::value;
     constexpr bool DMA = decltype(with_dma)::value;
     constexpr int S0 = decltype(slot0)::value;
-    const unsigned base = buf_addr(vb);
+    constexpr bool CT = !std::is_integral_v<decltype(vb)>;
+    unsigned base = 0;
+    if constexpr (!CT) base = buf_rel(vb - Ly::V0);
     s16x4 lo[kLead], hi[kLead];
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
       constexpr int u = F / DB, b = F % DB;
-      read_v<u * 16 * D * 2, (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], base + v_off[b]);
+      if constexpr (CT) {
+        constexpr int o = kb_slot(vb) * Ly::TILE * 2;
+        read_v<o + u * 16 * D * 2, o + (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], v_abs[b]);
+      } else {
+        read_v<u * 16 * D * 2, (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], base + v_abs[b]);
+      }
     };
     static_for<kLead>(issue);
     static_for<NV>([&](auto fc) {
@@ -690,7 +728,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
       oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[u], oacc[b], 0, 0, 0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
       if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
-      if constexpr (DMA && F % 8 == 3) dma_one(Kh, dma_b, dma_t, F / 8, std::false_type{});
+      if constexpr (DMA && F % 8 == 3) dma_any(Kh, dma_b, dma_t, F / 8, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -733,12 +771,12 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     if (!ovf) l_part += part;
     return ovf;
   };
-  // Exact update of the tile in sb: m raised to the row max, P recomputed,
+  // Exact update of the tile with scores sv: m raised to the row max, P recomputed,
   // O and l rescaled.
-  auto fast_redo = [&]() {
-    float mx = sb[0][0];
+  auto fast_redo = [&](const f32x16(&sv)[2]) {
+    float mx = sv[0][0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sb[i >> 4][i & 15]);
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, sv[i >> 4][i & 15]);
     const float m_new = fmaxf(m_run, swap_halves(mx, true) * c);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -750,8 +788,8 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const int i = u * 8 + e;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[i >> 4][i & 15], c, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[(i + 1) >> 4][(i + 1) & 15], c, -m_run));
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i >> 4][i & 15], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[(i + 1) >> 4][(i + 1) & 15], c, -m_run));
         const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
         ps[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[e >> 2], false);
         w[e >> 1] = __builtin_bit_cast(unsigned, pr);
@@ -764,11 +802,17 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // Steady interval: tile j unmasked for every row, 1 <= j, j + 1 < nkt.
   // Returns true when tile j's probabilities overflowed the budget (P_j
   // then needs fast_redo before the next interval's P.V).
-  auto steady = [&](int j) -> bool {
-    pv(vbuf(j - 1), On{}, On{}, j + 3, kbuf(j + 3), S_lo{}, sacc);
-    sb[0] = sacc[0];
-    sb[1] = sacc[1];
-    qk(kbuf(j + 1), On{}, On{}, j + 1, vbuf(j + 1), S_hi{}, sb);
+  // R = j mod 4 fixes every ring slot of the interval, and the scores of
+  // tile j sit in sacc for even j, in sb for odd j (Q.K of tile j + 1
+  // writes the other set, so no copy is needed).
+  auto steady = [&](int j, auto r_c) -> bool {
+    constexpr int R = decltype(r_c)::value;
+    f32x16(&cur)[2] = (R & 1) ? sb : sacc;
+    f32x16(&nxt)[2] = (R & 1) ? sacc : sb;
+    pv(std::integral_constant<int, (R + 3) % 4>{}, On{}, On{}, j + 3, std::integral_constant<int, (R + 3) % 4>{},
+       S_lo{}, cur);
+    qk(std::integral_constant<int, (R + 1) % 4>{}, On{}, On{}, j + 1, std::integral_constant<int, (R + 1) % 4>{},
+       S_hi{}, cur, nxt);
     const bool ovf = fast_check();
     iteration_barrier();
     return ovf;
@@ -786,7 +830,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     dma_all(j);
     if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
     if (j < wave_nt) masked_softmax(j);
-    if (j + 1 < wave_nt) qk(kbuf(j + 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    if (j + 1 < wave_nt) qk(kbuf(j + 1), Off{}, Off{}, 0, 0, S_lo{}, sacc, sacc);
     iteration_barrier();
   };
 
@@ -799,14 +843,42 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   const int jend = min(nfull, nkt - 1);
-  if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+  if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc, sacc);
   general(0);
+  // Steady tiles, the loop unrolled by the ring period (ring slots and the
+  // score set are compile-time in each copy).  A tile that overflowed the
+  // budget is redone after the loop; the remaining tiles then take the
+  // general path (correct for any tile, rarely needed).
   int j = 1;
-  for (;;) {  // steady tiles; a tile that overflowed the budget is redone outside the loop
+  if (j < jend) {
+    sb[0] = sacc[0];  // tile 1 (odd) in sb
+    sb[1] = sacc[1];
     bool ovf = false;
-    for (; j < jend && !ovf; ++j) ovf = steady(j);
-    if (!ovf) break;
-    fast_redo();
+    for (;;) {
+      if (j >= jend) break;
+      ovf = steady(j, std::integral_constant<int, 1>{});
+      ++j;
+      if (ovf || j >= jend) break;
+      ovf = steady(j, std::integral_constant<int, 2>{});
+      ++j;
+      if (ovf || j >= jend) break;
+      ovf = steady(j, std::integral_constant<int, 3>{});
+      ++j;
+      if (ovf || j >= jend) break;
+      ovf = steady(j, std::integral_constant<int, 0>{});
+      ++j;
+      if (ovf) break;
+    }
+    if (ovf) {
+      if (j & 1)  // tile j - 1 (even) is in sacc
+        fast_redo(sacc);
+      else
+        fast_redo(sb);
+    }
+    if (j & 1) {  // the general path expects the scores of tile j in sacc
+      sacc[0] = sb[0];
+      sacc[1] = sb[1];
+    }
   }
   for (; j < nkt; ++j) general(j);
   if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
