@@ -529,7 +529,7 @@ struct Layout {
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FULL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
                 __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate) {
@@ -603,14 +603,28 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 
   const int dma_row = lane / CPR;
   const int dma_chunk = lane % CPR;
+  // Source byte offsets of the lane within a tile, for FULL launches (N a
+  // multiple of the tile: no row is ever clamped).
+  unsigned dk_lane[IPW], dv_lane[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int row = (wave * IPW + i) * Ly::ROWS_PER_INSTR + dma_row;
+    dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (row % CPR)) * 16));
+    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (2 * (row & 3))) * 16));
+  }
   auto dma_one = [&](const __bf16* Xh, int buf, int t, int i, auto is_v) {
-    t = min(t, nkt - 1);
+    t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
     const int kt0 = t * kBK;
     const char* src = (const char*)(Xh + (size_t)kt0 * D);
     const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
-    const int row = r0 + dma_row;
-    const int chunk = decltype(is_v)::value ? (dma_chunk ^ (2 * (row & 3))) : (dma_chunk ^ (row % CPR));
-    const unsigned off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
+    unsigned off;
+    if constexpr (FULL) {
+      off = decltype(is_v)::value ? dv_lane[i] : dk_lane[i];
+    } else {
+      const int row = r0 + dma_row;
+      const int chunk = decltype(is_v)::value ? (dma_chunk ^ (2 * (row & 3))) : (dma_chunk ^ (row % CPR));
+      off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
+    }
     __builtin_amdgcn_global_load_lds((const void*)(src + off),
                                      (__attribute__((address_space(3))) void*)(smem + buf + r0 * D), 16, 0, 0);
   };
@@ -924,7 +938,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate};
   const void* fn;
   if constexpr (kDuo)
-    fn = (const void*)duo::fwd_kernel<D, CAUSAL>;
+    fn = p.N % kBK == 0 ? (const void*)duo::fwd_kernel<D, CAUSAL, true> : (const void*)duo::fwd_kernel<D, CAUSAL, false>;
   else
     fn = (const void*)fwd_bf16_kernel<D, CAUSAL>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -11,6 +11,8 @@ bounded sample of the same workload.
 
 --profile-run: the run used under rocprofv3 counters: one 1 GiB device
 copy (the byte-count calibration kernel) followed by --steps launches.
+--profile-bwd: --steps backward calls on B=2 H=16 N=4096 d=128 causal (the
+forward-plus-backward workload), printed as one JSON line.
 """
 from __future__ import annotations
 
@@ -188,6 +190,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extra", action="store_true", help="also time the other workloads and non-causal")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--profile-bwd", action="store_true",
+                    help="run --steps fa_bwd calls on B=2 H=16 N=4096 d=128 causal (for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the attention forward is sharded over heads with no "
@@ -199,6 +203,15 @@ def main():
 
     import aware_softmax_amd as fa
     import synthetic
+
+    if args.profile_bwd:
+        wb = synthetic.WORKLOADS[5]
+        qq, kk, vv = make_inputs(wb)
+        oo = torch.empty_like(qq)
+        ll = torch.empty((wb.B, wb.H, wb.N), dtype=torch.float32, device=qq.device)
+        r = time_backward(fa, wb, qq, kk, vv, oo, ll, args.steps, 2)
+        print(json.dumps({"profile-bwd": wb.name, **r}), flush=True)
+        return
 
     w = synthetic.WORKLOADS[3]
     q, k, v = make_inputs(w)
