@@ -480,8 +480,12 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
 // MFMAs, one slot of VALU work after each (the matrix unit computes while
 // the exponentials issue; the other wave of the SIMD fills the gaps).  The
 // HBM -> LDS copies (LDS-DMA, 1 KiB per wave instruction) are spread over
-// the same MFMAs two intervals ahead of use, into rings of four K and three
-// V tiles; one workgroup barrier per interval.
+// the same MFMAs two intervals ahead of use, into rings of four K and four
+// V tiles (128 KiB); one workgroup barrier per interval.  All eight waves
+// follow the same order (P.V of tile j-1 first, then Q.K of tile j+1); the
+// two waves of a SIMD interleave through the hardware's own arbitration.
+// The steady loop is unrolled by the ring period (4), so every LDS address
+// is a per-lane base plus a compile-time immediate.
 //
 // The reference max m of a row is not the running max.  O = O~/l and
 // L = m + log l do not depend on which reference m is used (the
@@ -917,8 +921,9 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 
 }  // namespace duo
 
-// Kernel per head dim: the staggered two-waves-per-SIMD kernel for d = 128,
-// the 4-wave kernel for d = 64 (whose 8 + 8 MFMAs per tile leave too few
+// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 (FULL when
+// the sequence is a whole number of key tiles: no row clamping in the
+// copies), the 4-wave kernel for d = 64 (whose 8 + 8 MFMAs per tile leave too few
 // slots to hide the softmax of a 64-key tile).
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
