@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -46,9 +47,15 @@ def causal_row_flops(rows, d):
     return float(sum(4.0 * d * (int(i) + 1) for i in rows))
 
 
-def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_hash(path=KERNEL_SOURCE):
+    """sha256 of the kernel source with comments and blank space removed, so
+    that only a change of the code itself invalidates stored counters."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def read_traffic():
@@ -62,7 +69,7 @@ def read_traffic():
             if ":" in line:
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_code_sha256 (source without comments or blank space)") != kernel_source_hash():
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
