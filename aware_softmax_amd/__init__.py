@@ -1,6 +1,6 @@
 """Python binding of libfa.so, the gfx950 fused exact-attention library.
 
-Argument marshalling only: every step of the forward and backward runs in the HIP
+Argument marshalling only: every step of the forward, backward and decode runs in the HIP
 kernels behind the C ABI declared in include/fa.h.  torch supplies device
 memory and the current stream.  There is no fallback: if libfa.so is
 missing or fails to load, importing this package raises ImportError.
@@ -19,6 +19,10 @@ __all__ = [
     "fa_bwd",
     "bwd_workspace_bytes",
     "bwd_tile_config",
+    "decode",
+    "fa_decode",
+    "decode_plan",
+    "decode_workspace_bytes",
     "tile_config",
     "version",
     "status_string",
@@ -64,6 +68,13 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_tile.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     lib.fa_bwd_tile.restype = ci
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
+    lib.fa_decode.restype = ci
+    lib.fa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
+                                   ctypes.POINTER(sz)]
+    lib.fa_decode_plan.restype = ci
+    lib.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
+    lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
     return lib
@@ -211,3 +222,74 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
                   workspace.numel() * workspace.element_size(), B, H, N, d, causal, scale, DTYPE_BF16,
                   stream.cuda_stream))
     return dq, dk, dv
+
+
+def decode_plan(B, H, Hkv, N, d, num_splits=0) -> tuple:
+    """(splits, keys per split, workspace bytes) that fa_decode uses."""
+    sp, ck, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+    _check(_LIB.fa_decode_plan(int(B), int(H), int(Hkv), int(N), int(d), int(num_splits), ctypes.byref(sp),
+                               ctypes.byref(ck), ctypes.byref(ws)))
+    return sp.value, ck.value, ws.value
+
+
+def decode_workspace_bytes(B, H, Hkv, N, d, num_splits=0) -> int:
+    """Device workspace bytes fa_decode needs (0 for invalid sizes)."""
+    return int(_LIB.fa_decode_workspace_bytes(int(B), int(H), int(Hkv), int(N), int(d), int(num_splits)))
+
+
+def fa_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, ws_ptr, ws_bytes, B, H, Hkv, N, d, scale, num_splits, dtype,
+              stream) -> int:
+    """Raw call of the C entry point with integer device addresses; returns
+    the fa_status_t code."""
+    return _LIB.fa_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, ws_ptr, int(ws_bytes), int(B), int(H), int(Hkv),
+                          int(N), int(d), float(scale), int(num_splits), int(dtype), stream)
+
+
+def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, lse=None, workspace=None,
+           stream=None):
+    """Split-K decode attention: q [B, H, d] against a cache k, v
+    [B, Hkv, N, d] (bf16 device tensors, H a multiple of Hkv).
+
+    Returns (o [B, H, d] bf16, lse [B, H] float32).  num_splits = 0 lets the
+    library choose; 1 runs the unsplit kernel.  out / lse / workspace (uint8,
+    at least decode_plan(...)[2] bytes) may be passed to reuse buffers.
+    Runs on `stream` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dtype != torch.bfloat16:
+        raise TypeError(f"unsupported dtype {q.dtype} for decode; use torch.bfloat16")
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, H, d] and k, v [B, Hkv, N, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if v.shape != k.shape:
+        raise ValueError("v must match k in shape")
+    B, H, d = q.shape
+    Bk, Hkv, N, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("k, v must be [B, Hkv, N, d] with the B and d of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_plan(B, H, Hkv, N, d, num_splits)[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                     workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits, DTYPE_BF16,
+                     stream.cuda_stream))
+    return out, lse

@@ -14,6 +14,9 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// A launch's work-items in x must fit in 32 bits.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+
 size_t elem_size(fa_dtype_t dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 
 fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
@@ -30,19 +33,19 @@ const char* fa_status_string(fa_status_t status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N and d must be positive and the sizes must fit";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be positive, consistent and within the supported range";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
     case FA_ERR_UNSUPPORTED_HEADDIM: return "FA_ERR_UNSUPPORTED_HEADDIM: d must be 64 or 128";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte and lse 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP kernel launch failed";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or smaller than the size the call needs";
   }
   return "unknown fa_status_t";
 }
 
-const char* fa_version(void) { return "0.2.0 gfx950"; }
+const char* fa_version(void) { return "0.3.0 gfx950"; }
 
 fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves) {
   if (!block_q || !block_k || !waves) return FA_ERR_NULL;
@@ -68,7 +71,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
   const fa::TileConfig tile = dtype == FA_DTYPE_BF16 ? fa::bf16_tile(d) : fa::f32_tile(d);
   const int64_t nqb = ((int64_t)N + tile.block_q - 1) / tile.block_q;
-  if (bh * nqb > INT_MAX) return FA_ERR_SHAPE;
+  if (bh * nqb * 64 * tile.waves > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
     return FA_ERR_ALIGN;
@@ -122,7 +125,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   const int64_t elems = bh * N * d;
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
   const int64_t nkb = ((int64_t)N + fa::bwd_block_k() - 1) / fa::bwd_block_k();
-  if (bh * nkb > INT_MAX) return FA_ERR_SHAPE;
+  if (bh * nkb * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
         (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
@@ -159,6 +162,69 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, int* splits, int* chunk_keys,
+                           size_t* workspace_bytes) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || num_splits < 0) return FA_ERR_SHAPE;
+  if (H % Hkv != 0 || N > (1 << 30)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX || (int64_t)B * Hkv * N * d > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const fa::DecodePlan pl = fa::decode_plan(B, H, Hkv, N, d, num_splits);
+  if (pl.split_wgs * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (splits) *splits = pl.splits;
+  if (chunk_keys) *chunk_keys = pl.chunk;
+  if (workspace_bytes) *workspace_bytes = pl.workspace_bytes;
+  return FA_OK;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_splits) {
+  size_t ws = 0;
+  return fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &ws) == FA_OK ? ws : 0;
+}
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
+                      fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  size_t need = 0;
+  const fa_status_t st = fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &need);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+    return FA_ERR_ALIGN;
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t qb = (size_t)B * H * d * 2;
+  const size_t kb = (size_t)B * Hkv * N * d * 2;
+  const size_t lb = (size_t)B * H * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t in_bytes[3] = {qb, kb, kb};
+  void* outs[3] = {o, lse, workspace};
+  const size_t out_bytes[3] = {qb, lb, need};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 3; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 3; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.workspace = workspace;
+  p.B = B;
+  p.H = H;
+  p.Hkv = Hkv;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.num_splits = num_splits;
+  return fa::launch_decode_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,367 @@
+// Decode attention with the key dimension split across workgroups
+// ("PidokuInfra 10 -- FlashAttention", section 5, "The decode variant:
+// FlashDecoding"), bfloat16 in/out, fp32 softmax state, gfx950.
+//
+// What is computed: one query row per (batch b, head h) against the N
+// cached keys and values of its key/value head hk = h / (H / Hkv)
+// (H = Hkv is ordinary multi-head attention; H / Hkv > 1 shares one
+// key/value head among a group of query heads):
+//     o_bh = sum_j softmax_j(scale * q_bh . k_j) v_j,   lse_bh = logsumexp_j(...)
+// No mask: the decoded token is the newest position and sees every cached
+// key (the causal mask with the query at the end of the sequence).
+//
+// How (the same section): with one query per sequence, a grid over
+// (batch, head) alone has too few workgroups to fill the GPU and each must
+// walk all N keys serially.  The keys are split into S chunks; each
+// workgroup computes an unnormalised partial (m, l, o~) over its chunk, and
+// a second kernel merges the S partials with the online-softmax rescale
+// ("FlashAttention: Move Less, Not Compute Less", "Tiling Is Easy; Softmax
+// Couples the Entire Row": partials are brought to the common max M by
+// exp(m_s - M) before summing), then divides once.
+//
+// MI355X mapping.  The work is a matrix-vector product per head, bound by
+// reading K and V from HBM once; it runs on the VALU (v_dot2_f32_bf16), not
+// on MFMA.  D/8 lanes share one key row, each holding 16 bytes (8 bf16) of
+// it, so one wave instruction reads 64 x 16 = 1 KiB of contiguous K or V;
+// the row's dot product is finished by a DPP reduction inside the 16-lane
+// (d = 128) or 8-lane (d = 64) group, which leaves the score in every lane
+// of the group.  Each lane keeps its own online-softmax state (m, l and its
+// 8 elements of o~) over the rows it has seen, so the hot loop has no
+// cross-lane max at all; the states of a workgroup are merged once at the
+// end.  A group of G query heads that share a key/value head is served by
+// one workgroup, so K and V are read once for all G.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Largest query-head group one workgroup serves (a divisor of H / Hkv).
+constexpr int kMaxGroup = 8;
+
+template <int D>
+struct Shape {
+  static constexpr int LPR = D / 8;         // lanes per key row (16 B each)
+  static constexpr int RPI = 64 / LPR;      // key rows per wave instruction
+};
+
+// Loads in flight per wave and iteration (K and V each).
+template <int G>
+constexpr int unroll() {
+  return G <= 2 ? 8 : 4;
+}
+
+// Rows of one workgroup iteration: every wave reads unroll() instructions
+// of RPI rows.
+template <int D, int G>
+constexpr int rows_per_iter() {
+  return kWaves * unroll<G>() * Shape<D>::RPI;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
+
+// Sum over the LPR lanes of a key row; every lane of the group gets the sum.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1]: sums over each 4-lane quad.
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  // row_half_mirror: lane i of an 8-lane half reads lane 7 - i (the other quad).
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if constexpr (LPR == 16)  // row_mirror: lane i of a 16-lane row reads lane 15 - i.
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// Split kernel.  Workgroup index -> (split s, head group hg, b * Hkv + hk).
+// part_o  [B*H][S][D]  fp32 unnormalised o~ of each split;
+// part_ml [B*H][S][2]  fp32 (m, l) of each split, m in log2 units of the
+//                      scaled scores (c = scale * log2 e folded in).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c) {
+  constexpr int LPR = Shape<D>::LPR;
+  constexpr int RPI = Shape<D>::RPI;
+  constexpr int U = unroll<G>();
+  constexpr int ROWS_WAVE = U * RPI;  // rows per wave and iteration
+  constexpr float kNegInf = -__builtin_inff();
+
+  const int group = H / Hkv;
+  const int n_hg = group / G;
+  int wg = blockIdx.x;
+  const int s = wg % S;
+  wg /= S;
+  const int hg = wg % n_hg;
+  const int bhk = wg / n_hg;  // b * Hkv + hk
+  const int b = bhk / Hkv;
+  const int hk = bhk - b * Hkv;
+  const int h0 = hk * group + hg * G;  // first query head of this workgroup
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cc = lane % LPR;  // 16-byte chunk of the row this lane holds
+  const int rr = lane / LPR;  // row within a wave instruction
+
+  // Query fragments: elements 8cc .. 8cc+7 of each head's query.
+  unsigned qf[G][4];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const u32x4 t = *(const u32x4*)(q + ((size_t)b * H + h0 + i) * D + cc * 8);
+    qf[i][0] = t[0];
+    qf[i][1] = t[1];
+    qf[i][2] = t[2];
+    qf[i][3] = t[3];
+  }
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = kNegInf;
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
+  }
+
+  const int k_begin = s * chunk;
+  const int k_end = min(N, k_begin + chunk);
+  const size_t head_off = (size_t)bhk * N * D;
+  const __bf16* kh = k + head_off + cc * 8;
+  const __bf16* vh = v + head_off + cc * 8;
+
+  for (int r0 = k_begin + wave * ROWS_WAVE; r0 < k_end; r0 += kWaves * ROWS_WAVE) {
+    u32x4 kf[U], vf[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * RPI + rr;
+      ok[u] = row < k_end;
+      const int rc = ok[u] ? row : k_end - 1;  // clamped rows are loaded but scored -inf
+      kf[u] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)rc * D));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = r0 + u * RPI + rr;
+      const int rc = row < k_end ? row : k_end - 1;
+      vf[u] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)rc * D));
+    }
+    // V rows as fp32 (bf16 is the high half of an fp32).
+    float vv[U][8];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float sc[U];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qf[i][t]), as_bf16x2(kf[u][t]), acc, false);
+        acc = row_sum<LPR>(acc);
+        sc[u] = ok[u] ? acc * c : kNegInf;
+        tmax = fmaxf(tmax, sc[u]);
+      }
+      const float m_new = fmaxf(m[i], tmax);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;  // no visible row yet: nothing to add
+      const float alpha = __builtin_amdgcn_exp2f(m[i] - m_use);
+      m[i] = m_new;
+      float ls = 0.f;
+      float p[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = __builtin_amdgcn_exp2f(sc[u] - m_use);
+        ls += p[u];
+      }
+      l[i] = l[i] * alpha + ls;
+      if (i == 0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            vv[u][2 * t] = __builtin_bit_cast(float, vf[u][t] << 16);
+            vv[u][2 * t + 1] = __builtin_bit_cast(float, vf[u][t] & 0xffff0000u);
+          }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float acc = o[i][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = fmaf(p[u], vv[u][e], acc);
+        o[i][e] = acc;
+      }
+    }
+  }
+
+  // Merge the RPI row groups of the wave (lanes cc, cc + LPR, ...), then the
+  // waves through LDS.  A state with no visible row has m = -inf, l = 0,
+  // o~ = 0 and gets weight 0.
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+  __shared__ float sm_o[kWaves][G][D];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float mm = m[i];
+#pragma unroll
+    for (int sh = LPR; sh < 64; sh <<= 1) mm = fmaxf(mm, __shfl_xor(mm, sh));
+    const float w = __builtin_amdgcn_exp2f(m[i] - (mm == kNegInf ? 0.f : mm));
+    float ll = l[i] * w;
+    float oo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) oo[e] = o[i][e] * w;
+#pragma unroll
+    for (int sh = LPR; sh < 64; sh <<= 1) {
+      ll += __shfl_xor(ll, sh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) oo[e] += __shfl_xor(oo[e], sh);
+    }
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm_o[wave][i][cc * 8 + e] = oo[e];
+      if (cc == 0) {
+        sm_m[wave][i] = mm;
+        sm_l[wave][i] = ll;
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < G * D; t += kThreads) {
+    const int i = t / D;
+    const int e = t - i * D;
+    float mm = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][i]);
+    float ll = 0.f, oo = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w][i] - mm);  // mm is finite: the split has a key
+      ll = fmaf(wt, sm_l[w][i], ll);
+      oo = fmaf(wt, sm_o[w][i][e], oo);
+    }
+    const size_t row = ((size_t)b * H + h0 + i) * S + s;
+    part_o[row * D + e] = oo;
+    if (e == 0) {
+      part_ml[row * 2] = mm;
+      part_ml[row * 2 + 1] = ll;
+    }
+  }
+}
+
+// Combine kernel: one workgroup of D threads per (b, h).  M = max_s m_s,
+// l = sum_s 2^(m_s - M) l_s, o = sum_s 2^(m_s - M) o~_s / l, and
+// lse = ln 2 * (M + log2 l) (m is in log2 units).
+template <int D>
+__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml, __bf16* __restrict__ o,
+                                                           float* __restrict__ lse, int S) {
+  const int bh = blockIdx.x;
+  const int e = threadIdx.x;
+  const float* ml = part_ml + (size_t)bh * S * 2;
+  const float* po = part_o + (size_t)bh * S * D + e;
+  float mm = -__builtin_inff();
+  for (int s = 0; s < S; ++s) mm = fmaxf(mm, ml[2 * s]);
+  float ll = 0.f, oo = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mm);
+    ll = fmaf(wt, ml[2 * s + 1], ll);
+    oo = fmaf(wt, po[(size_t)s * D], oo);
+  }
+  o[(size_t)bh * D + e] = (__bf16)(oo / ll);
+  if (e == 0) lse[bh] = (mm + __builtin_amdgcn_logf(ll)) * kLn2;
+}
+
+// Largest divisor of the query-head group that one workgroup serves.
+int heads_per_wg(int group) {
+  for (int g = kMaxGroup; g > 1; --g)
+    if (group % g == 0) return g;
+  return 1;
+}
+
+template <int D>
+int rows_per_iter_rt(int G) {
+  switch (G) {
+    case 1: return rows_per_iter<D, 1>();
+    case 2: return rows_per_iter<D, 2>();
+    case 3: return rows_per_iter<D, 3>();
+    case 4: return rows_per_iter<D, 4>();
+    case 5: return rows_per_iter<D, 5>();
+    case 6: return rows_per_iter<D, 6>();
+    case 7: return rows_per_iter<D, 7>();
+    default: return rows_per_iter<D, 8>();
+  }
+}
+
+template <int D, int G>
+hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
+  const float c = p.scale * kLog2e;
+  float* po = (float*)p.workspace;
+  float* pml = (float*)((char*)p.workspace + plan.ml_offset);
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(plan.split_wgs), dim3(kThreads), 0, stream,
+                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, po, pml, p.H, p.Hkv, p.N,
+                     plan.splits, plan.chunk, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.H), dim3(D), 0, stream, (const float*)po,
+                     (const float*)pml, (__bf16*)p.o, p.lse, plan.splits);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
+  switch (plan.heads_per_wg) {
+    case 1: return launch_g<D, 1>(p, plan, stream);
+    case 2: return launch_g<D, 2>(p, plan, stream);
+    case 3: return launch_g<D, 3>(p, plan, stream);
+    case 4: return launch_g<D, 4>(p, plan, stream);
+    case 5: return launch_g<D, 5>(p, plan, stream);
+    case 6: return launch_g<D, 6>(p, plan, stream);
+    case 7: return launch_g<D, 7>(p, plan, stream);
+    default: return launch_g<D, 8>(p, plan, stream);
+  }
+}
+
+}  // namespace
+
+// Split plan.  Chunks are whole workgroup iterations; with num_splits = 0
+// the count aims at >= kTargetWgs workgroups in all (eight per CU) while
+// keeping every chunk at least one iteration long.
+DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits) {
+  constexpr int64_t kTargetWgs = 2048;
+  DecodePlan pl{};
+  const int group = H / Hkv;
+  pl.heads_per_wg = heads_per_wg(group);
+  const int rows = d == 128 ? rows_per_iter_rt<128>(pl.heads_per_wg) : rows_per_iter_rt<64>(pl.heads_per_wg);
+  const int64_t iters = ((int64_t)N + rows - 1) / rows;
+  const int64_t base = (int64_t)B * Hkv * (group / pl.heads_per_wg);
+  int64_t want = num_splits > 0 ? num_splits : (kTargetWgs + base - 1) / base;
+  if (want > iters) want = iters;
+  if (want < 1) want = 1;
+  const int64_t iters_per_split = (iters + want - 1) / want;
+  pl.chunk = (int)(iters_per_split * rows);
+  pl.splits = (int)(((int64_t)N + pl.chunk - 1) / pl.chunk);
+  pl.split_wgs = base * pl.splits;
+  const size_t rows_bh = (size_t)B * H * pl.splits;
+  pl.ml_offset = (rows_bh * d * sizeof(float) + 255) & ~(size_t)255;
+  pl.workspace_bytes = pl.ml_offset + rows_bh * 2 * sizeof(float);
+  return pl;
+}
+
+int decode_rows_per_iter(int d, int heads_per_wg) {
+  return d == 128 ? rows_per_iter_rt<128>(heads_per_wg) : rows_per_iter_rt<64>(heads_per_wg);
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+  const DecodePlan plan = decode_plan(p.B, p.H, p.Hkv, p.N, p.d, p.num_splits);
+  return p.d == 128 ? launch_d<128>(p, plan, stream) : launch_d<64>(p, plan, stream);
+}
+
+}  // namespace fa

@@ -50,11 +50,45 @@ struct BwdParams {
   float scale;
 };
 
+// Everything a split-K decode launch needs: q, o [B][H][d]; k, v
+// [B][Hkv][N][d]; lse [B][H]; workspace at least decode_plan(...).workspace_bytes.
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;
+  int B;
+  int H;
+  int Hkv;
+  int N;
+  int d;
+  float scale;
+  int num_splits;  // 0: automatic
+};
+
+// How the keys of one (batch, key/value head) are split: `splits` chunks of
+// `chunk` keys (the last one shorter), `heads_per_wg` query heads of a group
+// per workgroup.  Workspace: fp32 partial o~ [B*H][splits][d] at offset 0,
+// fp32 (m, l) [B*H][splits][2] at ml_offset.
+struct DecodePlan {
+  int heads_per_wg;
+  int chunk;
+  int splits;
+  int64_t split_wgs;
+  size_t ml_offset;
+  size_t workspace_bytes;
+};
+DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits);
+int decode_rows_per_iter(int d, int heads_per_wg);
+
 // Launchers: enqueue the kernel(s) on `stream`; return the first
 // hipError_t a launch reported.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
 
 // Backward workspace: -L/scale and -D, fp32 [BH][Npad] each; Npad = N
 // rounded up to the query tile of the dK/dV pass.

@@ -11,6 +11,7 @@ bounded sample of the same workload.
 
 --profile-run: the run used under rocprofv3 counters: one 1 GiB device
 copy (the byte-count calibration kernel) followed by --steps launches.
+--profile-decode: --steps split-K decode calls on B=8 H=32 N=32768 d=128.
 --profile-bwd: --steps backward calls on B=2 H=16 N=4096 d=128 causal (the
 forward-plus-backward workload), printed as one JSON line.
 """
@@ -149,6 +150,51 @@ def time_backward(fa, w, q, k, v, o, lse, steps, warmup):
             "flops_per_call": f, "kernels": "bwd_pre + bwd_dkdv + bwd_dq"}
 
 
+def decode_inputs(w, threads=16):
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    st = synthetic.decode_storage(w.config_id, w.B, w.H, w.Hkv, w.N, w.d, threads)
+    return [torch.from_numpy(st[t].view(np.int16)).view(torch.bfloat16).cuda() for t in ("q", "k", "v")]
+
+
+def decode_bytes(w):
+    """Compulsory HBM bytes of one decode call: read K, V and q, write o
+    and lse."""
+    return 2 * w.B * w.Hkv * w.N * w.d * 2 + 2 * w.B * w.H * w.d * 2 + 4 * w.B * w.H
+
+
+def time_decode(fa, w, q, k, v, num_splits, steps, warmup):
+    """fa_decode (split kernel + combine kernel) on one decode workload with
+    inputs resident; GB/s of compulsory bytes against the 8 TB/s HBM peak."""
+    import torch
+
+    splits, chunk, need = fa.decode_plan(w.B, w.H, w.Hkv, w.N, w.d, num_splits)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+
+    def step():
+        fa.decode(q, k, v, scale=w.scale, num_splits=num_splits, out=o, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    gbs = decode_bytes(w) / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 3),
+            "splits": splits, "keys_per_split": chunk, "bytes_per_call": decode_bytes(w),
+            "kernels": "decode_split + decode_combine"}
+
+
 def cpu_baseline(w, budget_s=12.0, rows_per_head=512):
     """The fp64 oracle on the host cores over a bounded sample of the same
     workload: seeded (b, h) heads, 512 seeded query rows each, until the
@@ -197,6 +243,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extra", action="store_true", help="also time the other workloads and non-causal")
     ap.add_argument("--profile-run", action="store_true")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="run --steps fa_decode calls on B=8 H=32 N=32768 d=128 (for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="run --steps fa_bwd calls on B=2 H=16 N=4096 d=128 causal (for rocprofv3)")
     args = ap.parse_args()
@@ -210,6 +258,13 @@ def main():
 
     import aware_softmax_amd as fa
     import synthetic
+
+    if args.profile_decode:
+        dw = synthetic.DECODE_WORKLOADS[6]
+        dq_, dk_, dv_ = decode_inputs(dw)
+        r = time_decode(fa, dw, dq_, dk_, dv_, 0, args.steps, 2)
+        print(json.dumps({"profile-decode": dw.name, **r}), flush=True)
+        return
 
     if args.profile_bwd:
         wb = synthetic.WORKLOADS[5]
@@ -300,6 +355,15 @@ def main():
         extra["non-causal bf16 B8 H32 N8192 d128"] = {
             "ms": round(msk, 4), "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2),
             "causal_speedup_time_ratio": round(msk / ms_kernel, 3)}
+        del qq, kk, vv, oo, ll
+        torch.cuda.empty_cache()
+        for cid in (6, 7, 8):
+            dw = synthetic.DECODE_WORKLOADS[cid]
+            dq_, dk_, dv_ = decode_inputs(dw)
+            for ns, tag in ((0, "split-K"), (1, "unsplit")):
+                extra[f"{dw.name} {tag}"] = time_decode(fa, dw, dq_, dk_, dv_, ns, 20, 3)
+            del dq_, dk_, dv_
+            torch.cuda.empty_cache()
         result["other_workloads"] = extra
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)

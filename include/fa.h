@@ -50,7 +50,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,                 /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,                /* B, H, N or d <= 0, or sizes overflow */
+  FA_ERR_SHAPE = 2,                /* a size <= 0, sizes too large, or inconsistent */
   FA_ERR_DTYPE = 3,                /* dtype is not a fa_dtype_t value */
   FA_ERR_UNSUPPORTED_HEADDIM = 4,  /* d is not 64 or 128 */
   FA_ERR_ALIGN = 5,                /* q/k/v/o not 16-byte or lse not 4-byte aligned */
@@ -142,6 +142,63 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
  * FA_ERR_UNSUPPORTED_HEADDIM.
  */
 fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q);
+
+/*
+ * Decode: one new query row per sequence against a cache of N keys and
+ * values ("PidokuInfra 10 -- FlashAttention", section 5, "The decode
+ * variant: FlashDecoding").  Query head h of batch b attends to every key
+ * of key/value head h / (H / Hkv) (Hkv = H: multi-head; Hkv < H: groups of
+ * H / Hkv query heads share one key/value head); there is no mask (the new
+ * token is the last position and sees the whole cache).  The keys are split
+ * into chunks processed by separate workgroups, each producing an
+ * unnormalised partial (m, l, o~); a second kernel merges the partials with
+ * the online-softmax rescale and divides once.
+ *
+ * Layouts: q, o contiguous [B][H][d]; k, v contiguous [B][Hkv][N][d]; lse
+ * contiguous [B][H] float32 (natural-log logsumexp of the scaled scores).
+ */
+
+/*
+ * fa_decode_plan -- the split fa_decode uses for these sizes.
+ *   num_splits  0 picks the count automatically (enough workgroups to fill
+ *               the GPU); n > 0 asks for n splits, reduced to the number of
+ *               key chunks of one workgroup iteration if larger (1 gives the
+ *               unsplit kernel: one workgroup walks all N keys).
+ *   splits, chunk_keys, workspace_bytes  [out] the split count, keys per
+ *               split (the last split may be shorter) and the workspace
+ *               fa_decode needs.  Any of them may be NULL.
+ * Host-only.  Returns FA_OK, FA_ERR_SHAPE (a size <= 0, H not a multiple of
+ * Hkv, N > 2^30, num_splits < 0, or sizes too large), or
+ * FA_ERR_UNSUPPORTED_HEADDIM.
+ */
+fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, int* splits,
+                           int* chunk_keys, size_t* workspace_bytes);
+
+/* fa_decode_workspace_bytes -- the workspace of fa_decode_plan, 0 on error. */
+size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_splits);
+
+/*
+ * fa_decode -- split-K decode attention.
+ *   q         [in]  device, [B][H][d] bf16, 16-byte aligned.
+ *   k, v      [in]  device, [B][Hkv][N][d] bf16, 16-byte aligned.
+ *   o         [out] device, [B][H][d] bf16, 16-byte aligned.
+ *   lse       [out] device, [B][H] float32, 4-byte aligned.
+ *   workspace [scratch] device, at least fa_decode_workspace_bytes(...)
+ *             bytes (passed as workspace_bytes), 256-byte aligned, owned by
+ *             the caller; overwritten, needs no initialisation.
+ *   B, H, Hkv, N, d   batch, query heads, key/value heads (H % Hkv == 0),
+ *             cached keys (1 <= N <= 2^30), head dim (64 or 128).
+ *   scale     finite; multiplies q . k.
+ *   num_splits  as for fa_decode_plan.
+ *   dtype     FA_DTYPE_BF16 only.
+ *   stream    HIP stream; two kernels are enqueued in order on it.
+ * Outputs must not overlap each other, the inputs or the workspace
+ * (FA_ERR_ALIAS).  No atomics: results are deterministic for a given split.
+ * Returns FA_OK or the first failed check.
+ */
+fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
+                      fa_dtype_t dtype, hipStream_t stream);
 
 /* Library version string, e.g. "0.1.0 gfx950" (static storage). */
 const char* fa_version(void);

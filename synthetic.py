@@ -17,6 +17,13 @@ the method is measured on:
   3: B=8, H=32, N=8192,  d=128, bf16, causal   (the throughput workload)
   4: B=1, H=16, N=32768, d=128, bf16, causal   (long context, batch 1)
   5: B=2, H=16, N=4096,  d=128, bf16, causal   (forward plus backward)
+and the decode problems (one query row per sequence against a cache of N
+keys; q [B][H][d] is drawn as N = 1 rows of the q stream, k and v as
+[B][Hkv][N][d]):
+  6: B=8, H=Hkv=32, N=32768, d=128, bf16   (decode, batch 8, 32 heads)
+  7: B=1, H=Hkv=32, N=32768, d=128, bf16   (decode, batch 1)
+  8: B=8, H=32, Hkv=8, N=32768, d=128, bf16 (decode, 4 query heads per
+     key/value head)
 """
 from __future__ import annotations
 
@@ -52,6 +59,37 @@ WORKLOADS = {
     4: Workload(4, "long-context causal bf16 B1 H16 N32768 d128", 1, 16, 32768, 128, "bf16", True),
     5: Workload(5, "causal bf16 forward and backward B2 H16 N4096 d128", 2, 16, 4096, 128, "bf16", True),
 }
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    config_id: int
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+DECODE_WORKLOADS = {
+    6: DecodeWorkload(6, "decode bf16 B8 H32 N32768 d128", 8, 32, 32, 32768, 128),
+    7: DecodeWorkload(7, "decode bf16 B1 H32 N32768 d128", 1, 32, 32, 32768, 128),
+    8: DecodeWorkload(8, "decode bf16 B8 H32 Hkv8 N32768 d128", 8, 32, 8, 32768, 128),
+}
+
+
+def decode_storage(config_id: int, B: int, H: int, Hkv: int, N: int, d: int, threads: int = 8) -> dict:
+    """bf16 bits of a decode problem: q [B][H][d], k and v [B][Hkv][N][d]."""
+    return {
+        "q": full_storage(config_id, "q", B, H, 1, d, "bf16", threads).reshape(B, H, d),
+        "k": full_storage(config_id, "k", B, Hkv, N, d, "bf16", threads),
+        "v": full_storage(config_id, "v", B, Hkv, N, d, "bf16", threads),
+    }
 
 
 def bf16_round_bits(x: np.ndarray) -> np.ndarray:

@@ -35,7 +35,8 @@ def fa():
 def test_header_declares_entry_points():
     names = declared_functions()
     for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version", "fa_bwd",
-                     "fa_bwd_workspace_bytes", "fa_bwd_tile"):
+                     "fa_bwd_workspace_bytes", "fa_bwd_tile", "fa_decode", "fa_decode_plan",
+                     "fa_decode_workspace_bytes"):
         assert required in names
 
 
@@ -200,3 +201,86 @@ def test_bwd_binding_rejects_bad_tensors(fa):
         fa.bwd(q, q, q, q, lse, q)
     with pytest.raises(TypeError):
         fa.bwd(q.float(), q.float(), q.float(), q.float(), lse, q.float())
+
+
+# ------------------------------------------------------------------ decode
+
+def test_decode_plan_values(fa):
+    # B8 H32 N32768 d128 (multi-head): 256 (b, h) pairs x 8 splits of 4096 keys
+    sp, ck, ws = fa.decode_plan(8, 32, 32, 32768, 128)
+    assert (sp, ck) == (8, 4096)
+    assert ws == 256 * 8 * 128 * 4 + 256 * 8 * 2 * 4
+    # B1: 64 splits of 512 keys keep 2048 workgroups busy
+    assert fa.decode_plan(1, 32, 32, 32768, 128)[:2] == (64, 512)
+    # one split: one workgroup walks the whole cache
+    assert fa.decode_plan(8, 32, 32, 32768, 128, 1)[:2] == (1, 32768)
+    # requests beyond the number of chunks are reduced
+    assert fa.decode_plan(1, 1, 1, 1, 64, 7)[0] == 1
+    assert fa.decode_workspace_bytes(8, 32, 32, 32768, 128, 0) == ws
+    for bad in ((0, 1, 1, 8, 64, 0), (1, 3, 2, 8, 64, 0), (1, 2, 1, 0, 64, 0), (1, 2, 1, 8, 96, 0),
+                (1, 2, 1, 8, 64, -1), (1, 2, 1, (1 << 30) + 1, 64, 0)):
+        assert fa.decode_workspace_bytes(*bad) == 0
+    with pytest.raises(fa.FaError) as e:
+        fa.decode_plan(1, 3, 2, 8, 64)
+    assert e.value.code == 2
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_plan_covers_keys(fa, seed):
+    """Every plan splits 0..N-1 into chunks that are nonempty, equal except
+    the last, and whole workgroup iterations long."""
+    import numpy as np
+
+    rng = np.random.default_rng([0xFA, 7, seed])
+    for _ in range(200):
+        hkv = int(rng.integers(1, 9))
+        H = hkv * int(rng.integers(1, 17))
+        B = int(rng.integers(1, 9))
+        N = int(rng.integers(1, 200000))
+        d = int(rng.choice([64, 128]))
+        req = int(rng.choice([0, 0, 1, int(rng.integers(1, 300))]))
+        sp, ck, ws = fa.decode_plan(B, H, hkv, N, d, req)
+        assert sp >= 1 and (sp - 1) * ck < N <= sp * ck
+        assert ck % 64 == 0
+        if req > 0:
+            assert sp <= req
+        base = sp * B * H
+        assert ws >= base * (d + 2) * 4 and ws <= base * (d + 2) * 4 + 256
+
+
+DW = A + 0x8000000
+DGOOD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, ws=DW,
+             ws_bytes=1 << 20, B=1, H=4, Hkv=2, N=300, d=64, scale=0.125, splits=0, dtype=1, stream=None)
+
+
+def dcall(fa, **over):
+    a = dict(DGOOD)
+    a.update(over)
+    return fa.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["ws_bytes"], a["B"], a["H"],
+                        a["Hkv"], a["N"], a["d"], a["scale"], a["splits"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(N=0), 2), (dict(splits=-1), 2),
+    (dict(N=(1 << 30) + 1), 2),
+    (dict(dtype=0), 3), (dict(dtype=4), 3),
+    (dict(d=96), 4), (dict(d=256), 4),
+    (dict(k=A + 0x1000008), 5), (dict(o=A + 0x3000002), 5), (dict(lse=A + 0x4000002), 5),
+    (dict(scale=float("nan")), 6),
+    (dict(o=A + 0x1000000), 8), (dict(lse=A + 0x3000010), 8), (dict(ws=A + 0x2000000), 8),
+    (dict(ws=0), 9), (dict(ws=DW + 64), 9), (dict(ws_bytes=100), 9),
+])
+def test_decode_validation_rejects_before_launch(fa, over, code):
+    assert dcall(fa, **over) == code
+
+
+def test_decode_binding_rejects_bad_tensors(fa):
+    import torch
+
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.decode(q, k, k)
+    with pytest.raises(TypeError):
+        fa.decode(q.float(), k.float(), k.float())

@@ -1,0 +1,160 @@
+"""GPU parity of fa_decode (split-K decode) against the fp64 oracle.
+
+Every case draws seeded q [B][H][d] and k, v [B][Hkv][N][d] from
+synthetic.py, runs aware_softmax_amd.decode (-> fa_decode through the C
+ABI) and compares o and lse of each checked (b, h) with
+oracle.naive_attention of that head's single query row against the keys
+and values of its key/value head h // (H / Hkv), non-causal (the decoded
+token sees the whole cache), on the same bf16 values upcast to fp64.
+
+Tolerance: the bf16 bar of the forward (max |o - ref| <= 2e-2,
+max |lse - ref| <= 1e-2) and, because decode keeps P in fp32 and rounds only
+o to bf16 (relative 2^-9), a per-element bound with a 2x margin over that
+rounding, |o - ref| <= 2^-8 |ref| + 1e-4, and |lse - ref| <= 2e-4 max(1, |ref|)
+(fp32 dot products of length d and fp32 accumulation over N keys).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import aware_softmax_amd
+
+    return aware_softmax_amd
+
+
+def to_device(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def check_heads(st, o, lse, heads, H, Hkv, scale):
+    group = H // Hkv
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for b, h in heads:
+        q = synthetic.bf16_bits_to_f32(st["q"][b, h])[None, :]
+        k = synthetic.bf16_bits_to_f32(st["k"][b, h // group])
+        v = synthetic.bf16_bits_to_f32(st["v"][b, h // group])
+        ref_o, ref_l = oracle.naive_attention(q, k, v, False, scale)
+        err_o = np.abs(o[b, h].astype(np.float64) - ref_o[0])
+        err_l = abs(float(lse[b, h]) - float(ref_l[0]))
+        assert err_o.max() <= 2e-2, f"o[{b},{h}] max err {err_o.max():.3e}"
+        assert err_l <= 1e-2, f"lse[{b},{h}] err {err_l:.3e}"
+        assert np.all(err_o <= 2.0 ** -8 * np.abs(ref_o[0]) + 1e-4), \
+            f"o[{b},{h}] exceeds the rounding bound: {np.max(err_o - 2.0 ** -8 * np.abs(ref_o[0])):.3e}"
+        assert err_l <= 2e-4 * max(1.0, abs(float(ref_l[0]))), f"lse[{b},{h}] err {err_l:.3e}"
+
+
+def run(fa, cid, B, H, Hkv, N, d, scale=None, num_splits=0, heads=None, st=None):
+    import torch
+
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = synthetic.decode_storage(cid, B, H, Hkv, N, d) if st is None else st
+    q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
+    o, lse = fa.decode(q, k, v, scale=scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    check_heads(st, o, lse, heads, H, Hkv, scale)
+    return o, lse
+
+
+# ------------------------------------------------------------ the workloads
+
+
+@pytest.mark.parametrize("cid", [6, 7, 8])
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_decode_workloads(fa, cid, num_splits):
+    """The decode problems at full size, split automatically and unsplit;
+    32 seeded heads (all heads for B = 1)."""
+    w = synthetic.DECODE_WORKLOADS[cid]
+    heads = synthetic.sample_heads(cid, w.B, w.H, 32)
+    run(fa, cid, w.B, w.H, w.Hkv, w.N, w.d, num_splits=num_splits, heads=heads)
+
+
+# ------------------------------------------------------------ shapes and edges
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 4097])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2), (12, 1)])
+def test_ragged_decode(fa, n, d, heads):
+    H, Hkv = heads
+    run(fa, 7000 + n * 8 + (d == 128) * 4 + Hkv, 2, H, Hkv, n, d)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 5, 64, 10000])
+def test_forced_splits(fa, num_splits):
+    run(fa, 7100, 1, 8, 2, 5000, 128, num_splits=num_splits)
+
+
+@pytest.mark.parametrize("group", [2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 16])
+def test_group_sizes(fa, group):
+    """Query-head groups of every size a workgroup serves (1..8) and
+    groups split over several workgroups (9, 12, 16) or unsplittable (11)."""
+    run(fa, 7200 + group, 2, 2 * group, 2, 777, 128)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.5, 2.0])
+def test_other_scales(fa, scale):
+    run(fa, 7300 + int(scale * 10), 2, 4, 4, 3000, 128, scale=scale)
+
+
+def test_scale_zero_is_mean_of_values(fa):
+    """No oracle: with scale 0 every weight is 1/N, so o is the mean of the
+    value rows and lse = ln N."""
+    import torch
+
+    B, H, Hkv, N, d = 1, 4, 2, 2500, 64
+    st = synthetic.decode_storage(7400, B, H, Hkv, N, d)
+    q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
+    o, lse = fa.decode(q, k, v, scale=0.0)
+    torch.cuda.synchronize()
+    mean_v = synthetic.bf16_bits_to_f32(st["v"]).astype(np.float64).mean(axis=2)  # [B][Hkv][d]
+    got = o.float().cpu().numpy()
+    for h in range(H):
+        assert np.all(np.abs(got[0, h] - mean_v[0, h // 2]) <= 2.0 ** -8 * np.abs(mean_v[0, h // 2]) + 1e-4)
+    assert np.allclose(lse.cpu().numpy(), math.log(N), atol=1e-5, rtol=0)
+
+
+def test_deterministic_and_dirty_workspace(fa):
+    """No atomics: two calls with the same split agree bitwise, also when
+    the workspace starts out full of NaNs."""
+    import torch
+
+    B, H, Hkv, N, d = 2, 8, 4, 3333, 128
+    st = synthetic.decode_storage(7500, B, H, Hkv, N, d)
+    q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
+    need = fa.decode_plan(B, H, Hkv, N, d)[2]
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    o1, l1 = fa.decode(q, k, v, workspace=ws.view(torch.uint8))
+    o2, l2 = fa.decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.isfinite(o1.float()).all()
+
+
+def test_outputs_untouched_outside_bounds(fa):
+    import torch
+
+    B, H, Hkv, N, d = 1, 4, 4, 300, 64
+    st = synthetic.decode_storage(7600, B, H, Hkv, N, d)
+    q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
+    size = B * H * d
+    ob = torch.full((size + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((B * H + 64,), 7.0, dtype=torch.float32, device="cuda")
+    fa.decode(q, k, v, out=ob[:size].view(B, H, d), lse=lb[:B * H].view(B, H))
+    torch.cuda.synchronize()
+    assert torch.all(ob[size:] == 7.0) and torch.all(lb[B * H:] == 7.0)
+    check_heads(st, ob[:size].view(B, H, d), lb[:B * H].view(B, H), [(0, h) for h in range(H)], H, Hkv,
+                1.0 / math.sqrt(d))
