@@ -58,7 +58,7 @@ struct Shape {
 // Loads in flight per wave and iteration (K and V each).
 template <int G>
 constexpr int unroll() {
-  return G <= 2 ? 8 : 4;
+  return G <= 4 ? 8 : 4;
 }
 
 // Rows of one workgroup iteration: every wave reads unroll() instructions
@@ -268,8 +268,10 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const float* ml = part_ml + (size_t)bh * S * 2;
   const float* po = part_o + (size_t)bh * S * D + e;
   float mm = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < S; ++s) mm = fmaxf(mm, ml[2 * s]);
   float ll = 0.f, oo = 0.f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mm);
     ll = fmaf(wt, ml[2 * s + 1], ll);
@@ -332,10 +334,12 @@ hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t s
 }  // namespace
 
 // Split plan.  Chunks are whole workgroup iterations; with num_splits = 0
-// the count aims at >= kTargetWgs workgroups in all (eight per CU) while
-// keeping every chunk at least one iteration long.
+// the count aims at kTargetWgs workgroups in all, two per CU: measured over
+// batch 1-16, 8-64 heads, group sizes 1-8 and N = 8K-128K, one or two
+// resident workgroups per CU (each wave with 8-16 KiB of loads in flight)
+// already saturate HBM, and more splits only add partials and tail.
 DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits) {
-  constexpr int64_t kTargetWgs = 2048;
+  constexpr int64_t kTargetWgs = 512;
   DecodePlan pl{};
   const int group = H / Hkv;
   pl.heads_per_wg = heads_per_wg(group);

@@ -206,12 +206,14 @@ def test_bwd_binding_rejects_bad_tensors(fa):
 # ------------------------------------------------------------------ decode
 
 def test_decode_plan_values(fa):
-    # B8 H32 N32768 d128 (multi-head): 256 (b, h) pairs x 8 splits of 4096 keys
+    # B8 H32 N32768 d128 (multi-head): 256 (b, h) pairs x 2 splits of 16384 keys
     sp, ck, ws = fa.decode_plan(8, 32, 32, 32768, 128)
-    assert (sp, ck) == (8, 4096)
-    assert ws == 256 * 8 * 128 * 4 + 256 * 8 * 2 * 4
-    # B1: 64 splits of 512 keys keep 2048 workgroups busy
-    assert fa.decode_plan(1, 32, 32, 32768, 128)[:2] == (64, 512)
+    assert (sp, ck) == (2, 16384)
+    assert ws == 256 * 2 * 128 * 4 + 256 * 2 * 2 * 4
+    # B1: 16 splits of 2048 keys give 512 workgroups (two per CU)
+    assert fa.decode_plan(1, 32, 32, 32768, 128)[:2] == (16, 2048)
+    # four query heads per key/value head: one workgroup serves all four
+    assert fa.decode_plan(8, 32, 8, 32768, 128)[:2] == (8, 4096)
     # one split: one workgroup walks the whole cache
     assert fa.decode_plan(8, 32, 32, 32768, 128, 1)[:2] == (1, 32768)
     # requests beyond the number of chunks are reduced
