@@ -19,10 +19,11 @@ constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
 size_t elem_size(fa_dtype_t dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 
+// Head dims of the forward: bf16 32, 64, 96, 128, 256; fp32 32, 64, 96, 128.
 fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  return FA_OK;
+  const bool ok = d == 32 || d == 64 || d == 96 || d == 128 || (d == 256 && dtype == FA_DTYPE_BF16);
+  return ok ? FA_OK : FA_ERR_UNSUPPORTED_HEADDIM;
 }
 
 }  // namespace
@@ -35,7 +36,7 @@ const char* fa_status_string(fa_status_t status) {
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be positive, consistent and within the supported range";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
-    case FA_ERR_UNSUPPORTED_HEADDIM: return "FA_ERR_UNSUPPORTED_HEADDIM: d must be 64 or 128";
+    case FA_ERR_UNSUPPORTED_HEADDIM: return "FA_ERR_UNSUPPORTED_HEADDIM: this entry point and dtype do not support this head dim";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte and lse 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP kernel launch failed";

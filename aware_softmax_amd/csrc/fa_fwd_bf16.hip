@@ -170,8 +170,11 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
   return alpha;
 }
 
+// Any d that is a multiple of 32 (one 32-wide output block per step); two
+// workgroups per CU up to d = 128, one at d = 256 (O^T alone is 128 fp32
+// per lane there, and two K/V stages take 137 KB of LDS).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
     __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate) {
   using Ly = Layout<D>;
@@ -923,8 +926,9 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 
 // Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 (FULL when
 // the sequence is a whole number of key tiles: no row clamping in the
-// copies), the 4-wave kernel for d = 64 (whose 8 + 8 MFMAs per tile leave too few
-// slots to hide the softmax of a 64-key tile).
+// copies), the 4-wave kernel for d = 32, 64, 96 and 256 (at d <= 96 the
+// 2d/16 + 2d/16 MFMAs per tile leave too few slots to hide the softmax of a
+// 64-key tile; at d = 256 two waves per SIMD do not fit the registers).
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr bool kDuo = D == 128;
@@ -956,8 +960,14 @@ TileConfig bf16_tile(int d) {
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  switch (p.d) {
+    case 32: return p.causal ? launch<32, true>(p, stream) : launch<32, false>(p, stream);
+    case 64: return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+    case 96: return p.causal ? launch<96, true>(p, stream) : launch<96, false>(p, stream);
+    case 128: return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+    case 256: return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

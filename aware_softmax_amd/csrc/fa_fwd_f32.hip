@@ -167,8 +167,13 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
 TileConfig f32_tile(int) { return TileConfig{kBQ, kBK, kThreads / 64}; }
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-  return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  switch (p.d) {
+    case 32: return p.causal ? launch<32, true>(p, stream) : launch<32, false>(p, stream);
+    case 64: return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
+    case 96: return p.causal ? launch<96, true>(p, stream) : launch<96, false>(p, stream);
+    case 128: return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

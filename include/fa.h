@@ -52,7 +52,7 @@ typedef enum {
   FA_ERR_NULL = 1,                 /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,                /* a size <= 0, sizes too large, or inconsistent */
   FA_ERR_DTYPE = 3,                /* dtype is not a fa_dtype_t value */
-  FA_ERR_UNSUPPORTED_HEADDIM = 4,  /* d is not 64 or 128 */
+  FA_ERR_UNSUPPORTED_HEADDIM = 4,  /* d is not supported by the entry point for this dtype */
   FA_ERR_ALIGN = 5,                /* q/k/v/o not 16-byte or lse not 4-byte aligned */
   FA_ERR_SCALE = 6,                /* scale is NaN or infinite */
   FA_ERR_HIP = 7,                  /* the HIP launch reported an error */
@@ -68,7 +68,9 @@ typedef enum {
  *                  overlap q, k, v or lse.
  *   lse      [out] device, [B][H][N] float32, 4-byte aligned.
  *   B, H, N  sizes (> 0); any N >= 1 (ragged tails are masked).
- *   d        head dimension: 64 or 128.
+ *   d        head dimension: 32, 64, 96, 128 or 256 for bf16; 32, 64, 96
+ *            or 128 for fp32 ("PidokuInfra 10 -- FlashAttention", section
+ *            9: kernels commonly cover 64, 96, 128 and 256).
  *   causal   0: every query sees all N keys; nonzero: query i sees 0..i.
  *   scale    multiplies Q K^T before mask and softmax (finite; 1/sqrt(d)
  *            in the usual case; 0 and negative values are allowed).

@@ -66,8 +66,13 @@ def test_tile_config(fa):
     assert bk == 64 and bq == 32 * w and w in (4, 8)
     assert fa.tile_config(64, fa.DTYPE_BF16)[0] > 0
     assert fa.tile_config(64, fa.DTYPE_F32)[0] > 0
+    for d in (32, 96, 256):
+        assert fa.tile_config(d, fa.DTYPE_BF16)[0] > 0
     with pytest.raises(fa.FaError) as e:
-        fa.tile_config(96, fa.DTYPE_BF16)
+        fa.tile_config(80, fa.DTYPE_BF16)
+    assert e.value.code == 4
+    with pytest.raises(fa.FaError) as e:
+        fa.tile_config(256, fa.DTYPE_F32)
     assert e.value.code == 4
     with pytest.raises(fa.FaError) as e:
         fa.tile_config(64, 7)
@@ -93,7 +98,7 @@ def call(fa, **over):
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(d=0), 2),
     (dict(B=1 << 20, H=1 << 12, N=1 << 20), 2),
     (dict(dtype=2), 3), (dict(dtype=-1), 3),
-    (dict(d=96), 4), (dict(d=256), 4), (dict(d=32), 4),
+    (dict(d=48), 4), (dict(d=160), 4), (dict(d=512), 4), (dict(d=256, dtype=0), 4),
     (dict(q=A + 8), 5), (dict(o=A + 0x3000004), 5), (dict(lse=A + 0x4000002), 5),
     (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6),
     (dict(o=A), 8), (dict(lse=A + 0x3000100), 8), (dict(lse=A + 0x2000000), 8),

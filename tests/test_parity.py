@@ -122,11 +122,28 @@ def test_ragged_bf16(fa, n, d, causal):
     assert_close(run_case(fa, cid, 2, 3, n, d, "bf16", causal), "bf16")
 
 
+@pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 333, 1000])
+@pytest.mark.parametrize("d", [32, 96, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_bf16(fa, n, d, causal):
+    """The other head dims the pages list as common (96, 256) and d = 32."""
+    cid = 1500 + n * 8 + (d // 32) * 2 + causal
+    assert_close(run_case(fa, cid, 2, 3, n, d, "bf16", causal), "bf16")
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_head_dims_bf16_long(fa, d):
+    """B2 H8 N4096 causal: many key tiles per workgroup, sampled rows."""
+    rows = synthetic.sample_rows(1600 + d, 4096, 256)
+    assert_close(run_case(fa, 1600 + d, 2, 8, 4096, d, "bf16", True, rows=rows,
+                          heads=synthetic.sample_heads(1600 + d, 2, 8, 4)), "bf16")
+
+
 @pytest.mark.parametrize("n", [1, 5, 64, 100, 257])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_fp32(fa, n, d, causal):
-    cid = 3000 + n * 4 + (d == 128) * 2 + causal
+    cid = 3000 + n * 16 + (d // 32) * 2 + causal
     assert_close(run_case(fa, cid, 1, 2, n, d, "f32", causal), "f32")
 
 
