@@ -169,7 +169,7 @@ fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, 
                            size_t* workspace_bytes) {
   if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || num_splits < 0) return FA_ERR_SHAPE;
   if (H % Hkv != 0 || N > (1 << 30)) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED_HEADDIM;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX || (int64_t)B * Hkv * N * d > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
   const fa::DecodePlan pl = fa::decode_plan(B, H, Hkv, N, d, num_splits);

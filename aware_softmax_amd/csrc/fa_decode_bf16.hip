@@ -21,11 +21,11 @@
 //
 // MI355X mapping.  The work is a matrix-vector product per head, bound by
 // reading K and V from HBM once; it runs on the VALU (v_dot2_f32_bf16), not
-// on MFMA.  D/8 lanes share one key row, each holding 16 bytes (8 bf16) of
-// it, so one wave instruction reads 64 x 16 = 1 KiB of contiguous K or V;
-// the row's dot product is finished by a DPP reduction inside the 16-lane
-// (d = 128) or 8-lane (d = 64) group, which leaves the score in every lane
-// of the group.  Each lane keeps its own online-softmax state (m, l and its
+// on MFMA.  A group of LPR lanes (4, 8 or 16) shares one key row, each lane
+// holding CPL 16-byte chunks (8 bf16 each) of it, so one wave instruction
+// reads 64 x 16 = 1 KiB of K or V in runs of at least 64 contiguous bytes;
+// the row's dot product is finished by a DPP reduction inside the lane
+// group, which leaves the score in every lane of the group.  Each lane keeps its own online-softmax state (m, l and its
 // 8 elements of o~) over the rows it has seen, so the hot loop has no
 // cross-lane max at all; the states of a workgroup are merged once at the
 // end.  A group of G query heads that share a key/value head is served by
@@ -46,26 +46,39 @@ constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// Largest query-head group one workgroup serves (a divisor of H / Hkv).
-constexpr int kMaxGroup = 8;
-
+// Row split per head dim: CPL 16-byte chunks per lane, LPR lanes per row
+// (d = 32: 4 x 1, 64: 8 x 1, 96: 4 x 3, 128: 16 x 1, 256: 16 x 2); lane cc
+// holds chunks cc, cc + LPR, ..., cc + (CPL - 1) LPR of its row.
 template <int D>
 struct Shape {
-  static constexpr int LPR = D / 8;         // lanes per key row (16 B each)
-  static constexpr int RPI = 64 / LPR;      // key rows per wave instruction
+  static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "head dim");
+  static constexpr int CPL = D == 96 ? 3 : D == 256 ? 2 : 1;
+  static constexpr int LPR = D / 8 / CPL;  // lanes per key row
+  static constexpr int RPI = 64 / LPR;     // key rows per wave instruction
 };
 
-// Loads in flight per wave and iteration (K and V each).
-template <int G>
+// Largest query-head group one workgroup serves (a divisor of H / Hkv):
+// each head keeps 8 CPL fp32 of o~ per lane.
+template <int D>
+constexpr int max_group() {
+  return D >= 256 ? 4 : 8;
+}
+int max_group_rt(int d) { return d >= 256 ? max_group<256>() : max_group<128>(); }
+
+// Row-group instructions per wave and iteration (K and V each): about 8
+// loads of 16 bytes in flight per tensor for groups of up to 4 heads, 4
+// for larger groups.
+template <int D, int G>
 constexpr int unroll() {
-  return G <= 4 ? 8 : 4;
+  constexpr int loads = G <= 4 ? 8 : 4;
+  return loads / Shape<D>::CPL > 0 ? loads / Shape<D>::CPL : 1;
 }
 
 // Rows of one workgroup iteration: every wave reads unroll() instructions
 // of RPI rows.
 template <int D, int G>
 constexpr int rows_per_iter() {
-  return kWaves * unroll<G>() * Shape<D>::RPI;
+  return kWaves * unroll<D, G>() * Shape<D>::RPI;
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
@@ -73,11 +86,13 @@ __device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_c
 // Sum over the LPR lanes of a key row; every lane of the group gets the sum.
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "lane group of 4, 8 or 16");
   // quad_perm [1,0,3,2], quad_perm [2,3,0,1]: sums over each 4-lane quad.
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
   x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
   // row_half_mirror: lane i of an 8-lane half reads lane 7 - i (the other quad).
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if constexpr (LPR >= 8)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
   if constexpr (LPR == 16)  // row_mirror: lane i of a 16-lane row reads lane 15 - i.
     x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
   return x;
@@ -93,7 +108,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c) {
   constexpr int LPR = Shape<D>::LPR;
   constexpr int RPI = Shape<D>::RPI;
-  constexpr int U = unroll<G>();
+  constexpr int CPL = Shape<D>::CPL;
+  constexpr int E = 8 * CPL;  // elements of a row per lane
+  constexpr int U = unroll<D, G>();
   constexpr int ROWS_WAVE = U * RPI;  // rows per wave and iteration
   constexpr float kNegInf = -__builtin_inff();
 
@@ -110,27 +127,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int cc = lane % LPR;  // 16-byte chunk of the row this lane holds
+  const int cc = lane % LPR;  // first 16-byte chunk of the row this lane holds
   const int rr = lane / LPR;  // row within a wave instruction
 
-  // Query fragments: elements 8cc .. 8cc+7 of each head's query.
-  unsigned qf[G][4];
+  // Query fragments: the lane's chunks cc + x LPR of each head's query.
+  unsigned qf[G][4 * CPL];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const u32x4 t = *(const u32x4*)(q + ((size_t)b * H + h0 + i) * D + cc * 8);
-    qf[i][0] = t[0];
-    qf[i][1] = t[1];
-    qf[i][2] = t[2];
-    qf[i][3] = t[3];
-  }
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int x = 0; x < CPL; ++x) {
+      const u32x4 t = *(const u32x4*)(q + ((size_t)b * H + h0 + i) * D + (cc + x * LPR) * 8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) qf[i][4 * x + w] = t[w];
+    }
 
-  float m[G], l[G], o[G][8];
+  float m[G], l[G], o[G][E];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     m[i] = kNegInf;
     l[i] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
+    for (int e = 0; e < E; ++e) o[i][e] = 0.f;
   }
 
   const int k_begin = s * chunk;
@@ -140,23 +157,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const __bf16* vh = v + head_off + cc * 8;
 
   for (int r0 = k_begin + wave * ROWS_WAVE; r0 < k_end; r0 += kWaves * ROWS_WAVE) {
-    u32x4 kf[U], vf[U];
+    u32x4 kf[U][CPL], vf[U][CPL];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = r0 + u * RPI + rr;
       ok[u] = row < k_end;
       const int rc = ok[u] ? row : k_end - 1;  // clamped rows are loaded but scored -inf
-      kf[u] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)rc * D));
+#pragma unroll
+      for (int x = 0; x < CPL; ++x)
+        kf[u][x] = __builtin_nontemporal_load((const u32x4*)(kh + (size_t)rc * D + x * LPR * 8));
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = r0 + u * RPI + rr;
       const int rc = row < k_end ? row : k_end - 1;
-      vf[u] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)rc * D));
+#pragma unroll
+      for (int x = 0; x < CPL; ++x)
+        vf[u][x] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)rc * D + x * LPR * 8));
     }
     // V rows as fp32 (bf16 is the high half of an fp32).
-    float vv[U][8];
+    float vv[U][E];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       float sc[U];
@@ -165,8 +186,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       for (int u = 0; u < U; ++u) {
         float acc = 0.f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qf[i][t]), as_bf16x2(kf[u][t]), acc, false);
+        for (int x = 0; x < CPL; ++x)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qf[i][4 * x + t]), as_bf16x2(kf[u][x][t]), acc, false);
         acc = row_sum<LPR>(acc);
         sc[u] = ok[u] ? acc * c : kNegInf;
         tmax = fmaxf(tmax, sc[u]);
@@ -187,13 +210,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            vv[u][2 * t] = __builtin_bit_cast(float, vf[u][t] << 16);
-            vv[u][2 * t + 1] = __builtin_bit_cast(float, vf[u][t] & 0xffff0000u);
-          }
+          for (int x = 0; x < CPL; ++x)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              vv[u][8 * x + 2 * t] = __builtin_bit_cast(float, vf[u][x][t] << 16);
+              vv[u][8 * x + 2 * t + 1] = __builtin_bit_cast(float, vf[u][x][t] & 0xffff0000u);
+            }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < E; ++e) {
         float acc = o[i][e] * alpha;
 #pragma unroll
         for (int u = 0; u < U; ++u) acc = fmaf(p[u], vv[u][e], acc);
@@ -215,18 +240,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int sh = LPR; sh < 64; sh <<= 1) mm = fmaxf(mm, __shfl_xor(mm, sh));
     const float w = __builtin_amdgcn_exp2f(m[i] - (mm == kNegInf ? 0.f : mm));
     float ll = l[i] * w;
-    float oo[8];
+    float oo[E];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) oo[e] = o[i][e] * w;
+    for (int e = 0; e < E; ++e) oo[e] = o[i][e] * w;
 #pragma unroll
     for (int sh = LPR; sh < 64; sh <<= 1) {
       ll += __shfl_xor(ll, sh);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) oo[e] += __shfl_xor(oo[e], sh);
+      for (int e = 0; e < E; ++e) oo[e] += __shfl_xor(oo[e], sh);
     }
     if (rr == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][i][cc * 8 + e] = oo[e];
+      for (int x = 0; x < CPL; ++x)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm_o[wave][i][(cc + x * LPR) * 8 + e] = oo[8 * x + e];
       if (cc == 0) {
         sm_m[wave][i] = mm;
         sm_l[wave][i] = ll;
@@ -282,8 +309,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
 }
 
 // Largest divisor of the query-head group that one workgroup serves.
-int heads_per_wg(int group) {
-  for (int g = kMaxGroup; g > 1; --g)
+int heads_per_wg(int group, int d) {
+  for (int g = max_group_rt(d); g > 1; --g)
     if (group % g == 0) return g;
   return 1;
 }
@@ -299,6 +326,16 @@ int rows_per_iter_rt(int G) {
     case 6: return rows_per_iter<D, 6>();
     case 7: return rows_per_iter<D, 7>();
     default: return rows_per_iter<D, 8>();
+  }
+}
+
+int rows_per_iter_d(int d, int G) {
+  switch (d) {
+    case 32: return rows_per_iter_rt<32>(G);
+    case 64: return rows_per_iter_rt<64>(G);
+    case 96: return rows_per_iter_rt<96>(G);
+    case 128: return rows_per_iter_rt<128>(G);
+    default: return rows_per_iter_rt<256>(G);
   }
 }
 
@@ -319,15 +356,24 @@ hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t s
 
 template <int D>
 hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
-  switch (plan.heads_per_wg) {
-    case 1: return launch_g<D, 1>(p, plan, stream);
-    case 2: return launch_g<D, 2>(p, plan, stream);
-    case 3: return launch_g<D, 3>(p, plan, stream);
-    case 4: return launch_g<D, 4>(p, plan, stream);
-    case 5: return launch_g<D, 5>(p, plan, stream);
-    case 6: return launch_g<D, 6>(p, plan, stream);
-    case 7: return launch_g<D, 7>(p, plan, stream);
-    default: return launch_g<D, 8>(p, plan, stream);
+  if constexpr (max_group<D>() == 4) {
+    switch (plan.heads_per_wg) {
+      case 1: return launch_g<D, 1>(p, plan, stream);
+      case 2: return launch_g<D, 2>(p, plan, stream);
+      case 3: return launch_g<D, 3>(p, plan, stream);
+      default: return launch_g<D, 4>(p, plan, stream);
+    }
+  } else {
+    switch (plan.heads_per_wg) {
+      case 1: return launch_g<D, 1>(p, plan, stream);
+      case 2: return launch_g<D, 2>(p, plan, stream);
+      case 3: return launch_g<D, 3>(p, plan, stream);
+      case 4: return launch_g<D, 4>(p, plan, stream);
+      case 5: return launch_g<D, 5>(p, plan, stream);
+      case 6: return launch_g<D, 6>(p, plan, stream);
+      case 7: return launch_g<D, 7>(p, plan, stream);
+      default: return launch_g<D, 8>(p, plan, stream);
+    }
   }
 }
 
@@ -342,8 +388,8 @@ DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits) {
   constexpr int64_t kTargetWgs = 512;
   DecodePlan pl{};
   const int group = H / Hkv;
-  pl.heads_per_wg = heads_per_wg(group);
-  const int rows = d == 128 ? rows_per_iter_rt<128>(pl.heads_per_wg) : rows_per_iter_rt<64>(pl.heads_per_wg);
+  pl.heads_per_wg = heads_per_wg(group, d);
+  const int rows = rows_per_iter_d(d, pl.heads_per_wg);
   const int64_t iters = ((int64_t)N + rows - 1) / rows;
   const int64_t base = (int64_t)B * Hkv * (group / pl.heads_per_wg);
   int64_t want = num_splits > 0 ? num_splits : (kTargetWgs + base - 1) / base;
@@ -359,13 +405,18 @@ DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits) {
   return pl;
 }
 
-int decode_rows_per_iter(int d, int heads_per_wg) {
-  return d == 128 ? rows_per_iter_rt<128>(heads_per_wg) : rows_per_iter_rt<64>(heads_per_wg);
-}
+int decode_rows_per_iter(int d, int heads_per_wg) { return rows_per_iter_d(d, heads_per_wg); }
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
   const DecodePlan plan = decode_plan(p.B, p.H, p.Hkv, p.N, p.d, p.num_splits);
-  return p.d == 128 ? launch_d<128>(p, plan, stream) : launch_d<64>(p, plan, stream);
+  switch (p.d) {
+    case 32: return launch_d<32>(p, plan, stream);
+    case 64: return launch_d<64>(p, plan, stream);
+    case 96: return launch_d<96>(p, plan, stream);
+    case 128: return launch_d<128>(p, plan, stream);
+    case 256: return launch_d<256>(p, plan, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

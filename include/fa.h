@@ -189,7 +189,8 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
  *             bytes (passed as workspace_bytes), 256-byte aligned, owned by
  *             the caller; overwritten, needs no initialisation.
  *   B, H, Hkv, N, d   batch, query heads, key/value heads (H % Hkv == 0),
- *             cached keys (1 <= N <= 2^30), head dim (64 or 128).
+ *             cached keys (1 <= N <= 2^30), head dim (32, 64, 96, 128
+ *             or 256).
  *   scale     finite; multiplies q . k.
  *   num_splits  as for fa_decode_plan.
  *   dtype     FA_DTYPE_BF16 only.

@@ -224,7 +224,7 @@ def test_decode_plan_values(fa):
     # requests beyond the number of chunks are reduced
     assert fa.decode_plan(1, 1, 1, 1, 64, 7)[0] == 1
     assert fa.decode_workspace_bytes(8, 32, 32, 32768, 128, 0) == ws
-    for bad in ((0, 1, 1, 8, 64, 0), (1, 3, 2, 8, 64, 0), (1, 2, 1, 0, 64, 0), (1, 2, 1, 8, 96, 0),
+    for bad in ((0, 1, 1, 8, 64, 0), (1, 3, 2, 8, 64, 0), (1, 2, 1, 0, 64, 0), (1, 2, 1, 8, 80, 0),
                 (1, 2, 1, 8, 64, -1), (1, 2, 1, (1 << 30) + 1, 64, 0)):
         assert fa.decode_workspace_bytes(*bad) == 0
     with pytest.raises(fa.FaError) as e:
@@ -244,7 +244,7 @@ def test_decode_plan_covers_keys(fa, seed):
         H = hkv * int(rng.integers(1, 17))
         B = int(rng.integers(1, 9))
         N = int(rng.integers(1, 200000))
-        d = int(rng.choice([64, 128]))
+        d = int(rng.choice([32, 64, 96, 128, 256]))
         req = int(rng.choice([0, 0, 1, int(rng.integers(1, 300))]))
         sp, ck, ws = fa.decode_plan(B, H, hkv, N, d, req)
         assert sp >= 1 and (sp - 1) * ck < N <= sp * ck
@@ -272,7 +272,7 @@ def dcall(fa, **over):
     (dict(B=0), 2), (dict(Hkv=3), 2), (dict(Hkv=0), 2), (dict(N=0), 2), (dict(splits=-1), 2),
     (dict(N=(1 << 30) + 1), 2),
     (dict(dtype=0), 3), (dict(dtype=4), 3),
-    (dict(d=96), 4), (dict(d=256), 4),
+    (dict(d=80), 4), (dict(d=512), 4),
     (dict(k=A + 0x1000008), 5), (dict(o=A + 0x3000002), 5), (dict(lse=A + 0x4000002), 5),
     (dict(scale=float("nan")), 6),
     (dict(o=A + 0x1000000), 8), (dict(lse=A + 0x3000010), 8), (dict(ws=A + 0x2000000), 8),

@@ -92,6 +92,20 @@ def test_ragged_decode(fa, n, d, heads):
     run(fa, 7000 + n * 8 + (d == 128) * 4 + Hkv, 2, H, Hkv, n, d)
 
 
+@pytest.mark.parametrize("n", [1, 65, 1000, 4097])
+@pytest.mark.parametrize("d", [32, 96, 256])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2), (12, 1)])
+def test_head_dims_decode(fa, n, d, heads):
+    """The other head dims (lanes per key row 4 or 16, up to 3 chunks per lane)."""
+    H, Hkv = heads
+    run(fa, 7700 + n * 8 + Hkv + d, 2, H, Hkv, n, d)
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_head_dims_decode_long(fa, d):
+    run(fa, 7800 + d, 2, 16, 4, 20000, d, heads=synthetic.sample_heads(7800 + d, 2, 16, 8))
+
+
 @pytest.mark.parametrize("num_splits", [1, 2, 3, 5, 64, 10000])
 def test_forced_splits(fa, num_splits):
     run(fa, 7100, 1, 8, 2, 5000, 128, num_splits=num_splits)
