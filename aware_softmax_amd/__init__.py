@@ -15,6 +15,8 @@ __all__ = [
     "FaError",
     "fwd",
     "fa_fwd",
+    "fa_fwd_gqa",
+    "fa_bwd_gqa",
     "bwd",
     "fa_bwd",
     "bwd_workspace_bytes",
@@ -57,6 +59,8 @@ def _load() -> ctypes.CDLL:
     vp, ci = ctypes.c_void_p, ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd.restype = ci
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_fwd_gqa.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd_tile.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
@@ -64,6 +68,9 @@ def _load() -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_bwd.restype = ci
+    lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ctypes.c_float,
+                               ci, vp]
+    lib.fa_bwd_gqa.restype = ci
     lib.fa_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_tile.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
@@ -114,9 +121,17 @@ def fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, scale, dtype
                        int(bool(causal)), float(scale), int(dtype), stream)
 
 
+def fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, causal, scale, dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses."""
+    return _LIB.fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(Hkv), int(N), int(d),
+                           int(bool(causal)), float(scale), int(dtype), stream)
+
+
 def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, stream=None):
     """O, L = attention forward of [B, H, N, d] device tensors (bf16 or fp32).
 
+    k and v may have fewer heads, [B, Hkv, N, d] with H a multiple of Hkv
+    (grouped heads: query head h reads key/value head h // (H // Hkv)).
     Returns (o, lse): o like q, lse float32 [B, H, N] (natural-log
     logsumexp of each scaled, masked score row).  out / lse may be passed to
     reuse buffers.  Runs on `stream` (default: torch's current stream).
@@ -129,17 +144,18 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         dtype = DTYPE_F32
     else:
         raise TypeError(f"unsupported dtype {q.dtype}; use torch.bfloat16 or torch.float32")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
     for name, t in (("k", k), ("v", v)):
-        if t.dtype != q.dtype or t.shape != q.shape:
-            raise ValueError(f"{name} must match q in dtype and shape")
+        if t.dtype != q.dtype or t.shape != (B, Hkv, N, d):
+            raise ValueError(f"{name} must be [B, Hkv, N, d] with the dtype, B, N and d of q")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    if q.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, N, d]")
-    B, H, N, d = q.shape
+            raise ValueError(f"{name} must be contiguous")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -152,8 +168,8 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    _check(fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                  B, H, N, d, causal, scale, dtype, stream.cuda_stream))
+    _check(fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, Hkv, N, d, causal, scale, dtype, stream.cuda_stream))
     return out, lse
 
 
@@ -178,9 +194,20 @@ def fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, 
                        int(dtype), stream)
 
 
+def fa_bwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, ws_bytes,
+               B, H, Hkv, N, d, causal, scale, dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses."""
+    return _LIB.fa_bwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                           int(ws_bytes), int(B), int(H), int(Hkv), int(N), int(d), int(bool(causal)),
+                           float(scale), int(dtype), stream)
+
+
 def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
         workspace=None, stream=None):
     """dQ, dK, dV of attention for [B, H, N, d] bf16 device tensors.
+
+    k and v (and so dk, dv) may be [B, Hkv, N, d] with H a multiple of Hkv,
+    as in fwd(); dk and dv then sum over the query heads of each group.
 
     o and lse are the outputs of fwd() for the same q, k, v, causal and
     scale; do is the upstream gradient of o.  dq / dk / dv / workspace may
@@ -192,35 +219,37 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
 
     if q.dtype != torch.bfloat16:
         raise TypeError(f"unsupported dtype {q.dtype} for the backward; use torch.bfloat16")
-    if q.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, N, d]")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        if t.dtype != q.dtype or t.shape != q.shape:
-            raise ValueError(f"{name} must match q in dtype and shape")
+        want = (B, Hkv, N, d) if name in ("k", "v") else q.shape
+        if t.dtype != q.dtype or t.shape != want:
+            raise ValueError(f"{name} must be a {q.dtype} tensor of shape {tuple(want)}")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    B, H, N, d = q.shape
+            raise ValueError(f"{name} must be contiguous")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor like q")
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
+        if t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {tuple(like.shape)}")
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                  workspace.numel() * workspace.element_size(), B, H, N, d, causal, scale, DTYPE_BF16,
-                  stream.cuda_stream))
+    _check(fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, causal, scale, DTYPE_BF16,
+                      stream.cuda_stream))
     return dq, dk, dv
 
 

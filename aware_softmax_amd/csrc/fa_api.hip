@@ -59,10 +59,10 @@ fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int
   return FA_OK;
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                   int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
   const fa_status_t st = check_dtype_headdim(d, dtype);
   if (st != FA_OK) return st;
   // Sizes: element offsets are 64-bit in the kernels; the grid is one int.
@@ -77,11 +77,12 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
     return FA_ERR_ALIGN;
   const size_t tbytes = (size_t)elems * elem_size(dtype);
+  const size_t kvbytes = (size_t)B * Hkv * N * d * elem_size(dtype);
   const size_t lbytes = (size_t)bh * N * sizeof(float);
-  if (ranges_overlap(o, tbytes, q, tbytes) || ranges_overlap(o, tbytes, k, tbytes) ||
-      ranges_overlap(o, tbytes, v, tbytes) || ranges_overlap(o, tbytes, lse, lbytes) ||
-      ranges_overlap(lse, lbytes, q, tbytes) || ranges_overlap(lse, lbytes, k, tbytes) ||
-      ranges_overlap(lse, lbytes, v, tbytes))
+  if (ranges_overlap(o, tbytes, q, tbytes) || ranges_overlap(o, tbytes, k, kvbytes) ||
+      ranges_overlap(o, tbytes, v, kvbytes) || ranges_overlap(o, tbytes, lse, lbytes) ||
+      ranges_overlap(lse, lbytes, q, tbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+      ranges_overlap(lse, lbytes, v, kvbytes))
     return FA_ERR_ALIAS;
 
   fa::FwdParams p;
@@ -95,8 +96,14 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.d = d;
   p.causal = causal ? 1 : 0;
   p.scale = scale;
+  p.group = H / Hkv;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -114,17 +121,18 @@ fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q) {
   return FA_OK;
 }
 
-fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
-                   int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                       int H, int Hkv, int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
   if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   const int64_t elems = bh * N * d;
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  // The largest grid: one 256-thread workgroup per (query head, 128-row block).
   const int64_t nkb = ((int64_t)N + fa::bwd_block_k() - 1) / fa::bwd_block_k();
   if (bh * nkb * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
@@ -134,11 +142,12 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   const size_t need = fa::bwd_workspace_bytes((int)bh, N, d);
   if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   const size_t tb = (size_t)elems * 2;
+  const size_t kvb = (size_t)B * Hkv * N * d * 2;
   const size_t lb = (size_t)bh * N * sizeof(float);
   const void* ins[6] = {q, k, v, o, dout, lse};
-  const size_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  const size_t in_bytes[6] = {tb, kvb, kvb, tb, tb, lb};
   void* outs[4] = {dq, dk, dv, workspace};
-  const size_t out_bytes[4] = {tb, tb, tb, need};
+  const size_t out_bytes[4] = {tb, kvb, kvb, need};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 6; ++b)
       if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
@@ -162,7 +171,15 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.d = d;
   p.causal = causal ? 1 : 0;
   p.scale = scale;
+  p.group = H / Hkv;
   return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  return fa_bwd_gqa(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, d, causal, scale,
+                    dtype, stream);
 }
 
 fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, int* splits, int* chunk_keys,

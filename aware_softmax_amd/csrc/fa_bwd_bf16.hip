@@ -223,8 +223,8 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
                      const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
-                     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int BH, int N, int Npad, int nkb, float c,
-                     float scale) {
+                     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int BHkv, int N, int Npad, int nkb, float c,
+                     float scale, int group) {
   using Ly = DkdvLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -242,18 +242,17 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  int bh, jb;
-  map_block(blockIdx.x, BH * nkb, nkb, false, &bh, &jb);  // key block 0 (the most query tiles) first
+  // One workgroup per (key/value head, key block); it sums dK and dV over
+  // the `group` query heads that share the key/value head (consecutive
+  // query heads bhk * group .. bhk * group + group - 1).
+  int bhk, jb;
+  map_block(blockIdx.x, BHkv * nkb, nkb, false, &bhk, &jb);  // key block 0 (the most query tiles) first
   const int kb0 = jb * kBKV;
   const int kw0 = kb0 + 32 * wave;  // first key of this wave
   const int key = kw0 + col;        // this lane's key (MFMA column)
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = Qg + head;
+  const size_t head = (size_t)bhk * (size_t)N * D;
   const __bf16* Kh = Kg + head;
   const __bf16* Vh = Vg + head;
-  const __bf16* dOh = dOg + head;
-  const float* Lsh = Lsg + (size_t)bh * Npad;
-  const float* Dnh = Dng + (size_t)bh * Npad;
 
   // K and V fragments of the wave's keys: B operands of S = Q K^T and
   // dP = dO V^T (lane: key `col`, d = 16t + 8 half .. + 7).
@@ -267,19 +266,27 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
     }
   }
 
+  // Query tiles it0 .. nqt - 1 of each head of the group, streamed as one
+  // sequence v = r * span + (it - it0) (r: head within the group).
   const int nqt = Npad / kBQ;
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
-  auto ring = [&](int it) { return __builtin_amdgcn_readfirstlane((it - it0) % kRing); };
+  const int span = nqt - it0;
+  const int total = group * span;
+  auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % kRing); };
   constexpr int kDmaPerWave = 1 + 2 * (Ly::QTILE / 1024 / kWaves);  // statistics, Q, dO
-  auto dma_tile = [&](int it) {
-    const int b = ring(it);
+  auto dma_tile = [&](int v) {
+    const int b = ring(v);
+    const int r = __builtin_amdgcn_readfirstlane(v / span);
+    const int it = it0 + v - r * span;
+    const int bh = bhk * group + r;
+    const size_t qhead = (size_t)bh * (size_t)N * D;
     // the tile's 64 statistics: -L/scale by waves 0 and 2, -D by waves 1
     // and 3 (the duplicate copy writes the same bytes; it keeps the number
     // of DMA instructions per wave uniform for the waits)
-    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dnh : Lsh) + it * kBQ + lane),
+    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dng : Lsg) + (size_t)bh * Npad + it * kBQ + lane),
                                      (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + (wave & 1) * 4 * kBQ), 4, 0, 0);
-    dma_rows<D, kBQ>(Qh, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
-    dma_rows<D, kBQ>(dOh, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
+    dma_rows<D, kBQ>(Qg + qhead, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
+    dma_rows<D, kBQ>(dOg + qhead, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
   };
 
   // Lane-constant LDS byte offsets within a tile.
@@ -346,9 +353,9 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 
   // One tile: phase A, then phase B with the VALU groups of step u + 1
   // riding on the MFMAs of step u (groups 0 and 1 run before step 0).
-  auto iteration = [&](int it, auto mask_c) {
-    const int b = ring(it);
-    if (it + 2 < nqt) dma_tile(it + 2);
+  auto iteration = [&](int v, int it, auto mask_c) {
+    const int b = ring(v);
+    if (v + 2 < total) dma_tile(v + 2);
     const unsigned aq = sbase + Ly::OFF_Q + b * Ly::QTILE;
     const unsigned ado = sbase + Ly::OFF_DO + b * Ly::QTILE;
     {
@@ -428,8 +435,8 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    // tile it + 1 must be complete; the copies of tile it + 2 stay in flight
-    if (it + 2 < nqt)
+    // tile v + 1 must be complete; the copies of tile v + 2 stay in flight
+    if (v + 2 < total)
       dma_barrier<kDmaPerWave>();
     else
       dma_barrier<0>();
@@ -441,17 +448,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   int it_e = kb0 + kBKV <= N ? N / kBQ : 0;
   it_e = max(it_e, it_s);
 
-  dma_tile(it0);
-  if (it0 + 1 < nqt) {
-    dma_tile(it0 + 1);
+  dma_tile(0);
+  if (1 < total) {
+    dma_tile(1);
     dma_barrier<kDmaPerWave>();
   } else {
     dma_barrier<0>();
   }
-  int it = it0;
-  for (; it < it_s; ++it) iteration(it, std::true_type{});
-  for (; it < it_e; ++it) iteration(it, std::false_type{});
-  for (; it < nqt; ++it) iteration(it, std::true_type{});
+  for (int r = 0; r < group; ++r) {
+    int v = r * span;
+    int it = it0;
+    for (; it < it_s; ++it, ++v) iteration(v, it, std::true_type{});
+    for (; it < it_e; ++it, ++v) iteration(v, it, std::false_type{});
+    for (; it < nqt; ++it, ++v) iteration(v, it, std::true_type{});
+  }
 
   // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
   if (key < N) {
@@ -495,7 +505,7 @@ template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
                    const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
-                   __bf16* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale) {
+                   __bf16* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group) {
   using Ly = DqLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -519,9 +529,10 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
   const int qw = q0 + 32 * wave;
   const int qi = qw + col;  // this lane's query (MFMA column)
   const size_t head = (size_t)bh * (size_t)N * D;
+  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;  // key/value head of query head bh
   const __bf16* Qh = Qg + head;
-  const __bf16* Kh = Kg + head;
-  const __bf16* Vh = Vg + head;
+  const __bf16* Kh = Kg + kvhead;
+  const __bf16* Vh = Vg + kvhead;
   const __bf16* dOh = dOg + head;
 
   // Q and dO fragments of the wave's queries: B operands of S^T = K Q^T and
@@ -722,13 +733,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   }
   {
     const int nkb = (p.N + kBKV - 1) / kBKV;
-    const dim3 grid((unsigned)(p.BH * nkb)), block(kThreads);
+    const int bhkv = p.BH / p.group;
+    const dim3 grid((unsigned)(bhkv * nkb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
-                         (__bf16*)p.dv, p.BH, p.N, npad, nkb, c, p.scale);
+                         (__bf16*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
-                         (__bf16*)p.dv, p.BH, p.N, npad, nkb, c, p.scale);
+                         (__bf16*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -737,10 +749,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.BH * nqb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
-                         p.BH, p.N, npad, nqb, c, p.scale);
+                         p.BH, p.N, npad, nqb, c, p.scale, p.group);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
-                         p.BH, p.N, npad, nqb, c, p.scale);
+                         p.BH, p.N, npad, nqb, c, p.scale, p.group);
     return hipGetLastError();
   }
 }

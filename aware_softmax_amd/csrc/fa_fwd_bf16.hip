@@ -176,7 +176,8 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-    __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate) {
+    __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
+    int group) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;  // 16-wide d steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
@@ -193,8 +194,11 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
   const int q0 = qb * kBQ;
   const size_t head = (size_t)bh * (size_t)N * D;
   const __bf16* Qh = Qg + head;
-  const __bf16* Kh = Kg + head;
-  const __bf16* Vh = Vg + head;
+  // Query heads of a group are consecutive, so head bh reads key/value
+  // head bh / group.
+  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
+  const __bf16* Kh = Kg + kvhead;
+  const __bf16* Vh = Vg + kvhead;
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const int qw = q0 + wave * kRowsPerWave;  // first query row of this wave
@@ -539,7 +543,8 @@ struct Layout {
 template <int D, bool CAUSAL, bool FULL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate) {
+                __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
+    int group) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -561,8 +566,11 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   const int q0 = qb * kBQ;
   const size_t head = (size_t)bh * (size_t)N * D;
   const __bf16* Qh = Qg + head;
-  const __bf16* Kh = Kg + head;
-  const __bf16* Vh = Vg + head;
+  // Query heads of a group are consecutive, so head bh reads key/value
+  // head bh / group.
+  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
+  const __bf16* Kh = Kg + kvhead;
+  const __bf16* Vh = Vg + kvhead;
 
   // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
   // -inf * c stays -inf for hidden keys.
@@ -944,7 +952,8 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   __bf16* o = (__bf16*)p.o;
   float* lse = p.lse;
   int bh = p.BH, n = p.N;
-  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate};
+  int group = p.group;
+  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group};
   const void* fn;
   if constexpr (kDuo)
     fn = p.N % kBK == 0 ? (const void*)duo::fwd_kernel<D, CAUSAL, true> : (const void*)duo::fwd_kernel<D, CAUSAL, false>;

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
                                                           const float* __restrict__ Vg,
                                                           float* __restrict__ Og,
                                                           float* __restrict__ Lg, int BH, int N,
-                                                          int nqb, float c) {
+                                                          int nqb, float c, int group) {
   constexpr int KP = D + 4;       // padded K row (floats)
   constexpr int PP = kBK + 1;     // padded P row
   constexpr int DQ = D / 4;       // output columns per lane
@@ -46,8 +46,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const int qi = q0 + row;
   const size_t head = (size_t)bh * (size_t)N * D;
   const float* Qh = Qg + head;
-  const float* Kh = Kg + head;
-  const float* Vh = Vg + head;
+  // Query heads of a group are consecutive, so head bh reads key/value
+  // head bh / group.
+  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
+  const float* Kh = Kg + kvhead;
+  const float* Vh = Vg + kvhead;
 
   float qv[D];
 #pragma unroll
@@ -158,7 +161,8 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   float* o = (float*)p.o;
   float* lse = p.lse;
   int bh = p.BH, n = p.N;
-  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c};
+  int group = p.group;
+  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, &group};
   return hipLaunchKernel((const void*)fwd_f32_kernel<D, CAUSAL>, grid, block, args, 0, stream);
 }
 

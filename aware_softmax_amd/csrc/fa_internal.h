@@ -14,11 +14,12 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
-  int BH;       // B * H
+  int BH;       // B * H (query heads)
   int N;        // sequence length (queries = keys)
   int d;        // head dim
   int causal;   // nonzero: query i sees keys 0..i
   float scale;  // multiplies Q K^T
+  int group;    // query heads per key/value head (H / Hkv); k, v are [B][Hkv][N][d]
 };
 
 // Tile shape per (dtype, d).
@@ -43,11 +44,12 @@ struct BwdParams {
   void* dk;
   void* dv;
   void* workspace;  // bwd_workspace_bytes(BH, N, d) bytes
-  int BH;
+  int BH;           // B * H (query heads)
   int N;
   int d;
   int causal;
   float scale;
+  int group;        // query heads per key/value head; k, v, dk, dv are [B][H / group][N][d]
 };
 
 // Everything a split-K decode launch needs: q, o [B][H][d]; k, v

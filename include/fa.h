@@ -83,6 +83,20 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, int causal, float scale,
                    fa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * fa_fwd_gqa -- fa_fwd with grouped key/value heads: k and v are
+ * [B][Hkv][N][d] and query head h reads key/value head h / (H / Hkv)
+ * (Hkv = 1: one key/value head for all query heads; Hkv = H: fa_fwd).
+ * "FlashAttention: Move Less, Not Compute Less", "What It Changes--and
+ * What It Does Not": GQA cuts the number of key/value heads, and the
+ * reference implementation carries GQA/MQA paths next to the causal one;
+ * the sharing changes only which K and V tiles a workgroup streams.  q, o, lse and every other argument as for fa_fwd; H must be a
+ * multiple of Hkv (else FA_ERR_SHAPE).
+ */
+fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                       fa_dtype_t dtype, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(fa_status_t status);
 
@@ -137,6 +151,21 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float scale, fa_dtype_t dtype,
                    hipStream_t stream);
+
+/*
+ * fa_bwd_gqa -- fa_bwd with grouped key/value heads (the layouts of
+ * fa_fwd_gqa): k, v [in] and dk, dv [out] are [B][Hkv][N][d]; q, o, dout,
+ * dq are [B][H][N][d] and lse [B][H][N].  dK and dV of a key/value head
+ * are the sums over the H / Hkv query heads that read it (the chain rule
+ * through the shared K and V); they are summed on chip by the workgroup
+ * that owns the key block, so the result stays free of atomics and
+ * deterministic.  Every other argument as for fa_bwd; H must be a
+ * multiple of Hkv (else FA_ERR_SHAPE).
+ */
+fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale, fa_dtype_t dtype,
+                       hipStream_t stream);
 
 /*
  * fa_bwd_tile -- keys per workgroup of the dK/dV pass and queries per

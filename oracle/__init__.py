@@ -6,6 +6,8 @@ Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the
 from .attention import (  # noqa: F401
     attention_batched,
     attention_bwd,
+    attention_bwd_gqa,
+    attention_gqa,
     attention_from_scores,
     combine_partials,
     naive_attention,

@@ -18,7 +18,9 @@ Sources, cited by page title and section:
      "Tiling Is Easy; Softmax Couples the Entire Row" (stable softmax
      m, l; online recurrences m', l', o' and O = o / l),
      "Why More Arithmetic Can Finish Sooner" (the backward rebuilds S, P
-     from saved per-row statistics).
+     from saved per-row statistics),
+     "What It Changes--and What It Does Not" (GQA shrinks the number of
+     key/value heads; the reference implementation has GQA/MQA paths).
 [P3] "PidokuInfra 10 -- FlashAttention": section 1 (softmax(QK^T/sqrt(d))V,
      exact), section 4 "Tiny example -- the algorithm" (block loop with a
      causal per-row key bound, online update, normalise at the end),
@@ -33,7 +35,9 @@ Readings where the pages leave a step open:
   * "log" in L = m + log(l) is the natural logarithm, so L is the row
     logsumexp of the scaled, masked scores ([P1] change #1);
   * a row with no visible key (only possible when the caller passes
-    such a score matrix) has O = 0 and L = -inf.
+    such a score matrix) has O = 0 and L = -inf;
+  * grouped heads: of H query heads and Hkv key/value heads, query head h
+    uses key/value head h // (H // Hkv) (consecutive query heads share one).
 
 Parity pins live in ``tests/test_oracle.py``: closed forms, invariants,
 library cross-checks (torch's fp64 CPU attention, scipy's logsumexp),
@@ -54,6 +58,8 @@ __all__ = [
     "split_kv_partials",
     "combine_partials",
     "attention_batched",
+    "attention_gqa",
+    "attention_bwd_gqa",
 ]
 
 
@@ -267,3 +273,45 @@ def attention_batched(q, k, v, causal, scale, heads=None, rows=None):
         o_out[(b, h)] = o
         l_out[(b, h)] = lse
     return o_out, l_out
+
+
+def attention_gqa(q, k, v, causal, scale):
+    """Attention with grouped key/value heads for one batch entry.
+
+    [P2] "What It Changes--and What It Does Not": GQA keeps fewer key/value
+    heads than query heads; each query head computes ordinary attention
+    (``naive_attention``) against the K and V of its group, head
+    h // (H // Hkv).  q: (H, N, d); k, v: (Hkv, N, d) with H a multiple of
+    Hkv.  Returns (O (H, N, d), L (H, N)) in fp64.
+    """
+    n_h, n_kv = q.shape[0], k.shape[0]
+    group = n_h // n_kv
+    outs = [naive_attention(q[h], k[h // group], v[h // group], causal, scale) for h in range(n_h)]
+    return np.stack([o for o, _ in outs]), np.stack([l for _, l in outs])
+
+
+def attention_bwd_gqa(q, k, v, do, causal, scale):
+    """Gradients of ``attention_gqa`` for one batch entry, in fp64.
+
+    Each query head's dQ is that of its own attention (``attention_bwd``);
+    a key/value head enters the attention of every query head of its group,
+    so by the chain rule its dK and dV are the sums of those heads'
+    contributions.  Pinned against central finite differences through the
+    shared K, V and torch's fp64 autograd through repeated key/value heads.
+    Returns (dQ (H, N, d), dK (Hkv, N, d), dV (Hkv, N, d)).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    n_h, n_kv = q.shape[0], k.shape[0]
+    group = n_h // n_kv
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for h in range(n_h):
+        gq, gk, gv = attention_bwd(q[h], k[h // group], v[h // group], do[h], causal, scale)
+        dq[h] = gq
+        dk[h // group] += gk
+        dv[h // group] += gv
+    return dq, dk, dv

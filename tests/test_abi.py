@@ -36,7 +36,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version", "fa_bwd",
                      "fa_bwd_workspace_bytes", "fa_bwd_tile", "fa_decode", "fa_decode_plan",
-                     "fa_decode_workspace_bytes"):
+                     "fa_decode_workspace_bytes", "fa_fwd_gqa", "fa_bwd_gqa"):
         assert required in names
 
 
@@ -291,3 +291,34 @@ def test_decode_binding_rejects_bad_tensors(fa):
         fa.decode(q, k, k)
     with pytest.raises(TypeError):
         fa.decode(q.float(), k.float(), k.float())
+
+
+# ------------------------------------------------------------------ grouped heads
+
+@pytest.mark.parametrize("H,Hkv,code", [(3, 2, 2), (4, 0, 2), (4, -2, 2), (4, 8, 2)])
+def test_gqa_validation_rejects_before_launch(fa, H, Hkv, code):
+    g = dict(GOOD)
+    assert fa.fa_fwd_gqa(g["q"], g["k"], g["v"], g["o"], g["lse"], 1, H, Hkv, 64, 64, 1, 0.125, 1, None) == code
+    b = dict(BGOOD)
+    assert fa.fa_bwd_gqa(b["q"], b["k"], b["v"], b["o"], b["lse"], b["do"], b["dq"], b["dk"], b["dv"], b["ws"],
+                         b["ws_bytes"], 1, H, Hkv, 64, 64, 1, 0.125, 1, None) == code
+
+
+def test_gqa_alias_uses_kv_sizes(fa):
+    """With Hkv < H the key/value tensors are smaller: an output placed just
+    past the smaller k is no overlap, one inside it is."""
+    g = dict(GOOD)
+    kv_bytes = 1 * 1 * 64 * 64 * 2
+    assert fa.fa_fwd_gqa(g["q"], g["k"], g["v"], g["k"] + kv_bytes - 16, g["lse"], 1, 2, 1, 64, 64, 1,
+                         float("nan"), 1, None) == 6  # overlap not yet checked: scale fails first
+    assert fa.fa_fwd_gqa(g["q"], g["k"], g["v"], g["k"] + kv_bytes - 16, g["lse"], 1, 2, 1, 64, 64, 1, 0.125, 1,
+                         None) == 8
+
+
+def test_gqa_binding_rejects_bad_shapes(fa):
+    import torch
+
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k, k)

@@ -159,3 +159,51 @@ def test_outputs_untouched_outside_bounds(fa):
     for b in bufs:
         assert torch.all(b[size:] == 7.0)
         assert torch.isfinite(b[:size].float()).all()
+
+
+# ------------------------------------------------------------ grouped key/value heads
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 2, 333, 128), (1, 12, 4, 1000, 64), (1, 6, 1, 257, 128),
+                                   (1, 8, 2, 2048, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward(fa, shape, causal):
+    """fa_bwd_gqa: dK, dV of a key/value head sum over the query heads of
+    its group (oracle.attention_bwd_gqa), dQ per query head."""
+    import torch
+
+    B, H, Hkv, N, d = shape
+    cid = 6950 + H * 8 + Hkv + (d == 128)
+    st = {"q": synthetic.full_storage(cid, "q", B, H, N, d, "bf16"),
+          "do": synthetic.full_storage(cid, "do", B, H, N, d, "bf16"),
+          "k": synthetic.full_storage(cid, "k", B, Hkv, N, d, "bf16"),
+          "v": synthetic.full_storage(cid, "v", B, Hkv, N, d, "bf16")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert dk.shape == k.shape and dv.shape == v.shape
+    for b in range(B):
+        vals = [synthetic.bf16_bits_to_f32(st[t][b]) for t in ("q", "k", "v", "do")]
+        ref = oracle.attention_bwd_gqa(*vals, causal, scale)
+        for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            for h in range(r.shape[0]):
+                assert_grad_close(f"{name}[{b},{h}]", got[b, h].float().cpu().numpy().astype(np.float64), r[h])
+
+
+def test_gqa_backward_deterministic(fa):
+    import torch
+
+    B, H, Hkv, N, d = 1, 8, 2, 700, 128
+    st = {"q": synthetic.full_storage(6990, "q", B, H, N, d, "bf16"),
+          "do": synthetic.full_storage(6990, "do", B, H, N, d, "bf16"),
+          "k": synthetic.full_storage(6990, "k", B, Hkv, N, d, "bf16"),
+          "v": synthetic.full_storage(6990, "v", B, Hkv, N, d, "bf16")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -317,6 +317,78 @@ def test_bwd_invariants(causal):
     assert np.max(np.abs(dk.sum(axis=0))) < 1e-13
 
 
+# ---------------------------------------------------------------- grouped heads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_torch_repeated_heads(causal):
+    """Library cross-check: torch fp64 SDPA with each key/value head
+    repeated for its group (repeat_interleave), forward and autograd (which
+    sums the gradient of a repeated tensor over its copies)."""
+    H, Hkv, n, d = 6, 2, 13, 8
+    q = rnd(600, (H, n, d))
+    k = rnd(601, (Hkv, n, d))
+    v = rnd(602, (Hkv, n, d))
+    do = rnd(603, (H, n, d))
+    scale = 0.45
+    o, lse = oracle.attention_gqa(q, k, v, causal, scale)
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, causal, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    rk = tk.repeat_interleave(H // Hkv, dim=0)
+    rv = tv.repeat_interleave(H // Hkv, dim=0)
+    out = torch.nn.functional.scaled_dot_product_attention(tq[None], rk[None], rv[None], is_causal=causal,
+                                                           scale=scale)[0]
+    assert np.max(np.abs(o - out.detach().numpy())) < 1e-12
+    s = scale * torch.einsum("hnd,hmd->hnm", tq.detach(), rk.detach())
+    if causal:
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+    out.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) < 1e-12
+
+
+def test_gqa_finite_differences():
+    """Central differences of f = sum_h <O_h, dO_h> through the shared K and
+    V (H = 4 query heads on Hkv = 2 key/value heads, N = 9, d = 4)."""
+    H, Hkv, n, d = 4, 2, 9, 4
+    q = rnd(610, (H, n, d))
+    k = rnd(611, (Hkv, n, d))
+    v = rnd(612, (Hkv, n, d))
+    do = rnd(613, (H, n, d))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, True, scale)
+
+    def f(qq, kk, vv):
+        o, _ = oracle.attention_gqa(qq, kk, vv, True, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            fp = f(*args)
+            args[which][idx] -= 2 * h
+            fm = f(*args)
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - grad)) < 1e-7
+
+
+def test_gqa_one_group_is_multi_head():
+    """Hkv = H: every query head has its own key/value head."""
+    H, n, d = 3, 11, 8
+    q, k, v, do = (rnd(620 + i, (H, n, d)) for i in range(4))
+    o, lse = oracle.attention_gqa(q, k, v, True, 0.5)
+    dq, dk, dv = oracle.attention_bwd_gqa(q, k, v, do, True, 0.5)
+    for h in range(H):
+        ro, rl = oracle.naive_attention(q[h], k[h], v[h], True, 0.5)
+        assert np.array_equal(o[h], ro) and np.array_equal(lse[h], rl)
+        for a, b in zip((dq[h], dk[h], dv[h]), oracle.attention_bwd(q[h], k[h], v[h], do[h], True, 0.5)):
+            assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 

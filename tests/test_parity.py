@@ -248,3 +248,55 @@ def test_key_magnitude_ramp_d128(fa, causal):
     kv = synthetic.bf16_bits_to_f32(st["k"]) * (1.0 + np.arange(n, dtype=np.float32) / 16.0)[None, None, :, None]
     st["k"] = synthetic.bf16_round_bits(kv)
     assert_close(run_case(fa, 0, 1, 2, n, d, "bf16", causal, tensors=st), "bf16")
+
+
+# ------------------------------------------------------------ grouped key/value heads
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 2, 333, 128), (1, 12, 4, 1000, 64), (2, 6, 1, 129, 96),
+                                   (2, 4, 2, 65, 256), (1, 16, 2, 4096, 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_bf16(fa, shape, causal):
+    """fa_fwd_gqa: query head h reads key/value head h // (H // Hkv);
+    compared with oracle.attention_gqa on every head (sampled rows at
+    N = 4096)."""
+    import torch
+
+    B, H, Hkv, N, d = shape
+    cid = 1700 + H * 16 + Hkv + d
+    st = {"q": synthetic.full_storage(cid, "q", B, H, N, d, "bf16"),
+          "k": synthetic.full_storage(cid, "k", B, Hkv, N, d, "bf16"),
+          "v": synthetic.full_storage(cid, "v", B, Hkv, N, d, "bf16")}
+    q, k, v = (to_device(st[t], "bf16") for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    rows = synthetic.sample_rows(cid, N, 256) if N > 2000 else slice(None)
+    for b in range(B):
+        vals = [values(st[t][b], "bf16") for t in ("q", "k", "v")]
+        if N > 2000:
+            g = H // Hkv
+            ref = [oracle.naive_attention(vals[0][h], vals[1][h // g], vals[2][h // g], causal, 1 / math.sqrt(d),
+                                          rows=rows) for h in range(H)]
+            ref_o = np.stack([r[0] for r in ref])
+            ref_l = np.stack([r[1] for r in ref])
+        else:
+            ref_o, ref_l = oracle.attention_gqa(*vals, causal, 1 / math.sqrt(d))
+        got_o = o[b].float().cpu().numpy()[:, rows]
+        got_l = lse[b].cpu().numpy()[:, rows]
+        assert_close((float(np.max(np.abs(got_o - ref_o))), float(np.max(np.abs(got_l - ref_l)))), "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_forward_fp32(fa, causal):
+    import torch
+
+    B, H, Hkv, N, d = 1, 6, 3, 200, 64
+    st = {"q": synthetic.full_storage(1750, "q", B, H, N, d, "f32"),
+          "k": synthetic.full_storage(1750, "k", B, Hkv, N, d, "f32"),
+          "v": synthetic.full_storage(1750, "v", B, Hkv, N, d, "f32")}
+    q, k, v = (to_device(st[t], "f32") for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention_gqa(st["q"][0], st["k"][0], st["v"][0], causal, 1 / math.sqrt(d))
+    assert_close((float(np.max(np.abs(o[0].cpu().numpy() - ref_o))),
+                  float(np.max(np.abs(lse[0].cpu().numpy() - ref_l)))), "f32")
