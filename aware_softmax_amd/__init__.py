@@ -32,12 +32,14 @@ __all__ = [
     "LIB_PATH",
     "DTYPE_F32",
     "DTYPE_BF16",
+    "DTYPE_F16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 FA_OK = 0
 
 
@@ -128,7 +130,7 @@ def fa_fwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, causal, sca
 
 
 def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, stream=None):
-    """O, L = attention forward of [B, H, N, d] device tensors (bf16 or fp32).
+    """O, L = attention forward of [B, H, N, d] device tensors (bf16, fp16 or fp32).
 
     k and v may have fewer heads, [B, Hkv, N, d] with H a multiple of Hkv
     (grouped heads: query head h reads key/value head h // (H // Hkv)).
@@ -138,12 +140,10 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     """
     import torch
 
-    if q.dtype == torch.bfloat16:
-        dtype = DTYPE_BF16
-    elif q.dtype == torch.float32:
-        dtype = DTYPE_F32
-    else:
-        raise TypeError(f"unsupported dtype {q.dtype}; use torch.bfloat16 or torch.float32")
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16, torch.float32: DTYPE_F32}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype}; use torch.bfloat16, torch.float16 or torch.float32")
+    dtype = dtypes[q.dtype]
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
     B, H, N, d = q.shape

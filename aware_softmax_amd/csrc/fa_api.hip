@@ -17,12 +17,14 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 // A launch's work-items in x must fit in 32 bits.
 constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
-size_t elem_size(fa_dtype_t dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
+size_t elem_size(fa_dtype_t dtype) { return dtype == FA_DTYPE_F32 ? 4 : 2; }
 
-// Head dims of the forward: bf16 32, 64, 96, 128, 256; fp32 32, 64, 96, 128.
+bool is_16bit(fa_dtype_t dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16; }
+
+// Head dims of the forward: 16-bit 32, 64, 96, 128, 256; fp32 32, 64, 96, 128.
 fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
-  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  const bool ok = d == 32 || d == 64 || d == 96 || d == 128 || (d == 256 && dtype == FA_DTYPE_BF16);
+  if (dtype != FA_DTYPE_F32 && !is_16bit(dtype)) return FA_ERR_DTYPE;
+  const bool ok = d == 32 || d == 64 || d == 96 || d == 128 || (d == 256 && is_16bit(dtype));
   return ok ? FA_OK : FA_ERR_UNSUPPORTED_HEADDIM;
 }
 
@@ -35,7 +37,7 @@ const char* fa_status_string(fa_status_t status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: sizes must be positive, consistent and within the supported range";
-    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype is not supported by this entry point";
     case FA_ERR_UNSUPPORTED_HEADDIM: return "FA_ERR_UNSUPPORTED_HEADDIM: this entry point and dtype do not support this head dim";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: q/k/v/o must be 16-byte and lse 4-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite";
@@ -52,7 +54,7 @@ fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int
   if (!block_q || !block_k || !waves) return FA_ERR_NULL;
   const fa_status_t st = check_dtype_headdim(d, dtype);
   if (st != FA_OK) return st;
-  const fa::TileConfig t = dtype == FA_DTYPE_BF16 ? fa::bf16_tile(d) : fa::f32_tile(d);
+  const fa::TileConfig t = is_16bit(dtype) ? fa::mfma_tile(d) : fa::f32_tile(d);
   *block_q = t.block_q;
   *block_k = t.block_k;
   *waves = t.waves;
@@ -70,7 +72,7 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   const int64_t elems = bh * N * d;
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
-  const fa::TileConfig tile = dtype == FA_DTYPE_BF16 ? fa::bf16_tile(d) : fa::f32_tile(d);
+  const fa::TileConfig tile = is_16bit(dtype) ? fa::mfma_tile(d) : fa::f32_tile(d);
   const int64_t nqb = ((int64_t)N + tile.block_q - 1) / tile.block_q;
   if (bh * nqb * 64 * tile.waves > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
@@ -97,7 +99,9 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.group = H / Hkv;
-  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f32(p, stream);
+  const hipError_t e = dtype == FA_DTYPE_BF16  ? fa::launch_fwd_bf16(p, stream)
+                       : dtype == FA_DTYPE_F16 ? fa::launch_fwd_f16(p, stream)
+                                               : fa::launch_fwd_f32(p, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

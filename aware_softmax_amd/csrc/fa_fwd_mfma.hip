@@ -1,4 +1,6 @@
-// FlashAttention-2 forward, bfloat16 in/out, fp32 softmax state, gfx950 MFMA.
+// FlashAttention-2 forward, bfloat16 or float16 in/out, fp32 softmax state,
+// gfx950 MFMA (v_mfma_f32_32x32x16_bf16 / _f16; the element type is a
+// template parameter, everything else is shared).
 //
 // What is computed (per batch*head, per query row i):
 //   O_i = sum_j softmax_j(scale * q_i . k_j + mask_ij) v_j,  L_i = logsumexp_j(...)
@@ -48,14 +50,42 @@
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+template <class T>
+using vec8 = T __attribute__((ext_vector_type(8)));
+template <class T>
+using vec4 = T __attribute__((ext_vector_type(4)));
+template <class T>
+using vec2 = T __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The two 16-bit element types: MFMA, the fp32 pair -> element pair
+// conversion (round to nearest even) and the dot product of a pair with an
+// fp32 accumulate.
+__device__ __forceinline__ f32x16 mfma32(const vec8<__bf16>& a, const vec8<__bf16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const vec8<_Float16>& a, const vec8<_Float16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float dot2(vec2<__bf16> a, vec2<__bf16> b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+__device__ __forceinline__ float dot2(vec2<_Float16> a, vec2<_Float16> b, float c) {
+  return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+template <class T>
+__device__ __forceinline__ vec2<T> cvt2(float a, float b) {
+  return __builtin_convertvector((f32x2){a, b}, vec2<T>);
+}
+template <class T>
+__device__ __forceinline__ vec2<T> one2() {
+  return vec2<T>{(T)1.0f, (T)1.0f};
+}
 
 constexpr int kBQ = 128;  // query rows per workgroup
 constexpr int kBK = 64;   // keys per streamed tile
@@ -84,19 +114,17 @@ __device__ inline float swap_halves(float x, bool want_max) {
   return want_max ? fmaxf(a, b) : a + b;
 }
 
-__device__ inline bf16x8 read_vt(const __bf16* p0, const __bf16* p1) {
+template <class T>
+__device__ inline vec8<T> read_vt(const T* p0, const T* p1) {
   // Two transposing 8-byte LDS reads -> the 8 bf16 of one MFMA A operand.
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
   s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(vec8<T>, v);
 }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Raw LDS addressing: 32-bit byte addresses kept in VGPRs, so each operand
 // read is one ds_read with a compile-time immediate offset.
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 __device__ inline unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
@@ -116,9 +144,9 @@ __device__ constexpr int score_key_offset(int i) { return (i >> 4) * 32 + ((i >>
 //   MASK: the tile crosses the causal diagonal or the end of the sequence;
 //   scores with key offset > lim_causal (causal) or >= lim_n are excluded.
 //   Unmasked tiles run no per-score compare or select at all.
-template <bool MASK, bool CAUSAL>
+template <bool MASK, bool CAUSAL, class T>
 __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, int lim_n, float& m_run,
-                                     float& l_part, bf16x8 (&pfrag)[4]) {
+                                     float& l_part, vec8<T> (&pfrag)[4]) {
   if (MASK) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -146,7 +174,7 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
   m_run = m_new;
   float lsum = l_part * alpha;
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const vec2<T> one = one2<T>();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     unsigned w[4];
@@ -159,12 +187,12 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
         p0 = (x0 == -INFINITY) ? 0.f : p0;
         p1 = (x1 == -INFINITY) ? 0.f : p1;
       }
-      const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+      const vec2<T> pr = cvt2<T>(p0, p1);
       // Row sum of exactly the bf16 probabilities the P.V product uses.
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
+      lsum = dot2(pr, one, lsum);
       w[e >> 1] = __builtin_bit_cast(unsigned, pr);
     }
-    pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+    pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
   }
   l_part = lsum;
   return alpha;
@@ -173,15 +201,15 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
 // Any d that is a multiple of 32 (one 32-wide output block per step); two
 // workgroups per CU up to d = 128, one at d = 256 (O^T alone is 128 fp32
 // per lane there, and two K/V stages take 137 KB of LDS).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
-    const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-    __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
+    const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+    T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;  // 16-wide d steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * Ly::STAGE];
+  __shared__ __attribute__((aligned(16))) T smem[2 * Ly::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,30 +221,30 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
   const int q0 = qb * kBQ;
   const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = Qg + head;
+  const T* Qh = Qg + head;
   // Query heads of a group are consecutive, so head bh reads key/value
   // head bh / group.
   const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
-  const __bf16* Kh = Kg + kvhead;
-  const __bf16* Vh = Vg + kvhead;
+  const T* Kh = Kg + kvhead;
+  const T* Vh = Vg + kvhead;
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const int qw = q0 + wave * kRowsPerWave;  // first query row of this wave
   const int qi = qw + col;                  // this lane's query row
-  bf16x8 qf[DT];
+  vec8<T> qf[DT];
   if (qi < N) {
-    const bf16x8* src = (const bf16x8*)(Qh + (size_t)qi * D + half * 8);
+    const vec8<T>* src = (const vec8<T>*)(Qh + (size_t)qi * D + half * 8);
 #pragma unroll
     for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
   } else {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) qf[t] = bf16x8{};
+    for (int t = 0; t < DT; ++t) qf[t] = vec8<T>{};
   }
   if (negate) {  // scale < 0: use -Q and |scale| (negation is exact)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4 u = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
-      qf[t] = __builtin_bit_cast(bf16x8, u);
+      qf[t] = __builtin_bit_cast(vec8<T>, u);
     }
   }
 
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
   float l_part = 0.f;
 
   // ---- global -> register prefetch, register -> LDS store
-  bf16x8 kreg[Ly::CHUNKS_PER_THREAD], vreg[Ly::CHUNKS_PER_THREAD];
+  vec8<T> kreg[Ly::CHUNKS_PER_THREAD], vreg[Ly::CHUNKS_PER_THREAD];
   auto gload = [&](int j) {
     const int kt0 = j * kBK;
 #pragma unroll
@@ -242,24 +270,24 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
       const int key = kt0 + row;
       if (key < N) {
         const size_t off = (size_t)key * D + c8 * 8;
-        kreg[i] = *(const bf16x8*)(Kh + off);
-        vreg[i] = *(const bf16x8*)(Vh + off);
+        kreg[i] = *(const vec8<T>*)(Kh + off);
+        vreg[i] = *(const vec8<T>*)(Vh + off);
       } else {
-        kreg[i] = bf16x8{};
-        vreg[i] = bf16x8{};
+        kreg[i] = vec8<T>{};
+        vreg[i] = vec8<T>{};
       }
     }
   };
   auto lstore = [&](int buf) {
-    __bf16* Kl = smem + buf * Ly::STAGE;
-    __bf16* Vl = Kl + Ly::K_ELEMS;
+    T* Kl = smem + buf * Ly::STAGE;
+    T* Vl = Kl + Ly::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < Ly::CHUNKS_PER_THREAD; ++i) {
       const int ci = tid + kThreads * i;
       const int row = ci / Ly::CHUNKS_PER_ROW;
       const int c8 = ci % Ly::CHUNKS_PER_ROW;
-      *(bf16x8*)(Kl + row * Ly::KS + c8 * 8) = kreg[i];
-      *(bf16x8*)(Vl + row * Ly::VS + c8 * 8) = vreg[i];
+      *(vec8<T>*)(Kl + row * Ly::KS + c8 * 8) = kreg[i];
+      *(vec8<T>*)(Vl + row * Ly::VS + c8 * 8) = vreg[i];
     }
   };
 
@@ -280,19 +308,19 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
     const int kt0 = j * kBK;
     const bool skip = CAUSAL && kt0 > qw + kRowsPerWave - 1;
     if (!skip) {
-      const __bf16* Kl = smem + buf * Ly::STAGE;
-      const __bf16* Vl = Kl + Ly::K_ELEMS;
+      const T* Kl = smem + buf * Ly::STAGE;
+      const T* Vl = Kl + Ly::K_ELEMS;
 
       // S^T[key][query] for two 32-key halves of the tile.
       f32x16 s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
-        const __bf16* krow = Kl + (kb * 32 + col) * Ly::KS + half * 8;
+        const T* krow = Kl + (kb * 32 + col) * Ly::KS + half * 8;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const bf16x8 kf = *(const bf16x8*)(krow + t * 16);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
+          const vec8<T> kf = *(const vec8<T>*)(krow + t * 16);
+          s[kb] = mfma32(kf, qf[t], s[kb]);
         }
       }
 
@@ -307,7 +335,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
       const bool need_mask = (CAUSAL && kt0 + kBK - 1 > qw) || (kt0 + kBK > N);
       const int lim_causal = qi - kt0 - half * 4;
       const int lim_n = N - kt0 - half * 4;
-      bf16x8 pfrag[4];
+      vec8<T> pfrag[4];
       const float alpha = need_mask
                               ? tile_softmax<true, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag)
                               : tile_softmax<false, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag);
@@ -319,12 +347,12 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
       // O^T += V^T P^T, four 16-key steps.
 #pragma unroll
       for (int u = 0; u < kBK / 16; ++u) {
-        const bf16x8 pf = pfrag[u];
-        const __bf16* vrow = Vl + (u * 16 + half * 4 + tr_e) * Ly::VS + tr_cg * 16 + 4 * tr_t;
+        const vec8<T> pf = pfrag[u];
+        const T* vrow = Vl + (u * 16 + half * 4 + tr_e) * Ly::VS + tr_cg * 16 + 4 * tr_t;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
-          const bf16x8 vf = read_vt(vrow + b * 32, vrow + b * 32 + 8 * Ly::VS);
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[b], 0, 0, 0);
+          const vec8<T> vf = read_vt(vrow + b * 32, vrow + b * 32 + 8 * Ly::VS);
+          oacc[b] = mfma32(vf, pf, oacc[b]);
         }
       }
     }
@@ -336,15 +364,15 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_bf16_kernel(
   const float l_tot = swap_halves(l_part, false);
   if (qi < N) {
     const float inv = 1.f / l_tot;
-    __bf16* orow = Og + head + (size_t)qi * D + half * 4;
+    T* orow = Og + head + (size_t)qi * D + half * 4;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 out;
+        vec4<T> out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (__bf16)(oacc[b][g * 4 + e] * inv);
-        *(bf16x4*)(orow + b * 32 + g * 8) = out;
+        for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[b][g * 4 + e] * inv);
+        *(vec4<T>*)(orow + b * 32 + g * 8) = out;
       }
     if (half == 0) Lg[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
@@ -374,8 +402,8 @@ __device__ __forceinline__ void read_v(s16x4& lo, s16x4& hi, unsigned addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(addr), "i"(OFF_LO));
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(addr), "i"(OFF_HI));
 }
-template <int OFF>
-__device__ __forceinline__ void read_k(bf16x8& f, unsigned addr) {
+template <int OFF, class T>
+__device__ __forceinline__ void read_k(vec8<T>& f, unsigned addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
 
@@ -396,16 +424,16 @@ struct FastSoftmax {
   unsigned w[16];
 };
 
-template <int K>
+template <class T, int K>
 __device__ __forceinline__ void fast_slot(FastSoftmax& st, const f32x16 (&s)[2], float c, float m) {
   auto sv = [&](int i) { return s[i >> 4][i & 15]; };
   constexpr int r = K / 2;
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const vec2<T> one = one2<T>();
   if constexpr (K % 2 == 0) {
     if constexpr (r >= 1) {
       constexpr int q = r - 1;
-      const bf16x2 pr = __builtin_convertvector((f32x2){st.p[0], st.p[1]}, bf16x2);
-      st.ps[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, q < 4 ? 0.f : st.ps[q & 3], false);
+      const vec2<T> pr = cvt2<T>(st.p[0], st.p[1]);
+      st.ps[q & 3] = dot2(pr, one, q < 4 ? 0.f : st.ps[q & 3]);
       st.w[q] = __builtin_bit_cast(unsigned, pr);
       asm volatile("" ::"v"(st.w[q]), "v"(st.ps[q & 3]));
     }
@@ -420,14 +448,15 @@ __device__ __forceinline__ void fast_slot(FastSoftmax& st, const f32x16 (&s)[2],
 }
 
 // Packs pair 15 and returns the lane's partial row sum of the tile.
-__device__ __forceinline__ float fast_finish(FastSoftmax& st, bf16x8 (&pfrag)[4]) {
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  const bf16x2 pr = __builtin_convertvector((f32x2){st.p[0], st.p[1]}, bf16x2);
-  st.ps[3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.ps[3], false);
+template <class T>
+__device__ __forceinline__ float fast_finish(FastSoftmax& st, vec8<T> (&pfrag)[4]) {
+  const vec2<T> one = one2<T>();
+  const vec2<T> pr = cvt2<T>(st.p[0], st.p[1]);
+  st.ps[3] = dot2(pr, one, st.ps[3]);
   st.w[15] = __builtin_bit_cast(unsigned, pr);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){st.w[4 * u], st.w[4 * u + 1], st.w[4 * u + 2], st.w[4 * u + 3]});
+    pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){st.w[4 * u], st.w[4 * u + 1], st.w[4 * u + 2], st.w[4 * u + 3]});
   return (st.ps[0] + st.ps[1]) + (st.ps[2] + st.ps[3]);
 }
 
@@ -441,8 +470,9 @@ constexpr float kFastBudget = 65536.f;
 // lim; hidden scores become -inf through a sign-mask bit select (integer
 // ALU only, so no per-score lane masks occupy scalar registers).  With c > 0,
 // 2^(-inf) = 0 drops them from P; a row with no visible key keeps its state.
+template <class T>
 __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim, float& m_run, float& l_part,
-                                               bf16x8 (&pfrag)[4]) {
+                                               vec8<T> (&pfrag)[4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -458,7 +488,7 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
   if (raise) m_run = m_tile;
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const vec2<T> one = one2<T>();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     unsigned w[4];
@@ -467,11 +497,11 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
       const int i = u * 8 + e;
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 4][i & 15], c, -m_use));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m_use));
-      const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-      ps[e >> 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[e >> 1], false);
+      const vec2<T> pr = cvt2<T>(p0, p1);
+      ps[e >> 1] = dot2(pr, one, ps[e >> 1]);
       w[e >> 1] = __builtin_bit_cast(unsigned, pr);
     }
-    pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+    pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
   }
   l_part = l_part * alpha + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
   return alpha;
@@ -540,10 +570,10 @@ struct Layout {
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
 };
 
-template <int D, bool CAUSAL, bool FULL>
+template <class T, int D, bool CAUSAL, bool FULL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
+void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+                T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;
@@ -553,7 +583,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   constexpr int NK = 2 * DT;
   constexpr int IPW = Ly::INSTR_PER_WAVE;
   static_assert(NV == 16 && NK == 16, "32 MFMA slots per iteration");
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[Ly::TOTAL];
+  __shared__ __attribute__((aligned(1024))) T smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -565,12 +595,12 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
   const int q0 = qb * kBQ;
   const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = Qg + head;
+  const T* Qh = Qg + head;
   // Query heads of a group are consecutive, so head bh reads key/value
   // head bh / group.
   const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
-  const __bf16* Kh = Kg + kvhead;
-  const __bf16* Vh = Vg + kvhead;
+  const T* Kh = Kg + kvhead;
+  const T* Vh = Vg + kvhead;
 
   // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
   // -inf * c stays -inf for hidden keys.
@@ -580,20 +610,20 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // numbers of visible tiles differ by at most one).
   const int qw = q0 + (wave & 3) * 64 + (wave >> 2) * 32;
   const int qi = qw + col;
-  bf16x8 qf[DT];
+  vec8<T> qf[DT];
   if (qi < N) {
-    const bf16x8* src = (const bf16x8*)(Qh + (size_t)qi * D + half * 8);
+    const vec8<T>* src = (const vec8<T>*)(Qh + (size_t)qi * D + half * 8);
 #pragma unroll
     for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
   } else {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) qf[t] = bf16x8{};
+    for (int t = 0; t < DT; ++t) qf[t] = vec8<T>{};
   }
   if (negate) {  // scale < 0: use -Q and |scale| (negation is exact)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4 u = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
-      qf[t] = __builtin_bit_cast(bf16x8, u);
+      qf[t] = __builtin_bit_cast(vec8<T>, u);
     }
   }
 
@@ -610,9 +640,9 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
   f32x16 sacc[2];
   sacc[0] = sacc[1] = f32x16{};
-  bf16x8 pfrag[4];
+  vec8<T> pfrag[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) pfrag[u] = bf16x8{};
+  for (int u = 0; u < 4; ++u) pfrag[u] = vec8<T>{};
   float m_run = -INFINITY;
   float l_part = 0.f;
 
@@ -627,7 +657,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (row % CPR)) * 16));
     dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (2 * (row & 3))) * 16));
   }
-  auto dma_one = [&](const __bf16* Xh, int buf, int t, int i, auto is_v) {
+  auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
     const int kt0 = t * kBK;
     const char* src = (const char*)(Xh + (size_t)kt0 * D);
@@ -646,7 +676,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   // DMA of tile t into a ring slot given as an element offset (general
   // path) or as integral_constant<int, slot> of the K (is_v false) or V
   // ring.
-  auto dma_any = [&](const __bf16* Xh, auto buf, int t, int i, auto is_v) {
+  auto dma_any = [&](const T* Xh, auto buf, int t, int i, auto is_v) {
     if constexpr (std::is_integral_v<decltype(buf)>) {
       dma_one(Xh, buf, t, i, is_v);
     } else {
@@ -701,7 +731,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     constexpr bool CT = !std::is_integral_v<decltype(kb)>;
     unsigned base = 0;  // byte offset of the slot from slot 0
     if constexpr (!CT) base = buf_rel(kb - Ly::K0);
-    bf16x8 fr[kLead];
+    vec8<T> fr[kLead];
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
       if constexpr (CT)
@@ -715,11 +745,11 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
       constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fr[F % kLead]) : "i"(last - F));
       if constexpr (F < 2)
-        dst[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], f32x16{}, 0, 0, 0);
+        dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], f32x16{});
       else
-        dst[F % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[F % kLead], qf[F / 2], dst[F % 2], 0, 0, 0);
+        dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], dst[F % 2]);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
+      if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_any(Vh, dma_b, dma_t, F / 8, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -752,11 +782,11 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
       constexpr int u = F / DB, b = F % DB;
       constexpr int last = (F + kLead - 1 < NV - 1) ? F + kLead - 1 : NV - 1;
       asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo[F % kLead]), "+v"(hi[F % kLead]) : "i"(2 * (last - F)));
-      const bf16x8 vf =
-          __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[F % kLead], hi[F % kLead], 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfrag[u], oacc[b], 0, 0, 0);
+      const vec8<T> vf =
+          __builtin_bit_cast(vec8<T>, __builtin_shufflevector(lo[F % kLead], hi[F % kLead], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[b] = mfma32(vf, pfrag[u], oacc[b]);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) fast_slot<S0 + F>(fs, sc, c, m_run);
+      if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_any(Kh, dma_b, dma_t, F / 8, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -810,7 +840,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float ps[2] = {0.f, 0.f};
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const vec2<T> one = one2<T>();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       unsigned w[4];
@@ -819,11 +849,11 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
         const int i = u * 8 + e;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i >> 4][i & 15], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[(i + 1) >> 4][(i + 1) & 15], c, -m_run));
-        const bf16x2 pr = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-        ps[e >> 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[e >> 2], false);
+        const vec2<T> pr = cvt2<T>(p0, p1);
+        ps[e >> 2] = dot2(pr, one, ps[e >> 2]);
         w[e >> 1] = __builtin_bit_cast(unsigned, pr);
       }
-      pfrag[u] = __builtin_bit_cast(bf16x8, (u32x4){w[0], w[1], w[2], w[3]});
+      pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
     }
     l_part = l_part * alpha + (ps[0] + ps[1]);
     rescale(alpha);
@@ -916,15 +946,15 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
   const float l_tot = swap_halves(l_part, false);
   if (qi < N) {
     const float inv = 1.f / l_tot;
-    __bf16* orow = Og + head + (size_t)qi * D + half * 4;
+    T* orow = Og + head + (size_t)qi * D + half * 4;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 out;
+        vec4<T> out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (__bf16)(oacc[b][g * 4 + e] * inv);
-        *(bf16x4*)(orow + b * 32 + g * 8) = out;
+        for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[b][g * 4 + e] * inv);
+        *(vec4<T>*)(orow + b * 32 + g * 8) = out;
       }
     if (half == 0) Lg[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
@@ -937,7 +967,7 @@ void fwd_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, co
 // copies), the 4-wave kernel for d = 32, 64, 96 and 256 (at d <= 96 the
 // 2d/16 + 2d/16 MFMAs per tile leave too few slots to hide the softmax of a
 // 64-key tile; at d = 256 two waves per SIMD do not fit the registers).
-template <int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr bool kDuo = D == 128;
   const int bq = kDuo ? duo::kBQ : kBQ;
@@ -946,37 +976,42 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const int negate = p.scale < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
   dim3 grid(p.BH * nqb), block(kDuo ? duo::kThreads : kThreads);
-  const __bf16* q = (const __bf16*)p.q;
-  const __bf16* k = (const __bf16*)p.k;
-  const __bf16* v = (const __bf16*)p.v;
-  __bf16* o = (__bf16*)p.o;
+  const T* q = (const T*)p.q;
+  const T* k = (const T*)p.k;
+  const T* v = (const T*)p.v;
+  T* o = (T*)p.o;
   float* lse = p.lse;
   int bh = p.BH, n = p.N;
   int group = p.group;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group};
   const void* fn;
   if constexpr (kDuo)
-    fn = p.N % kBK == 0 ? (const void*)duo::fwd_kernel<D, CAUSAL, true> : (const void*)duo::fwd_kernel<D, CAUSAL, false>;
+    fn = p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
+                        : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
   else
-    fn = (const void*)fwd_bf16_kernel<D, CAUSAL>;
+    fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+template <class T>
+hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return p.causal ? launch<T, 32, true>(p, stream) : launch<T, 32, false>(p, stream);
+    case 64: return p.causal ? launch<T, 64, true>(p, stream) : launch<T, 64, false>(p, stream);
+    case 96: return p.causal ? launch<T, 96, true>(p, stream) : launch<T, 96, false>(p, stream);
+    case 128: return p.causal ? launch<T, 128, true>(p, stream) : launch<T, 128, false>(p, stream);
+    case 256: return p.causal ? launch<T, 256, true>(p, stream) : launch<T, 256, false>(p, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-TileConfig bf16_tile(int d) {
+TileConfig mfma_tile(int d) {
   return d == 128 ? TileConfig{duo::kBQ, kBK, duo::kWaves} : TileConfig{kBQ, kBK, kWaves};
 }
 
-hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  switch (p.d) {
-    case 32: return p.causal ? launch<32, true>(p, stream) : launch<32, false>(p, stream);
-    case 64: return p.causal ? launch<64, true>(p, stream) : launch<64, false>(p, stream);
-    case 96: return p.causal ? launch<96, true>(p, stream) : launch<96, false>(p, stream);
-    case 128: return p.causal ? launch<128, true>(p, stream) : launch<128, false>(p, stream);
-    case 256: return p.causal ? launch<256, true>(p, stream) : launch<256, false>(p, stream);
-  }
-  return hipErrorInvalidValue;
-}
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) { return launch_t<__bf16>(p, stream); }
+hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream) { return launch_t<_Float16>(p, stream); }
 
 }  // namespace fa

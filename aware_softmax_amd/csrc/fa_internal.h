@@ -29,7 +29,7 @@ struct TileConfig {
   int waves;
 };
 
-TileConfig bf16_tile(int d);
+TileConfig mfma_tile(int d);  // the 16-bit (MFMA) forward, bf16 and fp16
 TileConfig f32_tile(int d);
 
 // Everything a backward launch needs (device pointers, layouts of fa.h).
@@ -88,6 +88,7 @@ int decode_rows_per_iter(int d, int heads_per_wg);
 // Launchers: enqueue the kernel(s) on `stream`; return the first
 // hipError_t a launch reported.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);

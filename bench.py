@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "aware_softmax_amd", "csrc", "fa_fwd_bf16.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "aware_softmax_amd", "csrc", "fa_fwd_mfma.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_B8H32N8192d128_counters.txt")
 METRIC = "causal bf16 attention fwd TFLOPS at N=8k,d=128; % of MI355X MFMA peak"
 
@@ -148,6 +148,55 @@ def time_backward(fa, w, q, k, v, o, lse, steps, warmup):
     f = 2.5 * attention_flops(w.B, w.H, w.N, w.d, w.causal)
     return {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2),
             "flops_per_call": f, "kernels": "bwd_pre + bwd_dkdv + bwd_dq"}
+
+
+def time_gqa(fa, steps=10, warmup=2):
+    """Grouped key/value heads: causal forward B8 H32 Hkv8 N8192 d128 and
+    forward + backward B2 H16 Hkv4 N4096 d128 (FLOPs as for H heads)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    out = {}
+    dev = torch.device("cuda:0")
+
+    def tens(cid, t, B, H, N, d):
+        st = synthetic.full_storage(cid, t, B, H, N, d, "bf16", threads=16)
+        return torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for (B, H, Hkv, N, d, with_bwd) in ((8, 32, 8, 8192, 128, False), (2, 16, 4, 4096, 128, True)):
+        q, do = tens(3, "q", B, H, N, d), tens(3, "do", B, H, N, d)
+        k, v = tens(3, "k", B, Hkv, N, d), tens(3, "v", B, Hkv, N, d)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        f = attention_flops(B, H, N, d, True)
+        label = f"causal bf16 B{B} H{H} Hkv{Hkv} N{N} d{d}"
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / steps
+
+        ms = timed(lambda: fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse))
+        out[f"{label} fwd"] = {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2)}
+        if with_bwd:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
+            ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+            ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale, dq=dq, dk=dk, dv=dv,
+                                      workspace=ws))
+            out[f"{label} bwd"] = {"ms": round(ms, 4), "TFLOP/s": round(2.5 * f / (ms * 1e-3) / 1e12, 2)}
+        del q, k, v, do, o, lse
+        torch.cuda.empty_cache()
+    return out
 
 
 def decode_inputs(w, threads=16):
@@ -357,6 +406,19 @@ def main():
             "causal_speedup_time_ratio": round(msk / ms_kernel, 3)}
         del qq, kk, vv, oo, ll
         torch.cuda.empty_cache()
+        # other head dims and grouped key/value heads (seeded like workload 3)
+        for d in (32, 64, 96, 256):
+            hw = synthetic.Workload(3, "", 8, 32, 8192, d, "bf16", True)
+            qq, kk, vv = make_inputs(hw)
+            oo = torch.empty_like(qq)
+            ll = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=qq.device)
+            ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, True, hw.scale, 10, 2)
+            f = attention_flops(hw.B, hw.H, hw.N, hw.d, True)
+            extra[f"causal bf16 fwd B8 H32 N8192 d{d}"] = {"ms": round(msk, 4),
+                                                           "TFLOP/s": round(f / (msk * 1e-3) / 1e12, 2)}
+            del qq, kk, vv, oo, ll
+            torch.cuda.empty_cache()
+        extra.update(time_gqa(fa))
         for cid in (6, 7, 8):
             dw = synthetic.DECODE_WORKLOADS[cid]
             dq_, dk_, dv_ = decode_inputs(dw)

@@ -44,7 +44,8 @@ extern "C" {
 
 typedef enum {
   FA_DTYPE_F32 = 0,  /* float32 in, float32 out, fp32 arithmetic */
-  FA_DTYPE_BF16 = 1  /* bfloat16 in/out, fp32 accumulation and softmax */
+  FA_DTYPE_BF16 = 1, /* bfloat16 in/out, fp32 accumulation and softmax */
+  FA_DTYPE_F16 = 2   /* float16 in/out, fp32 accumulation and softmax */
 } fa_dtype_t;
 
 typedef enum {
@@ -68,13 +69,14 @@ typedef enum {
  *                  overlap q, k, v or lse.
  *   lse      [out] device, [B][H][N] float32, 4-byte aligned.
  *   B, H, N  sizes (> 0); any N >= 1 (ragged tails are masked).
- *   d        head dimension: 32, 64, 96, 128 or 256 for bf16; 32, 64, 96
- *            or 128 for fp32 ("PidokuInfra 10 -- FlashAttention", section
- *            9: kernels commonly cover 64, 96, 128 and 256).
+ *   d        head dimension: 32, 64, 96, 128 or 256 for bf16 and fp16;
+ *            32, 64, 96 or 128 for fp32 ("PidokuInfra 10 -- FlashAttention",
+ *            section 9: kernels commonly cover 64, 96, 128 and 256).
  *   causal   0: every query sees all N keys; nonzero: query i sees 0..i.
  *   scale    multiplies Q K^T before mask and softmax (finite; 1/sqrt(d)
  *            in the usual case; 0 and negative values are allowed).
- *   dtype    FA_DTYPE_BF16 (MFMA path) or FA_DTYPE_F32 (fp32 path).
+ *   dtype    FA_DTYPE_BF16 or FA_DTYPE_F16 (MFMA path; P is rounded to the
+ *            input type for the P.V product) or FA_DTYPE_F32 (fp32 path).
  *   stream   HIP stream the kernel is enqueued on.
  * Returns FA_OK or the first failed check (see fa_status_t).  The output
  * is deterministic: the same inputs give bitwise identical o and lse.

@@ -44,7 +44,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     causal: bool
 
     @property
@@ -112,25 +112,29 @@ def head_stream(config_id: int, tensor: str, b: int, h: int) -> np.random.Genera
 
 
 def head_values(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dtype: str) -> np.ndarray:
-    """One head's (n, d) tensor as fp32 values (bf16-representable if dtype is bf16)."""
+    """One head's (n, d) tensor as fp32 values (representable in the dtype)."""
     x = head_stream(config_id, tensor, b, h).standard_normal((n, d), dtype=np.float32)
     if dtype == "bf16":
         return bf16_bits_to_f32(bf16_round_bits(x))
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)  # IEEE round to nearest even
     return x
 
 
 def head_storage(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dtype: str) -> np.ndarray:
-    """One head's (n, d) tensor in storage form: uint16 bf16 bits or float32."""
+    """One head's (n, d) tensor in storage form: uint16 bf16 bits, float16 or float32."""
     x = head_stream(config_id, tensor, b, h).standard_normal((n, d), dtype=np.float32)
     if dtype == "bf16":
         return bf16_round_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16)
     return x
 
 
 def full_storage(config_id: int, tensor: str, B: int, H: int, N: int, d: int, dtype: str,
                  threads: int = 8) -> np.ndarray:
-    """The whole [B][H][N][d] tensor in storage form (uint16 bf16 bits or float32)."""
-    out = np.empty((B, H, N, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    """The whole [B][H][N][d] tensor in storage form (uint16 bf16 bits, float16 or float32)."""
+    out = np.empty((B, H, N, d), dtype={"bf16": np.uint16, "f16": np.float16}.get(dtype, np.float32))
 
     def fill(bh):
         b, h = divmod(bh, H)

@@ -97,7 +97,7 @@ def call(fa, **over):
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(d=0), 2),
     (dict(B=1 << 20, H=1 << 12, N=1 << 20), 2),
-    (dict(dtype=2), 3), (dict(dtype=-1), 3),
+    (dict(dtype=3), 3), (dict(dtype=-1), 3),
     (dict(d=48), 4), (dict(d=160), 4), (dict(d=512), 4), (dict(d=256, dtype=0), 4),
     (dict(q=A + 8), 5), (dict(o=A + 0x3000004), 5), (dict(lse=A + 0x4000002), 5),
     (dict(scale=float("nan")), 6), (dict(scale=float("inf")), 6),
@@ -114,7 +114,7 @@ def test_python_binding_rejects_host_tensors(fa):
     with pytest.raises(ValueError):
         fa.fwd(q, q, q)
     with pytest.raises(TypeError):
-        fa.fwd(q.half(), q.half(), q.half())
+        fa.fwd(q.double(), q.double(), q.double())
 
 
 def test_schedule_is_a_bijection(tmp_path):

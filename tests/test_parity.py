@@ -4,7 +4,10 @@ Every case draws seeded inputs from synthetic.py, runs the HIP path through
 the C ABI (aware_softmax_amd.fwd -> fa_fwd) and compares O and L with
 oracle.naive_attention on the same bf16/fp32 values upcast to fp64.
 Tolerances (max-abs over every checked element): fp32 1e-5 on O and L;
-bf16 2e-2 on O and 1e-2 on L (fp32 accumulation).
+bf16 2e-2 on O and 1e-2 on L (fp32 accumulation); fp16 5e-3 on O and
+2e-3 on L: P and O are each rounded once to fp16 (relative 2^-11), so O
+moves by at most 2^-11 max|v - O| + half an fp16 ulp of |O| < 4
+(together < 3e-3) and L by the relative error of the row sum, < 1e-3.
 """
 import math
 
@@ -16,7 +19,7 @@ import synthetic
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2)}
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2), "f16": (5e-3, 2e-3)}
 
 
 @pytest.fixture(scope="module")
@@ -31,13 +34,13 @@ def to_device(storage, dtype):
 
     if dtype == "bf16":
         return torch.from_numpy(storage.view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(storage).cuda()
+    return torch.from_numpy(np.ascontiguousarray(storage)).cuda()
 
 
 def values(storage, dtype):
     if dtype == "bf16":
         return synthetic.bf16_bits_to_f32(storage)
-    return storage
+    return storage.astype(np.float32)
 
 
 def run_case(fa, config_id, B, H, N, d, dtype, causal, scale=None, heads=None, rows=None,
@@ -300,3 +303,29 @@ def test_gqa_forward_fp32(fa, causal):
     ref_o, ref_l = oracle.attention_gqa(st["q"][0], st["k"][0], st["v"][0], causal, 1 / math.sqrt(d))
     assert_close((float(np.max(np.abs(o[0].cpu().numpy() - ref_o))),
                   float(np.max(np.abs(lse[0].cpu().numpy() - ref_l)))), "f32")
+
+
+# ------------------------------------------------------------ float16
+
+
+@pytest.mark.parametrize("n", [1, 7, 64, 65, 129, 333, 1000])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f16_forward(fa, n, d, causal):
+    """The fp16 instantiation of both MFMA kernels (v_mfma_f32_32x32x16_f16)."""
+    cid = 1800 + n * 8 + (d // 32) * 2 + causal
+    assert_close(run_case(fa, cid, 2, 3, n, d, "f16", causal), "f16")
+
+
+def test_f16_forward_throughput_shape_sampled(fa):
+    """B2 H16 N4096 d128 causal fp16 (the steady max-free loop over many tiles)."""
+    rows = synthetic.sample_rows(1900, 4096, 256)
+    assert_close(run_case(fa, 1900, 2, 16, 4096, 128, "f16", True, rows=rows,
+                          heads=synthetic.sample_heads(1900, 2, 16, 4)), "f16")
+
+
+@pytest.mark.parametrize("scale", [2.0, -1.5])
+def test_f16_large_scores(fa, scale):
+    """Scores of |scale| * q.k up to ~30: probabilities above the fp16 range
+    must send the tile through the exact update (the overflow check)."""
+    assert_close(run_case(fa, 1910 + int(scale * 10), 1, 2, 1000, 128, "f16", True, scale=scale), "f16")
