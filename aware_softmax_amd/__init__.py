@@ -277,22 +277,23 @@ def fa_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, ws_ptr, ws_bytes, B, H, Hkv, 
 def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, lse=None, workspace=None,
            stream=None):
     """Split-K decode attention: q [B, H, d] against a cache k, v
-    [B, Hkv, N, d] (bf16 device tensors, H a multiple of Hkv).
+    [B, Hkv, N, d] (bf16 or fp16 device tensors, H a multiple of Hkv).
 
-    Returns (o [B, H, d] bf16, lse [B, H] float32).  num_splits = 0 lets the
+    Returns (o [B, H, d] like q, lse [B, H] float32).  num_splits = 0 lets the
     library choose; 1 runs the unsplit kernel.  out / lse / workspace (uint8,
     at least decode_plan(...)[2] bytes) may be passed to reuse buffers.
     Runs on `stream` (default: torch's current stream).
     """
     import torch
 
-    if q.dtype != torch.bfloat16:
-        raise TypeError(f"unsupported dtype {q.dtype} for decode; use torch.bfloat16")
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype} for decode; use torch.bfloat16 or torch.float16")
     if q.dim() != 3 or k.dim() != 4:
         raise ValueError("q must be [B, H, d] and k, v [B, Hkv, N, d]")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype:
-            raise ValueError(f"{name} must be bfloat16")
+            raise ValueError(f"{name} must have the dtype of q")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
@@ -319,6 +320,6 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
-                     workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits, DTYPE_BF16,
-                     stream.cuda_stream))
+                     workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits,
+                     dtypes[q.dtype], stream.cuda_stream))
     return out, lse

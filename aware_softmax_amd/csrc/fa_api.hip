@@ -213,7 +213,7 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
   size_t need = 0;
   const fa_status_t st = fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &need);
   if (st != FA_OK) return st;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!is_16bit(dtype)) return FA_ERR_DTYPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
     return FA_ERR_ALIGN;
@@ -246,7 +246,8 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
   p.d = d;
   p.scale = scale;
   p.num_splits = num_splits;
-  return fa::launch_decode_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_decode_bf16(p, stream) : fa::launch_decode_f16(p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

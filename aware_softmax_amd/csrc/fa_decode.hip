@@ -1,6 +1,7 @@
 // Decode attention with the key dimension split across workgroups
 // ("PidokuInfra 10 -- FlashAttention", section 5, "The decode variant:
-// FlashDecoding"), bfloat16 in/out, fp32 softmax state, gfx950.
+// FlashDecoding"), bfloat16 or float16 in/out (a template parameter), fp32
+// softmax state, gfx950.
 //
 // What is computed: one query row per (batch b, head h) against the N
 // cached keys and values of its key/value head hk = h / (H / Hkv)
@@ -38,7 +39,9 @@
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <class T>
+using vec2 = T __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
@@ -81,7 +84,23 @@ constexpr int rows_per_iter() {
   return kWaves * unroll<D, G>() * Shape<D>::RPI;
 }
 
-__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) { return __builtin_bit_cast(bf16x2, u); }
+// Dot product of two packed pairs with an fp32 accumulate (v_dot2), and the
+// two fp32 values of a packed pair: bf16 is the high half of an fp32, fp16
+// converts exactly.
+__device__ __forceinline__ float dot2(__bf16, unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(vec2<__bf16>, a), __builtin_bit_cast(vec2<__bf16>, b), c,
+                                         false);
+}
+__device__ __forceinline__ float dot2(_Float16, unsigned a, unsigned b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(vec2<_Float16>, a), __builtin_bit_cast(vec2<_Float16>, b), c,
+                                false);
+}
+__device__ __forceinline__ f32x2 unpack2(__bf16, unsigned u) {
+  return f32x2{__builtin_bit_cast(float, u << 16), __builtin_bit_cast(float, u & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x2 unpack2(_Float16, unsigned u) {
+  return __builtin_convertvector(__builtin_bit_cast(vec2<_Float16>, u), f32x2);
+}
 
 // Sum over the LPR lanes of a key row; every lane of the group gets the sum.
 template <int LPR>
@@ -102,9 +121,9 @@ __device__ __forceinline__ float row_sum(float x) {
 // part_o  [B*H][S][D]  fp32 unnormalised o~ of each split;
 // part_ml [B*H][S][2]  fp32 (m, l) of each split, m in log2 units of the
 //                      scaled scores (c = scale * log2 e folded in).
-template <int D, int G>
+template <class T, int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c) {
   constexpr int LPR = Shape<D>::LPR;
   constexpr int RPI = Shape<D>::RPI;
@@ -153,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const int k_begin = s * chunk;
   const int k_end = min(N, k_begin + chunk);
   const size_t head_off = (size_t)bhk * N * D;
-  const __bf16* kh = k + head_off + cc * 8;
-  const __bf16* vh = v + head_off + cc * 8;
+  const T* kh = k + head_off + cc * 8;
+  const T* vh = v + head_off + cc * 8;
 
   for (int r0 = k_begin + wave * ROWS_WAVE; r0 < k_end; r0 += kWaves * ROWS_WAVE) {
     u32x4 kf[U][CPL], vf[U][CPL];
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       for (int x = 0; x < CPL; ++x)
         vf[u][x] = __builtin_nontemporal_load((const u32x4*)(vh + (size_t)rc * D + x * LPR * 8));
     }
-    // V rows as fp32 (bf16 is the high half of an fp32).
+    // V rows as fp32.
     float vv[U][E];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -189,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         for (int x = 0; x < CPL; ++x)
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qf[i][4 * x + t]), as_bf16x2(kf[u][x][t]), acc, false);
+            acc = dot2(T{}, qf[i][4 * x + t], kf[u][x][t], acc);
         acc = row_sum<LPR>(acc);
         sc[u] = ok[u] ? acc * c : kNegInf;
         tmax = fmaxf(tmax, sc[u]);
@@ -213,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
           for (int x = 0; x < CPL; ++x)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-              vv[u][8 * x + 2 * t] = __builtin_bit_cast(float, vf[u][x][t] << 16);
-              vv[u][8 * x + 2 * t + 1] = __builtin_bit_cast(float, vf[u][x][t] & 0xffff0000u);
+              const f32x2 pr = unpack2(T{}, vf[u][x][t]);
+              vv[u][8 * x + 2 * t] = pr[0];
+              vv[u][8 * x + 2 * t + 1] = pr[1];
             }
       }
 #pragma unroll
@@ -286,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
 // Combine kernel: one workgroup of D threads per (b, h).  M = max_s m_s,
 // l = sum_s 2^(m_s - M) l_s, o = sum_s 2^(m_s - M) o~_s / l, and
 // lse = ln 2 * (M + log2 l) (m is in log2 units).
-template <int D>
+template <class T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml, __bf16* __restrict__ o,
+                                                           const float* __restrict__ part_ml, T* __restrict__ o,
                                                            float* __restrict__ lse, int S) {
   const int bh = blockIdx.x;
   const int e = threadIdx.x;
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
     ll = fmaf(wt, ml[2 * s + 1], ll);
     oo = fmaf(wt, po[(size_t)s * D], oo);
   }
-  o[(size_t)bh * D + e] = (__bf16)(oo / ll);
+  o[(size_t)bh * D + e] = (T)(oo / ll);
   if (e == 0) lse[bh] = (mm + __builtin_amdgcn_logf(ll)) * kLn2;
 }
 
@@ -339,40 +359,40 @@ int rows_per_iter_d(int d, int G) {
   }
 }
 
-template <int D, int G>
+template <class T, int D, int G>
 hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
   const float c = p.scale * kLog2e;
   float* po = (float*)p.workspace;
   float* pml = (float*)((char*)p.workspace + plan.ml_offset);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(plan.split_wgs), dim3(kThreads), 0, stream,
-                     (const __bf16*)p.q, (const __bf16*)p.k, (const __bf16*)p.v, po, pml, p.H, p.Hkv, p.N,
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(plan.split_wgs), dim3(kThreads), 0, stream,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, po, pml, p.H, p.Hkv, p.N,
                      plan.splits, plan.chunk, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.B * p.H), dim3(D), 0, stream, (const float*)po,
-                     (const float*)pml, (__bf16*)p.o, p.lse, plan.splits);
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.B * p.H), dim3(D), 0, stream, (const float*)po,
+                     (const float*)pml, (T*)p.o, p.lse, plan.splits);
   return hipGetLastError();
 }
 
-template <int D>
+template <class T, int D>
 hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
   if constexpr (max_group<D>() == 4) {
     switch (plan.heads_per_wg) {
-      case 1: return launch_g<D, 1>(p, plan, stream);
-      case 2: return launch_g<D, 2>(p, plan, stream);
-      case 3: return launch_g<D, 3>(p, plan, stream);
-      default: return launch_g<D, 4>(p, plan, stream);
+      case 1: return launch_g<T, D, 1>(p, plan, stream);
+      case 2: return launch_g<T, D, 2>(p, plan, stream);
+      case 3: return launch_g<T, D, 3>(p, plan, stream);
+      default: return launch_g<T, D, 4>(p, plan, stream);
     }
   } else {
     switch (plan.heads_per_wg) {
-      case 1: return launch_g<D, 1>(p, plan, stream);
-      case 2: return launch_g<D, 2>(p, plan, stream);
-      case 3: return launch_g<D, 3>(p, plan, stream);
-      case 4: return launch_g<D, 4>(p, plan, stream);
-      case 5: return launch_g<D, 5>(p, plan, stream);
-      case 6: return launch_g<D, 6>(p, plan, stream);
-      case 7: return launch_g<D, 7>(p, plan, stream);
-      default: return launch_g<D, 8>(p, plan, stream);
+      case 1: return launch_g<T, D, 1>(p, plan, stream);
+      case 2: return launch_g<T, D, 2>(p, plan, stream);
+      case 3: return launch_g<T, D, 3>(p, plan, stream);
+      case 4: return launch_g<T, D, 4>(p, plan, stream);
+      case 5: return launch_g<T, D, 5>(p, plan, stream);
+      case 6: return launch_g<T, D, 6>(p, plan, stream);
+      case 7: return launch_g<T, D, 7>(p, plan, stream);
+      default: return launch_g<T, D, 8>(p, plan, stream);
     }
   }
 }
@@ -407,16 +427,20 @@ DecodePlan decode_plan(int B, int H, int Hkv, int N, int d, int num_splits) {
 
 int decode_rows_per_iter(int d, int heads_per_wg) { return rows_per_iter_d(d, heads_per_wg); }
 
-hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
+template <class T>
+hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const DecodePlan plan = decode_plan(p.B, p.H, p.Hkv, p.N, p.d, p.num_splits);
   switch (p.d) {
-    case 32: return launch_d<32>(p, plan, stream);
-    case 64: return launch_d<64>(p, plan, stream);
-    case 96: return launch_d<96>(p, plan, stream);
-    case 128: return launch_d<128>(p, plan, stream);
-    case 256: return launch_d<256>(p, plan, stream);
+    case 32: return launch_d<T, 32>(p, plan, stream);
+    case 64: return launch_d<T, 64>(p, plan, stream);
+    case 96: return launch_d<T, 96>(p, plan, stream);
+    case 128: return launch_d<T, 128>(p, plan, stream);
+    case 256: return launch_d<T, 256>(p, plan, stream);
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) { return launch_decode_t<__bf16>(p, stream); }
+hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream) { return launch_decode_t<_Float16>(p, stream); }
 
 }  // namespace fa

@@ -92,6 +92,7 @@ hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream);
 
 // Backward workspace: -L/scale and -D, fp32 [BH][Npad] each; Npad = N
 // rounded up to the query tile of the dK/dV pass.

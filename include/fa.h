@@ -212,9 +212,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
 
 /*
  * fa_decode -- split-K decode attention.
- *   q         [in]  device, [B][H][d] bf16, 16-byte aligned.
- *   k, v      [in]  device, [B][Hkv][N][d] bf16, 16-byte aligned.
- *   o         [out] device, [B][H][d] bf16, 16-byte aligned.
+ *   q         [in]  device, [B][H][d] of dtype, 16-byte aligned.
+ *   k, v      [in]  device, [B][Hkv][N][d] of dtype, 16-byte aligned.
+ *   o         [out] device, [B][H][d] of dtype, 16-byte aligned.
  *   lse       [out] device, [B][H] float32, 4-byte aligned.
  *   workspace [scratch] device, at least fa_decode_workspace_bytes(...)
  *             bytes (passed as workspace_bytes), 256-byte aligned, owned by
@@ -224,7 +224,7 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
  *             or 256).
  *   scale     finite; multiplies q . k.
  *   num_splits  as for fa_decode_plan.
- *   dtype     FA_DTYPE_BF16 only.
+ *   dtype     FA_DTYPE_BF16 or FA_DTYPE_F16 (fp32 products and softmax).
  *   stream    HIP stream; two kernels are enqueued in order on it.
  * Outputs must not overlap each other, the inputs or the workspace
  * (FA_ERR_ALIAS).  No atomics: results are deterministic for a given split.

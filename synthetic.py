@@ -83,12 +83,14 @@ DECODE_WORKLOADS = {
 }
 
 
-def decode_storage(config_id: int, B: int, H: int, Hkv: int, N: int, d: int, threads: int = 8) -> dict:
-    """bf16 bits of a decode problem: q [B][H][d], k and v [B][Hkv][N][d]."""
+def decode_storage(config_id: int, B: int, H: int, Hkv: int, N: int, d: int, threads: int = 8,
+                   dtype: str = "bf16") -> dict:
+    """Storage form (bf16 bits or float16) of a decode problem: q [B][H][d],
+    k and v [B][Hkv][N][d]."""
     return {
-        "q": full_storage(config_id, "q", B, H, 1, d, "bf16", threads).reshape(B, H, d),
-        "k": full_storage(config_id, "k", B, Hkv, N, d, "bf16", threads),
-        "v": full_storage(config_id, "v", B, Hkv, N, d, "bf16", threads),
+        "q": full_storage(config_id, "q", B, H, 1, d, dtype, threads).reshape(B, H, d),
+        "k": full_storage(config_id, "k", B, Hkv, N, d, dtype, threads),
+        "v": full_storage(config_id, "v", B, Hkv, N, d, dtype, threads),
     }
 
 

@@ -9,9 +9,10 @@ token sees the whole cache), on the same bf16 values upcast to fp64.
 
 Tolerance: the bf16 bar of the forward (max |o - ref| <= 2e-2,
 max |lse - ref| <= 1e-2) and, because decode keeps P in fp32 and rounds only
-o to bf16 (relative 2^-9), a per-element bound with a 2x margin over that
-rounding, |o - ref| <= 2^-8 |ref| + 1e-4, and |lse - ref| <= 2e-4 max(1, |ref|)
-(fp32 dot products of length d and fp32 accumulation over N keys).
+o to the output type (relative 2^-9 for bf16, 2^-11 for fp16), a
+per-element bound with a 2x margin over that rounding,
+|o - ref| <= 2 u |ref| + 1e-4, and |lse - ref| <= 2e-4 max(1, |ref|) (fp32
+dot products of length d and fp32 accumulation over N keys).
 """
 import math
 
@@ -31,35 +32,46 @@ def fa():
     return aware_softmax_amd
 
 
-def to_device(bits):
+ROUND = {"bf16": 2.0 ** -9, "f16": 2.0 ** -11}
+
+
+def to_device(x):
     import torch
 
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float16:
+        return torch.from_numpy(x).cuda()
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def vals(x):
+    return x.astype(np.float32) if x.dtype == np.float16 else synthetic.bf16_bits_to_f32(x)
 
 
 def check_heads(st, o, lse, heads, H, Hkv, scale):
     group = H // Hkv
+    u = ROUND["f16" if st["q"].dtype == np.float16 else "bf16"]
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
     for b, h in heads:
-        q = synthetic.bf16_bits_to_f32(st["q"][b, h])[None, :]
-        k = synthetic.bf16_bits_to_f32(st["k"][b, h // group])
-        v = synthetic.bf16_bits_to_f32(st["v"][b, h // group])
+        q = vals(st["q"][b, h])[None, :]
+        k = vals(st["k"][b, h // group])
+        v = vals(st["v"][b, h // group])
         ref_o, ref_l = oracle.naive_attention(q, k, v, False, scale)
         err_o = np.abs(o[b, h].astype(np.float64) - ref_o[0])
         err_l = abs(float(lse[b, h]) - float(ref_l[0]))
         assert err_o.max() <= 2e-2, f"o[{b},{h}] max err {err_o.max():.3e}"
         assert err_l <= 1e-2, f"lse[{b},{h}] err {err_l:.3e}"
-        assert np.all(err_o <= 2.0 ** -8 * np.abs(ref_o[0]) + 1e-4), \
-            f"o[{b},{h}] exceeds the rounding bound: {np.max(err_o - 2.0 ** -8 * np.abs(ref_o[0])):.3e}"
+        assert np.all(err_o <= 2 * u * np.abs(ref_o[0]) + 1e-4), \
+            f"o[{b},{h}] exceeds the rounding bound: {np.max(err_o - 2 * u * np.abs(ref_o[0])):.3e}"
         assert err_l <= 2e-4 * max(1.0, abs(float(ref_l[0]))), f"lse[{b},{h}] err {err_l:.3e}"
 
 
-def run(fa, cid, B, H, Hkv, N, d, scale=None, num_splits=0, heads=None, st=None):
+def run(fa, cid, B, H, Hkv, N, d, scale=None, num_splits=0, heads=None, st=None, dtype="bf16"):
     import torch
 
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    st = synthetic.decode_storage(cid, B, H, Hkv, N, d) if st is None else st
+    st = synthetic.decode_storage(cid, B, H, Hkv, N, d, dtype=dtype) if st is None else st
     q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
     o, lse = fa.decode(q, k, v, scale=scale, num_splits=num_splits)
     torch.cuda.synchronize()
@@ -133,7 +145,7 @@ def test_scale_zero_is_mean_of_values(fa):
     q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
     o, lse = fa.decode(q, k, v, scale=0.0)
     torch.cuda.synchronize()
-    mean_v = synthetic.bf16_bits_to_f32(st["v"]).astype(np.float64).mean(axis=2)  # [B][Hkv][d]
+    mean_v = vals(st["v"]).astype(np.float64).mean(axis=2)  # [B][Hkv][d]
     got = o.float().cpu().numpy()
     for h in range(H):
         assert np.all(np.abs(got[0, h] - mean_v[0, h // 2]) <= 2.0 ** -8 * np.abs(mean_v[0, h // 2]) + 1e-4)
@@ -172,3 +184,18 @@ def test_outputs_untouched_outside_bounds(fa):
     assert torch.all(ob[size:] == 7.0) and torch.all(lb[B * H:] == 7.0)
     check_heads(st, ob[:size].view(B, H, d), lb[:B * H].view(B, H), [(0, h) for h in range(H)], H, Hkv,
                 1.0 / math.sqrt(d))
+
+
+# ------------------------------------------------------------ float16
+
+
+@pytest.mark.parametrize("n", [1, 65, 1000, 4097])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2)])
+def test_f16_decode(fa, n, d, heads):
+    H, Hkv = heads
+    run(fa, 7900 + n * 8 + Hkv + d, 2, H, Hkv, n, d, dtype="f16")
+
+
+def test_f16_decode_long(fa):
+    run(fa, 7990, 2, 32, 8, 32768, 128, dtype="f16", heads=synthetic.sample_heads(7990, 2, 32, 8))
