@@ -204,7 +204,7 @@ def fa_bwd_gqa(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_p
 
 def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq=None, dk=None, dv=None,
         workspace=None, stream=None):
-    """dQ, dK, dV of attention for [B, H, N, d] bf16 device tensors.
+    """dQ, dK, dV of attention for [B, H, N, d] bf16 or fp16 device tensors.
 
     k and v (and so dk, dv) may be [B, Hkv, N, d] with H a multiple of Hkv,
     as in fwd(); dk and dv then sum over the query heads of each group.
@@ -217,8 +217,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
     """
     import torch
 
-    if q.dtype != torch.bfloat16:
-        raise TypeError(f"unsupported dtype {q.dtype} for the backward; use torch.bfloat16")
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype} for the backward; use torch.bfloat16 or torch.float16")
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
     B, H, N, d = q.shape
@@ -240,7 +241,7 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
     dv = torch.empty_like(k) if dv is None else dv
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
         if t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {tuple(like.shape)}")
+            raise ValueError(f"{name} must be a contiguous tensor of q's dtype and shape {tuple(like.shape)}")
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -248,8 +249,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
         stream = torch.cuda.current_stream(q.device)
     _check(fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, causal, scale, DTYPE_BF16,
-                      stream.cuda_stream))
+                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, causal, scale,
+                      dtypes[q.dtype], stream.cuda_stream))
     return dq, dk, dv
 
 

@@ -130,7 +130,7 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
                        int H, int Hkv, int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (!is_16bit(dtype)) return FA_ERR_DTYPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX) return FA_ERR_SHAPE;
@@ -176,7 +176,8 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.group = H / Hkv;
-  return fa::launch_bwd_bf16(p, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f16(p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -1,4 +1,5 @@
-// FlashAttention-2 backward, bfloat16 in/out, fp32 accumulation, gfx950 MFMA.
+// FlashAttention-2 backward, bfloat16 or float16 in/out (a template
+// parameter), fp32 accumulation, gfx950 MFMA.
 //
 // What is computed (per batch*head), the chain rule through
 // O = softmax(scale * Q K^T + mask) V with P rebuilt from the saved row
@@ -61,9 +62,12 @@
 namespace fa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <class T>
+using vec8 = T __attribute__((ext_vector_type(8)));
+template <class T>
+using vec4 = T __attribute__((ext_vector_type(4)));
+template <class T>
+using vec2 = T __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -114,8 +118,8 @@ __device__ inline unsigned lds_addr(const void* p) {
 // queue before every read).  LDS reads complete in order, so a wait that
 // counts only the reads issued after a fragment is exact for it.  The loops
 // below issue no other LDS operation.
-template <int OFF>
-__device__ __forceinline__ void ds_b128(bf16x8& f, unsigned addr) {
+template <int OFF, class T>
+__device__ __forceinline__ void ds_b128(vec8<T>& f, unsigned addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
 template <int OFF>
@@ -126,14 +130,20 @@ template <int OFF>
 __device__ __forceinline__ void ds_tr64(s16x4& f, unsigned addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "i"(OFF));
 }
-__device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+template <class T>
+__device__ __forceinline__ vec8<T> join(const s16x4& lo, const s16x4& hi) {
+  return __builtin_bit_cast(vec8<T>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+// Two fp32 values rounded (to nearest even) to the element type, packed.
+template <class T>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, vec2<T>));
 }
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+__device__ __forceinline__ f32x16 mfma(const vec8<__bf16>& a, const vec8<__bf16>& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(const vec8<_Float16>& a, const vec8<_Float16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 // Waits until all but this wave's last KEEP vector memory operations (the
 // LDS-DMA copies of the tile after next, issued this iteration) and all its
@@ -146,13 +156,13 @@ __device__ __forceinline__ void dma_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copies rows [r0, r0 + kRows) of a row-major [N][D] bf16 matrix into a
+// Copies rows [r0, r0 + kRows) of a row-major [N][D] 16-bit matrix into a
 // swizzled LDS tile (rows past N - 1 are clamped; their values are never
 // used unmasked).  One wave instruction writes 1 KiB of LDS contiguously
 // (lane l at byte 16 l); the swizzle is applied by choosing which logical
 // chunk each lane fetches.  Wave w issues instructions [w IPW, (w + 1) IPW).
-template <int D, int kRows>
-__device__ __forceinline__ void dma_rows(const __bf16* X, int r0, int N, char* tile, int wave, int lane) {
+template <int D, int kRows, class T>
+__device__ __forceinline__ void dma_rows(const T* X, int r0, int N, char* tile, int wave, int lane) {
   constexpr int ROWB = 2 * D, CPR = D / 8, RPI = 1024 / ROWB;
   constexpr int IPW = kRows * ROWB / 1024 / kWaves;
   static_assert(kRows * ROWB % (1024 * kWaves) == 0, "DMA splits evenly over waves");
@@ -171,8 +181,8 @@ __device__ __forceinline__ void dma_rows(const __bf16* X, int r0, int N, char* t
 // Writes -D_i and -L_i / scale (in the units of the raw score q.k): the
 // initial values of the dP and S accumulators of the two main kernels, so
 // that their MFMAs produce dP - D and q.k - L / scale directly.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__ Og, const __bf16* __restrict__ dOg,
+template <class T, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, const T* __restrict__ dOg,
                                                       const float* __restrict__ Lg, float* __restrict__ Lsg,
                                                       float* __restrict__ Dng, int N, int Npad, float l_to_score) {
   constexpr int LPR = D / 8;
@@ -185,8 +195,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16* __restrict__
   float acc = 0.f;
   if (i < N) {
     const size_t off = ((size_t)bh * N + i) * D + c * 8;
-    const bf16x8 a = *(const bf16x8*)(Og + off);
-    const bf16x8 b = *(const bf16x8*)(dOg + off);
+    const vec8<T> a = *(const vec8<T>*)(Og + off);
+    const vec8<T> b = *(const vec8<T>*)(dOg + off);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
   }
@@ -219,11 +229,11 @@ struct DkdvLayout {
 //   B  dV^T += dO^T P and dK^T += Q^T dS        (8 DB MFMAs, transposing reads).
 // Iteration t runs A(t + 1) with V(t) riding on its MFMAs, then B(t); the
 // DMA of tile t + 2 is in flight meanwhile; one barrier per iteration.
-template <int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                     const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
-                     __bf16* __restrict__ dKg, __bf16* __restrict__ dVg, int BHkv, int N, int Npad, int nkb, float c,
+void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+                     const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
+                     T* __restrict__ dKg, T* __restrict__ dVg, int BHkv, int N, int Npad, int nkb, float c,
                      float scale, int group) {
   using Ly = DkdvLayout<D>;
   constexpr int DT = D / 16;
@@ -251,18 +261,18 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
   const int kw0 = kb0 + 32 * wave;  // first key of this wave
   const int key = kw0 + col;        // this lane's key (MFMA column)
   const size_t head = (size_t)bhk * (size_t)N * D;
-  const __bf16* Kh = Kg + head;
-  const __bf16* Vh = Vg + head;
+  const T* Kh = Kg + head;
+  const T* Vh = Vg + head;
 
   // K and V fragments of the wave's keys: B operands of S = Q K^T and
   // dP = dO V^T (lane: key `col`, d = 16t + 8 half .. + 7).
-  bf16x8 kf[DT], vf[DT];
+  vec8<T> kf[DT], vf[DT];
   {
     const size_t r = (size_t)min(key, N - 1) * D + half * 8;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      kf[t] = *(const bf16x8*)(Kh + r + 16 * t);
-      vf[t] = *(const bf16x8*)(Vh + r + 16 * t);
+      kf[t] = *(const vec8<T>*)(Kh + r + 16 * t);
+      vf[t] = *(const vec8<T>*)(Vh + r + 16 * t);
     }
   }
 
@@ -345,10 +355,10 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
       p[e] = pe;
       ds[e] = pe * dP[qb][4 * g + e];
     }
-    pw[qb][2 * g] = pack_bf16(p[0], p[1]);
-    pw[qb][2 * g + 1] = pack_bf16(p[2], p[3]);
-    dw[qb][2 * g] = pack_bf16(ds[0], ds[1]);
-    dw[qb][2 * g + 1] = pack_bf16(ds[2], ds[3]);
+    pw[qb][2 * g] = pack2<T>(p[0], p[1]);
+    pw[qb][2 * g + 1] = pack2<T>(p[2], p[3]);
+    dw[qb][2 * g] = pack2<T>(ds[0], ds[1]);
+    dw[qb][2 * g + 1] = pack2<T>(ds[2], ds[3]);
   };
 
   // One tile: phase A, then phase B with the VALU groups of step u + 1
@@ -368,7 +378,7 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         ds_b128f<(32 * qb + 8 * g) * 4>(init[0][qb][g], ast);
         ds_b128f<(kBQ + 32 * qb + 8 * g) * 4>(init[1][qb][g], ast);
       });
-      bf16x8 fa[LA];
+      vec8<T> fa[LA];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, qb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
         ds_b128<0>(fa[F % LA], (X ? ado : aq) + (rf_lane[qb] ^ (unsigned)(t << 5)));
@@ -418,13 +428,13 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
         constexpr int qb = u / 2, h2 = u % 2;
         asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo_[F % LB]), "+v"(hi_[F % LB]) : "i"(2 * (last - F)));
         if constexpr (X == 0) {
-          const bf16x8 pf = __builtin_bit_cast(
-              bf16x8, (u32x4){pw[qb][4 * h2], pw[qb][4 * h2 + 1], pw[qb][4 * h2 + 2], pw[qb][4 * h2 + 3]});
-          dvT[bb] = mfma(join(lo_[F % LB], hi_[F % LB]), pf, dvT[bb]);
+          const vec8<T> pf = __builtin_bit_cast(
+              vec8<T>, (u32x4){pw[qb][4 * h2], pw[qb][4 * h2 + 1], pw[qb][4 * h2 + 2], pw[qb][4 * h2 + 3]});
+          dvT[bb] = mfma(join<T>(lo_[F % LB], hi_[F % LB]), pf, dvT[bb]);
         } else {
-          const bf16x8 dsf = __builtin_bit_cast(
-              bf16x8, (u32x4){dw[qb][4 * h2], dw[qb][4 * h2 + 1], dw[qb][4 * h2 + 2], dw[qb][4 * h2 + 3]});
-          dkT[bb] = mfma(join(lo_[F % LB], hi_[F % LB]), dsf, dkT[bb]);
+          const vec8<T> dsf = __builtin_bit_cast(
+              vec8<T>, (u32x4){dw[qb][4 * h2], dw[qb][4 * h2 + 1], dw[qb][4 * h2 + 2], dw[qb][4 * h2 + 3]});
+          dkT[bb] = mfma(join<T>(lo_[F % LB], hi_[F % LB]), dsf, dkT[bb]);
         }
         if constexpr (F + LB < NB) issue(ic<F + LB>{});
         // groups 2 (u + 1) and 2 (u + 1) + 1 after the first and second half
@@ -465,20 +475,20 @@ void bwd_dkdv_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ K
 
   // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
   if (key < N) {
-    __bf16* dkrow = dKg + head + (size_t)key * D + 4 * half;
-    __bf16* dvrow = dVg + head + (size_t)key * D + 4 * half;
+    T* dkrow = dKg + head + (size_t)key * D + 4 * half;
+    T* dvrow = dVg + head + (size_t)key * D + 4 * half;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 ok, ov;
+        vec4<T> ok, ov;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ok[e] = (__bf16)(dkT[b][4 * g + e] * scale);
-          ov[e] = (__bf16)dvT[b][4 * g + e];
+          ok[e] = (T)(dkT[b][4 * g + e] * scale);
+          ov[e] = (T)dvT[b][4 * g + e];
         }
-        *(bf16x4*)(dkrow + 32 * b + 8 * g) = ok;
-        *(bf16x4*)(dvrow + 32 * b + 8 * g) = ov;
+        *(vec4<T>*)(dkrow + 32 * b + 8 * g) = ok;
+        *(vec4<T>*)(dvrow + 32 * b + 8 * g) = ov;
       }
   }
 }
@@ -501,11 +511,11 @@ struct DqLayout {
 //   V  P = 2^(c S^T), dS^T = P dP^T, packed to bf16;
 //   C  dQ^T += K^T dS^T                               (4 DB MFMAs, transposing reads).
 // Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
-template <int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg, const __bf16* __restrict__ Vg,
-                   const __bf16* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
-                   __bf16* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group) {
+void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
+                   const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
+                   T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group) {
   using Ly = DqLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -530,20 +540,20 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
   const int qi = qw + col;  // this lane's query (MFMA column)
   const size_t head = (size_t)bh * (size_t)N * D;
   const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;  // key/value head of query head bh
-  const __bf16* Qh = Qg + head;
-  const __bf16* Kh = Kg + kvhead;
-  const __bf16* Vh = Vg + kvhead;
-  const __bf16* dOh = dOg + head;
+  const T* Qh = Qg + head;
+  const T* Kh = Kg + kvhead;
+  const T* Vh = Vg + kvhead;
+  const T* dOh = dOg + head;
 
   // Q and dO fragments of the wave's queries: B operands of S^T = K Q^T and
   // dP^T = V dO^T (lane: query `col`, d = 16t + 8 half .. + 7).
-  bf16x8 qf[DT], dof[DT];
+  vec8<T> qf[DT], dof[DT];
   {
     const size_t r = (size_t)min(qi, N - 1) * D + half * 8;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      qf[t] = *(const bf16x8*)(Qh + r + 16 * t);
-      dof[t] = *(const bf16x8*)(dOh + r + 16 * t);
+      qf[t] = *(const vec8<T>*)(Qh + r + 16 * t);
+      dof[t] = *(const vec8<T>*)(dOh + r + 16 * t);
     }
   }
   const int qs = min(qi, Npad - 1);
@@ -605,8 +615,8 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
       }
       ds[e] = pe * dP[kb][4 * g + e];
     }
-    dw[kb][2 * g] = pack_bf16(ds[0], ds[1]);
-    dw[kb][2 * g + 1] = pack_bf16(ds[2], ds[3]);
+    dw[kb][2 * g] = pack2<T>(ds[0], ds[1]);
+    dw[kb][2 * g + 1] = pack2<T>(ds[2], ds[3]);
   };
 
   auto iteration = [&](int j, auto mask_c) {
@@ -622,7 +632,7 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
           S[kb][r] = ls;
           dP[kb][r] = dn;
         }
-      bf16x8 fa[LA];
+      vec8<T> fa[LA];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, kb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
         ds_b128<0>(fa[F % LA], (X ? av : ak) + (rf_lane[kb] ^ (unsigned)(t << 5)));
@@ -655,9 +665,9 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
         constexpr int last = (F + LC - 1 < NC - 1) ? F + LC - 1 : NC - 1;
         constexpr int kb = u / 2, h2 = u % 2;
         asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo_[F % LC]), "+v"(hi_[F % LC]) : "i"(2 * (last - F)));
-        const bf16x8 dsf = __builtin_bit_cast(
-            bf16x8, (u32x4){dw[kb][4 * h2], dw[kb][4 * h2 + 1], dw[kb][4 * h2 + 2], dw[kb][4 * h2 + 3]});
-        dqT[bb] = mfma(join(lo_[F % LC], hi_[F % LC]), dsf, dqT[bb]);
+        const vec8<T> dsf = __builtin_bit_cast(
+            vec8<T>, (u32x4){dw[kb][4 * h2], dw[kb][4 * h2 + 1], dw[kb][4 * h2 + 2], dw[kb][4 * h2 + 3]});
+        dqT[bb] = mfma(join<T>(lo_[F % LC], hi_[F % LC]), dsf, dqT[bb]);
         if constexpr (F + LC < NC) issue(ic<F + LC>{});
         // groups 2 (u + 1) and 2 (u + 1) + 1 ride on step u's MFMAs
         constexpr int f = F % DB;
@@ -696,20 +706,20 @@ void bwd_dq_kernel(const __bf16* __restrict__ Qg, const __bf16* __restrict__ Kg,
 
   // ---- dQ = scale * (dQ^T)^T: lane writes query qi, d = 32 b + 8 g + 4 half + {0..3}.
   if (qi < N) {
-    __bf16* row = dQg + head + (size_t)qi * D + 4 * half;
+    T* row = dQg + head + (size_t)qi * D + 4 * half;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        bf16x4 o;
+        vec4<T> o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (__bf16)(dqT[b][4 * g + e] * scale);
-        *(bf16x4*)(row + 32 * b + 8 * g) = o;
+        for (int e = 0; e < 4; ++e) o[e] = (T)(dqT[b][4 * g + e] * scale);
+        *(vec4<T>*)(row + 32 * b + 8 * g) = o;
       }
   }
 }
 
-template <int D>
+template <class T, int D>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const int npad = (p.N + kBQ - 1) / kBQ * kBQ;
   // P = 2^(c (q.k - L / scale)) with c = scale log2(e).  |c| is kept at
@@ -719,14 +729,14 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   if (fabsf(c) < 1e-30f) c = c < 0.f ? -1e-30f : 1e-30f;
   float* ls = (float*)p.workspace;
   float* dn = ls + (size_t)p.BH * npad;
-  const __bf16* q = (const __bf16*)p.q;
-  const __bf16* k = (const __bf16*)p.k;
-  const __bf16* v = (const __bf16*)p.v;
-  const __bf16* dout = (const __bf16*)p.dout;
+  const T* q = (const T*)p.q;
+  const T* k = (const T*)p.k;
+  const T* v = (const T*)p.v;
+  const T* dout = (const T*)p.dout;
   {
     constexpr int RPB = 256 / (D / 8);
     const size_t rows = (size_t)p.BH * npad;  // a multiple of RPB
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(rows / RPB)), dim3(256), 0, stream, (const __bf16*)p.o,
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)(rows / RPB)), dim3(256), 0, stream, (const T*)p.o,
                        dout, p.lse, ls, dn, p.N, npad, kLog2e / c);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -736,11 +746,11 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const int bhkv = p.BH / p.group;
     const dim3 grid((unsigned)(bhkv * nkb)), block(kThreads);
     if (p.causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
-                         (__bf16*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dk,
-                         (__bf16*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -748,10 +758,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const int nqb = (p.N + kBQdq - 1) / kBQdq;
     const dim3 grid((unsigned)(p.BH * nqb)), block(kThreads);
     if (p.causal)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dq,
                          p.BH, p.N, npad, nqb, c, p.scale, p.group);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (__bf16*)p.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dq,
                          p.BH, p.N, npad, nqb, c, p.scale, p.group);
     return hipGetLastError();
   }
@@ -769,7 +779,10 @@ int bwd_block_k() { return kBKV; }
 int bwd_block_q() { return kBQ; }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  return p.d == 64 ? launch_bwd<64>(p, stream) : launch_bwd<128>(p, stream);
+  return p.d == 64 ? launch_bwd<__bf16, 64>(p, stream) : launch_bwd<__bf16, 128>(p, stream);
+}
+hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream) {
+  return p.d == 64 ? launch_bwd<_Float16, 64>(p, stream) : launch_bwd<_Float16, 128>(p, stream);
 }
 
 }  // namespace fa

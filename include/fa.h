@@ -134,17 +134,18 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  * and dV are formed that way, and dQ by a second, query-parallel pass that
  * rebuilds P and dP for its rows instead of atomics (no atomics at all).
  *
- *   q, k, v, o, dout  [in]  device, [B][H][N][d] bf16, 16-byte aligned; o is
+ *   q, k, v, o, dout  [in]  device, [B][H][N][d] of dtype, 16-byte aligned; o is
  *                     the forward output for the same q, k, v, causal, scale.
  *   lse       [in]  device, [B][H][N] float32 (the forward's L), 4-byte aligned.
- *   dq, dk, dv [out] device, [B][H][N][d] bf16, 16-byte aligned; must not
+ *   dq, dk, dv [out] device, [B][H][N][d] of dtype, 16-byte aligned; must not
  *                     overlap each other, the inputs or the workspace.
  *   workspace [scratch] device, at least fa_bwd_workspace_bytes(B, H, N, d)
  *                     bytes (passed as workspace_bytes), 256-byte aligned,
  *                     owned by the caller; overwritten, contents undefined
  *                     afterwards.  It needs no initialisation.
  *   B, H, N, d, causal, scale   as for fa_fwd.
- *   dtype     FA_DTYPE_BF16 only (FA_DTYPE_F32 returns FA_ERR_DTYPE).
+ *   dtype     FA_DTYPE_BF16 or FA_DTYPE_F16 (P and dS are rounded to it for
+ *             the MFMAs); FA_DTYPE_F32 returns FA_ERR_DTYPE.
  *   stream    HIP stream; three kernels are enqueued in order on it.
  * Returns FA_OK or the first failed check.  The outputs are deterministic:
  * the same inputs give bitwise identical dq, dk and dv.

@@ -18,6 +18,9 @@ workload gives max-abs errors of 0.007-0.011 against max |ref| of 2-5 and
 a relative rms error of 2.4e-3; the bounds leave a 2-4x margin over that
 model while a wrong term (a dropped D, a missing scale, a transposed
 operand) moves the gradients by O(max |ref|).
+float16 rounds P, dS, O and the gradients 4x finer (2^-11 relative), and
+its bounds scale down accordingly: max <= 5e-3 * max(1, max |ref|),
+rms <= 2.5e-3 * rms(ref) + 1e-4.
 """
 import math
 
@@ -37,38 +40,49 @@ def fa():
     return aware_softmax_amd
 
 
+TOL = {"bf16": (2e-2, 1e-2), "f16": (5e-3, 2.5e-3)}
+
+
 def to_device(storage):
     import torch
 
+    storage = np.ascontiguousarray(storage)
+    if storage.dtype == np.float16:
+        return torch.from_numpy(storage).cuda()
     return torch.from_numpy(storage.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def assert_grad_close(name, got, ref):
+def vals(storage):
+    return storage.astype(np.float32) if storage.dtype == np.float16 else synthetic.bf16_bits_to_f32(storage)
+
+
+def assert_grad_close(name, got, ref, dtype="bf16"):
+    t_max, t_rms = TOL[dtype]
     max_abs = float(np.abs(got - ref).max())
-    bound = 2e-2 * max(1.0, float(np.abs(ref).max()))
+    bound = t_max * max(1.0, float(np.abs(ref).max()))
     assert max_abs <= bound, f"{name}: max |got - ref| = {max_abs:.3e} > {bound:.3e}"
     rms_err = float(np.sqrt(np.mean((got - ref) ** 2)))
-    rms_bound = 1e-2 * float(np.sqrt(np.mean(ref ** 2))) + 1e-4
+    rms_bound = t_rms * float(np.sqrt(np.mean(ref ** 2))) + 1e-4
     assert rms_err <= rms_bound, f"{name}: rms error {rms_err:.3e} > {rms_bound:.3e}"
 
 
-def run_bwd(fa, config_id, B, H, N, d, causal, scale=None, heads=None, tensors=None):
+def run_bwd(fa, config_id, B, H, N, d, causal, scale=None, heads=None, tensors=None, dtype="bf16"):
     """Runs fwd + bwd on the GPU and checks dQ, dK, dV of the given heads."""
     import torch
 
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if tensors is None:
-        tensors = {t: synthetic.full_storage(config_id, t, B, H, N, d, "bf16") for t in ("q", "k", "v", "do")}
+        tensors = {t: synthetic.full_storage(config_id, t, B, H, N, d, dtype) for t in ("q", "k", "v", "do")}
     q, k, v, do = (to_device(tensors[t]) for t in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
     torch.cuda.synchronize()
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     for b, h in heads:
-        vals = [synthetic.bf16_bits_to_f32(tensors[t][b, h]) for t in ("q", "k", "v", "do")]
-        ref = oracle.attention_bwd(*vals, causal, scale)
+        v64 = [vals(tensors[t][b, h]) for t in ("q", "k", "v", "do")]
+        ref = oracle.attention_bwd(*v64, causal, scale)
         for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
-            assert_grad_close(f"{name}[{b},{h}]", got[b, h].float().cpu().numpy().astype(np.float64), r)
+            assert_grad_close(f"{name}[{b},{h}]", got[b, h].float().cpu().numpy().astype(np.float64), r, dtype)
     return dq, dk, dv
 
 
@@ -207,3 +221,18 @@ def test_gqa_backward_deterministic(fa):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+# ------------------------------------------------------------ float16
+
+
+@pytest.mark.parametrize("n", [1, 65, 200, 513])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f16_backward(fa, n, d, causal):
+    run_bwd(fa, 8000 + n * 4 + (d == 128) * 2 + causal, 1, 2, n, d, causal, dtype="f16")
+
+
+def test_f16_backward_workload5_sampled_heads(fa):
+    w = synthetic.WORKLOADS[5]
+    run_bwd(fa, 8100, w.B, w.H, w.N, w.d, True, heads=synthetic.sample_heads(8100, w.B, w.H, 2), dtype="f16")
