@@ -199,6 +199,63 @@ def time_gqa(fa, steps=10, warmup=2):
     return out
 
 
+def time_f16(fa, steps=10, warmup=2):
+    """float16 legs: causal forward B8 H32 N8192 d128, backward B2 H16 N4096
+    d128 and decode B8 H32 N32768 d128 (inputs seeded like the bf16
+    workloads, rounded to fp16)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    out = {}
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def tens(cid, t, B, H, N, d):
+        return torch.from_numpy(synthetic.full_storage(cid, t, B, H, N, d, "f16", threads=16)).to(dev)
+
+    for (B, H, N, d, with_bwd) in ((8, 32, 8192, 128, False), (2, 16, 4096, 128, True)):
+        q, k, v = (tens(3, t, B, H, N, d) for t in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        f = attention_flops(B, H, N, d, True)
+        ms = timed(lambda: fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse))
+        out[f"causal fp16 fwd B{B} H{H} N{N} d{d}"] = {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2)}
+        if with_bwd:
+            do = tens(3, "do", B, H, N, d)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+            ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale, dq=dq, dk=dk, dv=dv,
+                                      workspace=ws))
+            out[f"causal fp16 bwd B{B} H{H} N{N} d{d}"] = {"ms": round(ms, 4),
+                                                          "TFLOP/s": round(2.5 * f / (ms * 1e-3) / 1e12, 2)}
+            del do, dq, dk, dv
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    w = synthetic.DECODE_WORKLOADS[6]
+    st = synthetic.decode_storage(w.config_id, w.B, w.H, w.Hkv, w.N, w.d, 16, dtype="f16")
+    q, k, v = (torch.from_numpy(st[t]).to(dev) for t in ("q", "k", "v"))
+    del st
+    r = time_decode(fa, w, q, k, v, 0, steps, warmup)
+    out["decode fp16 B8 H32 N32768 d128 split-K"] = r
+    del q, k, v
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_inputs(w, threads=16):
     import numpy as np
     import torch
@@ -419,6 +476,7 @@ def main():
             del qq, kk, vv, oo, ll
             torch.cuda.empty_cache()
         extra.update(time_gqa(fa))
+        extra.update(time_f16(fa))
         for cid in (6, 7, 8):
             dw = synthetic.DECODE_WORKLOADS[cid]
             dq_, dk_, dv_ = decode_inputs(dw)
