@@ -16,6 +16,8 @@ __all__ = [
     "fwd",
     "fa_fwd",
     "fa_fwd_gqa",
+    "fa_fwd_varlen",
+    "fwd_varlen",
     "fa_bwd_gqa",
     "bwd",
     "fa_bwd",
@@ -63,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_fwd.restype = ci
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd_gqa.restype = ci
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+    lib.fa_fwd_varlen.restype = ci
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd_tile.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
@@ -323,4 +327,59 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits,
                      dtypes[q.dtype], stream.cuda_stream))
+    return out, lse
+
+
+def fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, B, H, Hkv, total, max_seqlen, d, causal, scale,
+                  dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses."""
+    return _LIB.fa_fwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, cu_ptr, int(B), int(H), int(Hkv), int(total),
+                              int(max_seqlen), int(d), int(bool(causal)), float(scale), int(dtype), stream)
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None, out=None,
+               lse=None, stream=None):
+    """Forward over packed sequences of different lengths.
+
+    q [H, total, d] and k, v [Hkv, total, d] (bf16 or fp16 device tensors)
+    hold the rows of all sequences one after another; cu_seqlens is an int32
+    device tensor of B + 1 offsets (sequence b = rows cu_seqlens[b] ..
+    cu_seqlens[b + 1] - 1) and max_seqlen the longest length (a host int).
+    Returns (o [H, total, d], lse [H, total] float32).
+    """
+    import torch
+
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype} for varlen; use torch.bfloat16 or torch.float16")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [H, total, d] and k, v [Hkv, total, d]")
+    H, total, d = q.shape
+    Hkv = k.shape[0]
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != (Hkv, total, d):
+            raise ValueError(f"{name} must be [Hkv, total, d] with the dtype, total and d of q")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of B + 1 offsets")
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [H, total] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                         cu_seqlens.data_ptr(), B, H, Hkv, total, max_seqlen, d, causal, scale, dtypes[q.dtype],
+                         stream.cuda_stream))
     return out, lse

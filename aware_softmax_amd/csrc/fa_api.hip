@@ -110,6 +110,58 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);
 }
 
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens,
+                          int B, int H, int Hkv, int total, int max_seqlen, int d, int causal, float scale,
+                          fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || total <= 0 || max_seqlen <= 0 || d <= 0 || H % Hkv != 0)
+    return FA_ERR_SHAPE;
+  if (!is_16bit(dtype)) return FA_ERR_DTYPE;
+  const fa_status_t st = check_dtype_headdim(d, dtype);
+  if (st != FA_OK) return st;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX || max_seqlen > total) return FA_ERR_SHAPE;
+  const int64_t elems = (int64_t)H * total * d;
+  if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const fa::TileConfig tile = fa::mfma_tile(d);
+  const int64_t nqb = ((int64_t)max_seqlen + tile.block_q - 1) / tile.block_q;
+  if (bh * nqb * 64 * tile.waves > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 ||
+      (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t tbytes = (size_t)elems * 2;
+  const size_t kvbytes = (size_t)Hkv * total * d * 2;
+  const size_t lbytes = (size_t)H * total * sizeof(float);
+  const size_t cbytes = (size_t)(B + 1) * sizeof(int);
+  const void* ins[4] = {q, k, v, cu_seqlens};
+  const size_t in_bytes[4] = {tbytes, kvbytes, kvbytes, cbytes};
+  void* outs[2] = {o, lse};
+  const size_t out_bytes[2] = {tbytes, lbytes};
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 4; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
+  if (ranges_overlap(o, tbytes, lse, lbytes)) return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)bh;
+  p.N = max_seqlen;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.group = H / Hkv;
+  p.cu_seqlens = cu_seqlens;
+  p.H = H;
+  p.total = total;
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f16(p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
   const int64_t bh = (int64_t)B * H;

@@ -134,6 +134,36 @@ __device__ inline unsigned lds_addr(const void* p) {
 // lane's 4*half: kb*32 + (r/4)*8 + r%4.
 __device__ constexpr int score_key_offset(int i) { return (i >> 4) * 32 + ((i >> 2) & 3) * 8 + (i & 3); }
 
+// Where the rows of query head bh live.  Fixed length: q, o [BH][N][D],
+// k, v [BH / group][N][D], L [BH][N].  Variable length (cu_seqlens, B + 1
+// offsets into `total` packed rows per head): q, o [H][total][D], k, v
+// [H / group][total][D], L [H][total]; bh = b H + h, and sequence b holds
+// rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of every head.  Query heads of
+// a group are consecutive, so head h reads key/value head h / group.
+struct HeadRows {
+  size_t q, kv, l;  // element offsets of row 0 of the Q/O head, the K/V head, the L row
+  int n;            // rows of the sequence
+};
+__device__ inline HeadRows head_rows(int bh, int group, int N, int D, const int* cu_seqlens, int H, int total) {
+  HeadRows r;
+  if (cu_seqlens) {
+    const int b = bh / H, h = bh - b * H;
+    // offsets clamped to [0, total], so no row outside the packed tensors is
+    // ever addressed, whatever the array holds
+    const int r0 = min(max(cu_seqlens[b], 0), total);
+    r.n = min(max(cu_seqlens[b + 1], r0), total) - r0;
+    r.l = (size_t)h * total + r0;
+    r.q = r.l * D;
+    r.kv = ((size_t)(h / group) * total + r0) * D;
+  } else {
+    r.n = N;
+    r.l = (size_t)bh * N;
+    r.q = r.l * D;
+    r.kv = (size_t)(bh / group) * N * D;
+  }
+  return r;
+}
+
 // Online-softmax update of one 64-key tile for the lane's query row
 // ("FlashAttention-2: ...", "FA2 change #1"; "FlashAttention: Move Less,
 // Not Compute Less", "Tiling Is Easy"): sv holds the lane's 32 raw scores
@@ -205,7 +235,7 @@ template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
     const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
     T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
-    int group) {
+    int group, const int* __restrict__ cu_seqlens, int H, int total) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;  // 16-wide d steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
@@ -220,13 +250,15 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
   const int q0 = qb * kBQ;
-  const size_t head = (size_t)bh * (size_t)N * D;
+  HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
+  if (cu_seqlens) {
+    N = hr.n;
+    if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
+  }
+  const size_t head = hr.q;
   const T* Qh = Qg + head;
-  // Query heads of a group are consecutive, so head bh reads key/value
-  // head bh / group.
-  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
-  const T* Kh = Kg + kvhead;
-  const T* Vh = Vg + kvhead;
+  const T* Kh = Kg + hr.kv;
+  const T* Vh = Vg + hr.kv;
 
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
   const int qw = q0 + wave * kRowsPerWave;  // first query row of this wave
@@ -374,7 +406,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
         for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[b][g * 4 + e] * inv);
         *(vec4<T>*)(orow + b * 32 + g * 8) = out;
       }
-    if (half == 0) Lg[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    if (half == 0) Lg[hr.l + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 
@@ -574,7 +606,7 @@ template <class T, int D, bool CAUSAL, bool FULL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
-    int group) {
+    int group, const int* __restrict__ cu_seqlens, int H, int total) {
   using Ly = Layout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -594,13 +626,15 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
   const int q0 = qb * kBQ;
-  const size_t head = (size_t)bh * (size_t)N * D;
+  HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
+  if (cu_seqlens) {
+    N = hr.n;
+    if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
+  }
+  const size_t head = hr.q;
   const T* Qh = Qg + head;
-  // Query heads of a group are consecutive, so head bh reads key/value
-  // head bh / group.
-  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;
-  const T* Kh = Kg + kvhead;
-  const T* Vh = Vg + kvhead;
+  const T* Kh = Kg + hr.kv;
+  const T* Vh = Vg + hr.kv;
 
   // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
   // -inf * c stays -inf for hidden keys.
@@ -956,7 +990,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[b][g * 4 + e] * inv);
         *(vec4<T>*)(orow + b * 32 + g * 8) = out;
       }
-    if (half == 0) Lg[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+    if (half == 0) Lg[hr.l + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 
@@ -983,11 +1017,15 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   float* lse = p.lse;
   int bh = p.BH, n = p.N;
   int group = p.group;
-  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group};
+  const int* cu = p.cu_seqlens;
+  int H = p.H, total = p.total;
+  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
   const void* fn;
+  // FULL (no row clamping in the copies) needs every sequence to be a whole
+  // number of key tiles: known only for fixed length.
   if constexpr (kDuo)
-    fn = p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
-                        : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
+    fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
+                               : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
   else
     fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -20,6 +20,12 @@ struct FwdParams {
   int causal;   // nonzero: query i sees keys 0..i
   float scale;  // multiplies Q K^T
   int group;    // query heads per key/value head (H / Hkv); k, v are [B][Hkv][N][d]
+  // Variable length (16-bit forward only): when cu_seqlens (device, B + 1
+  // ints) is set, N is the longest sequence, BH = B * H, and q, o are
+  // [H][total][d], k, v [H / group][total][d], lse [H][total].
+  const int* cu_seqlens = nullptr;
+  int H = 0;
+  int total = 0;
 };
 
 // Tile shape per (dtype, d).

@@ -71,7 +71,7 @@ typedef enum {
  *   B, H, N  sizes (> 0); any N >= 1 (ragged tails are masked).
  *   d        head dimension: 32, 64, 96, 128 or 256 for bf16 and fp16;
  *            32, 64, 96 or 128 for fp32 ("PidokuInfra 10 -- FlashAttention",
- *            section 9: kernels commonly cover 64, 96, 128 and 256).
+ *            sections 8-9: kernels commonly cover 64, 96, 128 and 256).
  *   causal   0: every query sees all N keys; nonzero: query i sees 0..i.
  *   scale    multiplies Q K^T before mask and softmax (finite; 1/sqrt(d)
  *            in the usual case; 0 and negative values are allowed).
@@ -98,6 +98,37 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int Hkv, int N, int d, int causal, float scale,
                        fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_fwd_varlen -- the forward over a batch of B sequences of different
+ * lengths packed without padding ("FlashAttention: Move Less, Not Compute
+ * Less", "What It Changes--and What It Does Not": the reference
+ * implementation has variable-length paths; "PidokuInfra 10 --
+ * FlashAttention", sections 8-9: padding sequences instead wastes the
+ * kernel's work).  Every head holds the `total` rows of all sequences one
+ * after another; sequence b is rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1
+ * and attends only within itself (causal: row i of the sequence sees its
+ * rows 0..i).
+ *
+ *   q, o        [in]/[out] device, [H][total][d] of dtype, 16-byte aligned.
+ *   k, v        [in]  device, [Hkv][total][d] of dtype, 16-byte aligned
+ *               (query head h reads key/value head h / (H / Hkv)).
+ *   lse         [out] device, [H][total] float32, 4-byte aligned.
+ *   cu_seqlens  [in]  device, B + 1 int32, 4-byte aligned: 0 =
+ *               cu_seqlens[0] <= cu_seqlens[1] <= ... <= cu_seqlens[B] =
+ *               total.  Read only by the kernel (the host never waits for
+ *               it); offsets are clamped to [0, total] on the device, so
+ *               malformed offsets cannot address memory outside the
+ *               tensors, but their results are undefined.
+ *   max_seqlen  the longest sequence (1 <= max_seqlen <= total); rows of a
+ *               longer sequence past max_seqlen are not written.
+ *   dtype       FA_DTYPE_BF16 or FA_DTYPE_F16.
+ *   d, causal, scale, stream   as for fa_fwd.
+ * Empty sequences are allowed.  Returns FA_OK or the first failed check.
+ */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                          int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(fa_status_t status);

@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     attention_bwd,
     attention_bwd_gqa,
     attention_gqa,
+    attention_varlen,
     attention_from_scores,
     combine_partials,
     naive_attention,

@@ -20,7 +20,8 @@ Sources, cited by page title and section:
      "Why More Arithmetic Can Finish Sooner" (the backward rebuilds S, P
      from saved per-row statistics),
      "What It Changes--and What It Does Not" (GQA shrinks the number of
-     key/value heads; the reference implementation has GQA/MQA paths).
+     key/value heads; the reference implementation has GQA/MQA and
+     variable-length paths).
 [P3] "PidokuInfra 10 -- FlashAttention": section 1 (softmax(QK^T/sqrt(d))V,
      exact), section 4 "Tiny example -- the algorithm" (block loop with a
      causal per-row key bound, online update, normalise at the end),
@@ -60,6 +61,7 @@ __all__ = [
     "attention_batched",
     "attention_gqa",
     "attention_bwd_gqa",
+    "attention_varlen",
 ]
 
 
@@ -315,3 +317,26 @@ def attention_bwd_gqa(q, k, v, do, causal, scale):
         dk[h // group] += gk
         dv[h // group] += gv
     return dq, dk, dv
+
+
+def attention_varlen(q, k, v, cu_seqlens, causal, scale):
+    """Attention over packed sequences of different lengths.
+
+    [P2] "What It Changes--and What It Does Not" (variable-length paths) and
+    [P3] sections 8-9 (pack sequences instead of padding them): sequence b
+    is rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of every head and attends
+    only within itself -- ``attention_gqa`` applied to each sequence's rows.
+    q: (H, total, d); k, v: (Hkv, total, d); cu_seqlens: B + 1 offsets.
+    Returns (O (H, total, d), L (H, total)) in fp64.
+    """
+    q = _f64(q)
+    n_h, total, _ = q.shape
+    out = np.zeros(q.shape[:2] + (v.shape[2],))
+    lse = np.zeros((n_h, total))
+    for b in range(len(cu_seqlens) - 1):
+        r0, r1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if r1 > r0:
+            o_b, l_b = attention_gqa(q[:, r0:r1], k[:, r0:r1], v[:, r0:r1], causal, scale)
+            out[:, r0:r1] = o_b
+            lse[:, r0:r1] = l_b
+    return out, lse

@@ -36,7 +36,7 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version", "fa_bwd",
                      "fa_bwd_workspace_bytes", "fa_bwd_tile", "fa_decode", "fa_decode_plan",
-                     "fa_decode_workspace_bytes", "fa_fwd_gqa", "fa_bwd_gqa"):
+                     "fa_decode_workspace_bytes", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_varlen"):
         assert required in names
 
 
@@ -322,3 +322,29 @@ def test_gqa_binding_rejects_bad_shapes(fa):
     k = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd(q, k, k)
+
+
+# ------------------------------------------------------------------ variable length
+
+VGOOD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, cu=A + 0x5000000,
+             B=3, H=4, Hkv=2, total=500, max_seqlen=300, d=128, causal=1, scale=0.1, dtype=1, stream=None)
+
+
+def vcall(fa, **over):
+    a = dict(VGOOD)
+    a.update(over)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["H"], a["Hkv"],
+                            a["total"], a["max_seqlen"], a["d"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu=0), 1), (dict(q=0), 1), (dict(lse=0), 1),
+    (dict(B=0), 2), (dict(total=0), 2), (dict(max_seqlen=0), 2), (dict(max_seqlen=501), 2), (dict(Hkv=3), 2),
+    (dict(dtype=0), 3), (dict(dtype=9), 3),
+    (dict(d=80), 4),
+    (dict(cu=A + 0x5000002), 5), (dict(v=A + 0x2000008), 5),
+    (dict(scale=float("inf")), 6),
+    (dict(o=A + 0x5000000 - 16), 8), (dict(lse=A + 0x1000000), 8), (dict(lse=A + 0x3000000 + 16), 8),
+])
+def test_varlen_validation_rejects_before_launch(fa, over, code):
+    assert vcall(fa, **over) == code

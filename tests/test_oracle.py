@@ -389,6 +389,47 @@ def test_gqa_one_group_is_multi_head():
             assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------- variable length
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_batched(causal):
+    """Equal lengths: the packed problem is the batched one with the batch
+    axis folded into the rows (torch fp64 SDPA per sequence)."""
+    H, B, n, d = 3, 4, 9, 8
+    q = rnd(700, (H, B * n, d))
+    k = rnd(701, (H, B * n, d))
+    v = rnd(702, (H, B * n, d))
+    cu = np.arange(B + 1) * n
+    o, lse = oracle.attention_varlen(q, k, v, cu, causal, 0.4)
+    for b in range(B):
+        sl = slice(b * n, (b + 1) * n)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[:, sl]), torch.from_numpy(k[:, sl]), torch.from_numpy(v[:, sl]),
+            is_causal=causal, scale=0.4).numpy()
+        assert np.max(np.abs(o[:, sl] - ref)) < 1e-12
+
+
+def test_varlen_sequences_are_independent():
+    """Changing the keys and values of one sequence leaves every other
+    sequence's output bit-identical; empty sequences are allowed."""
+    H, d = 2, 4
+    cu = np.array([0, 5, 5, 12, 13])
+    total = cu[-1]
+    q, k, v = (rnd(710 + i, (H, total, d)) for i in range(3))
+    o1, l1 = oracle.attention_varlen(q, k, v, cu, True, 0.9)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 5:12] += 1.0
+    v2[:, 5:12] -= 2.0
+    o2, l2 = oracle.attention_varlen(q, k2, v2, cu, True, 0.9)
+    for sl in (slice(0, 5), slice(12, 13)):
+        assert np.array_equal(o1[:, sl], o2[:, sl]) and np.array_equal(l1[:, sl], l2[:, sl])
+    assert np.max(np.abs(o1[:, 5:12] - o2[:, 5:12])) > 0.1
+    # a sequence of one row sees only itself: o = v, L = scale q.k
+    assert np.allclose(o1[:, 12], v[:, 12], atol=1e-15)
+    assert np.allclose(l1[:, 12], 0.9 * np.sum(q[:, 12] * k[:, 12], axis=-1), atol=1e-14)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 

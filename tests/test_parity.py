@@ -329,3 +329,61 @@ def test_f16_large_scores(fa, scale):
     """Scores of |scale| * q.k up to ~30: probabilities above the fp16 range
     must send the tile through the exact update (the overflow check)."""
     assert_close(run_case(fa, 1910 + int(scale * 10), 1, 2, 1000, 128, "f16", True, scale=scale), "f16")
+
+
+# ------------------------------------------------------------ variable length
+
+
+def varlen_case(fa, cid, lengths, H, Hkv, d, dtype, causal, scale=None, check_rows=None):
+    """Packs seeded sequences of the given lengths ([H][total][d]), runs
+    fa_fwd_varlen and compares with oracle.attention_varlen."""
+    import torch
+
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    st = {"q": synthetic.full_storage(cid, "q", 1, H, total, d, dtype)[0],
+          "k": synthetic.full_storage(cid, "k", 1, Hkv, total, d, dtype)[0],
+          "v": synthetic.full_storage(cid, "v", 1, Hkv, total, d, dtype)[0]}
+    q, k, v = (to_device(np.ascontiguousarray(st[t]), dtype) for t in ("q", "k", "v"))
+    cu_d = torch.from_numpy(cu).cuda()
+    o, lse = fa.fwd_varlen(q, k, v, cu_d, int(max(lengths)), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.attention_varlen(*(values(st[t], dtype) for t in ("q", "k", "v")), cu, causal, scale)
+    got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+    return float(np.max(np.abs(got_o - ref_o))), float(np.max(np.abs(got_l - ref_l)))
+
+
+@pytest.mark.parametrize("lengths", [[1], [300], [5, 0, 130, 64, 1, 257], [1000, 17, 513], [64] * 7,
+                                     [2048, 1, 700]])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_bf16(fa, lengths, d, causal):
+    cid = 1950 + len(lengths) * 8 + (d == 128) * 2 + causal
+    assert_close(varlen_case(fa, cid, lengths, 4, 2, d, "bf16", causal), "bf16")
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_varlen_head_dims(fa, d):
+    assert_close(varlen_case(fa, 1980 + d, [77, 300, 0, 129], 2, 2, d, "bf16", True), "bf16")
+
+
+def test_varlen_f16(fa):
+    assert_close(varlen_case(fa, 1990, [400, 33, 1100], 4, 1, 128, "f16", True), "f16")
+
+
+def test_varlen_matches_fixed_length(fa):
+    """Equal lengths: the packed call and the batched call give the same
+    bits (same kernel, same tiles; only the addressing differs)."""
+    import torch
+
+    B, H, N, d = 3, 4, 320, 128
+    st = {t: synthetic.full_storage(1995, t, B, H, N, d, "bf16") for t in ("q", "k", "v")}
+    q, k, v = (to_device(st[t], "bf16") for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    pack = lambda x: x.permute(1, 0, 2, 3).reshape(H, B * N, d).contiguous()
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    o2, l2 = fa.fwd_varlen(pack(q), pack(k), pack(v), cu, N, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pack(o).view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.permute(1, 0, 2).reshape(H, B * N), l2)
