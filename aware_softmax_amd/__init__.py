@@ -81,7 +81,7 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_tile.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     lib.fa_bwd_tile.restype = ci
-    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
     lib.fa_decode.restype = ci
     lib.fa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
                                    ctypes.POINTER(sz)]
@@ -271,19 +271,21 @@ def decode_workspace_bytes(B, H, Hkv, N, d, num_splits=0) -> int:
     return int(_LIB.fa_decode_workspace_bytes(int(B), int(H), int(Hkv), int(N), int(d), int(num_splits)))
 
 
-def fa_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, ws_ptr, ws_bytes, B, H, Hkv, N, d, scale, num_splits, dtype,
-              stream) -> int:
+def fa_decode(q_ptr, k_ptr, v_ptr, seqlens_ptr, o_ptr, lse_ptr, ws_ptr, ws_bytes, B, H, Hkv, N, d, scale,
+              num_splits, dtype, stream) -> int:
     """Raw call of the C entry point with integer device addresses; returns
     the fa_status_t code."""
-    return _LIB.fa_decode(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, ws_ptr, int(ws_bytes), int(B), int(H), int(Hkv),
-                          int(N), int(d), float(scale), int(num_splits), int(dtype), stream)
+    return _LIB.fa_decode(q_ptr, k_ptr, v_ptr, seqlens_ptr, o_ptr, lse_ptr, ws_ptr, int(ws_bytes), int(B), int(H),
+                          int(Hkv), int(N), int(d), float(scale), int(num_splits), int(dtype), stream)
 
 
 def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, lse=None, workspace=None,
-           stream=None):
+           stream=None, cache_seqlens=None):
     """Split-K decode attention: q [B, H, d] against a cache k, v
     [B, Hkv, N, d] (bf16 or fp16 device tensors, H a multiple of Hkv).
 
+    cache_seqlens (optional int32 device tensor [B]): sequence b attends to
+    the first cache_seqlens[b] rows of its cache (default: all N).
     Returns (o [B, H, d] like q, lse [B, H] float32).  num_splits = 0 lets the
     library choose; 1 runs the unsplit kernel.  out / lse / workspace (uint8,
     at least decode_plan(...)[2] bytes) may be passed to reuse buffers.
@@ -322,9 +324,16 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    seq_ptr = None
+    if cache_seqlens is not None:
+        if (cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (B,) or not cache_seqlens.is_cuda
+                or not cache_seqlens.is_contiguous()):
+            raise ValueError("cache_seqlens must be a contiguous int32 device tensor of shape [B]")
+        seq_ptr = cache_seqlens.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+    _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_ptr, out.data_ptr(), lse.data_ptr(),
+                     workspace.data_ptr(),
                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits,
                      dtypes[q.dtype], stream.cuda_stream))
     return out, lse

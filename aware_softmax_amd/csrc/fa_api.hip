@@ -259,27 +259,28 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
   return fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &ws) == FA_OK ? ws : 0;
 }
 
-fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-                      size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
-                      fa_dtype_t dtype, hipStream_t stream) {
+fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                      int num_splits, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   size_t need = 0;
   const fa_status_t st = fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &need);
   if (st != FA_OK) return st;
   if (!is_16bit(dtype)) return FA_ERR_DTYPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 ||
+      (((uintptr_t)lse | (uintptr_t)cache_seqlens) & 3u) != 0)
     return FA_ERR_ALIGN;
   if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
   const size_t qb = (size_t)B * H * d * 2;
   const size_t kb = (size_t)B * Hkv * N * d * 2;
   const size_t lb = (size_t)B * H * sizeof(float);
-  const void* ins[3] = {q, k, v};
-  const size_t in_bytes[3] = {qb, kb, kb};
+  const void* ins[4] = {q, k, v, cache_seqlens};
+  const size_t in_bytes[4] = {qb, kb, kb, cache_seqlens ? (size_t)B * sizeof(int) : 0};
   void* outs[3] = {o, lse, workspace};
   const size_t out_bytes[3] = {qb, lb, need};
   for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 3; ++b)
+    for (int b = 0; b < 4; ++b)
       if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
     for (int b = a + 1; b < 3; ++b)
       if (ranges_overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
@@ -289,6 +290,7 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, floa
   p.q = q;
   p.k = k;
   p.v = v;
+  p.seqlens = cache_seqlens;
   p.o = o;
   p.lse = lse;
   p.workspace = workspace;

@@ -128,7 +128,7 @@ __device__ __forceinline__ float row_sum(float x) {
 //                      scaled scores (c = scale * log2 e folded in).
 template <class T, int D, int G>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int* __restrict__ seqlens,
     float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c) {
   constexpr int LPR = Shape<D>::LPR;
   constexpr int RPI = Shape<D>::RPI;
@@ -174,8 +174,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     for (int e = 0; e < E; ++e) o[i][e] = 0.f;
   }
 
+  // Keys of sequence b: the first seqlens[b] rows of the cache (clamped to
+  // [0, N]), all N without seqlens.  A split past the end has no keys and
+  // writes the empty partial (m = -inf, l = 0, o~ = 0).
+  const int n_b = seqlens ? min(max(seqlens[b], 0), N) : N;
   const int k_begin = s * chunk;
-  const int k_end = min(N, k_begin + chunk);
+  const int k_end = min(n_b, k_begin + chunk);
   const size_t head_off = (size_t)bhk * N * D;
   const T* kh = k + head_off + cc * 8;
   const T* vh = v + head_off + cc * 8;
@@ -292,10 +296,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     float mm = kNegInf;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][i]);
+    const float mref = mm == kNegInf ? 0.f : mm;  // -inf: the split has no key
     float ll = 0.f, oo = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(sm_m[w][i] - mm);  // mm is finite: the split has a key
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w][i] - mref);
       ll = fmaf(wt, sm_l[w][i], ll);
       oo = fmaf(wt, sm_o[w][i][e], oo);
     }
@@ -322,15 +327,17 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   float mm = -__builtin_inff();
 #pragma unroll 8
   for (int s = 0; s < S; ++s) mm = fmaxf(mm, ml[2 * s]);
+  const float mref = mm == -__builtin_inff() ? 0.f : mm;  // -inf: the sequence has no key
   float ll = 0.f, oo = 0.f;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mm);
+    const float wt = __builtin_amdgcn_exp2f(ml[2 * s] - mref);
     ll = fmaf(wt, ml[2 * s + 1], ll);
     oo = fmaf(wt, po[(size_t)s * D], oo);
   }
-  o[(size_t)bh * D + e] = (T)(oo / ll);
-  if (e == 0) lse[bh] = (mm + __builtin_amdgcn_logf(ll)) * kLn2;
+  // No key at all: o = 0 and lse = -inf (an empty softmax row).
+  o[(size_t)bh * D + e] = (T)(ll > 0.f ? oo / ll : 0.f);
+  if (e == 0) lse[bh] = ll > 0.f ? (mm + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
 }
 
 // Largest divisor of the query-head group that one workgroup serves.
@@ -370,7 +377,7 @@ hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t s
   float* po = (float*)p.workspace;
   float* pml = (float*)((char*)p.workspace + plan.ml_offset);
   hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(plan.split_wgs), dim3(kThreads), 0, stream,
-                     (const T*)p.q, (const T*)p.k, (const T*)p.v, po, pml, p.H, p.Hkv, p.N,
+                     (const T*)p.q, (const T*)p.k, (const T*)p.v, p.seqlens, po, pml, p.H, p.Hkv, p.N,
                      plan.splits, plan.chunk, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -64,6 +64,7 @@ struct DecodeParams {
   const void* q;
   const void* k;
   const void* v;
+  const int* seqlens;  // device [B] keys per sequence, or null: all N
   void* o;
   float* lse;
   void* workspace;

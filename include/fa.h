@@ -245,7 +245,12 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
 /*
  * fa_decode -- split-K decode attention.
  *   q         [in]  device, [B][H][d] of dtype, 16-byte aligned.
- *   k, v      [in]  device, [B][Hkv][N][d] of dtype, 16-byte aligned.
+ *   k, v      [in]  device, [B][Hkv][N][d] of dtype, 16-byte aligned: a
+ *             cache of capacity N per sequence.
+ *   cache_seqlens [in] device, B int32, 4-byte aligned, or NULL: sequence
+ *             b attends to the first cache_seqlens[b] rows of its cache
+ *             (clamped to [0, N] on the device); NULL means all N.  A
+ *             sequence with no key gets o = 0 and lse = -inf.
  *   o         [out] device, [B][H][d] of dtype, 16-byte aligned.
  *   lse       [out] device, [B][H] float32, 4-byte aligned.
  *   workspace [scratch] device, at least fa_decode_workspace_bytes(...)
@@ -262,9 +267,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
  * (FA_ERR_ALIAS).  No atomics: results are deterministic for a given split.
  * Returns FA_OK or the first failed check.
  */
-fa_status_t fa_decode(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
-                      size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
-                      fa_dtype_t dtype, hipStream_t stream);
+fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o,
+                      float* lse, void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
+                      float scale, int num_splits, fa_dtype_t dtype, hipStream_t stream);
 
 /* Library version string, e.g. "0.1.0 gfx950" (static storage). */
 const char* fa_version(void);

@@ -257,13 +257,13 @@ def test_decode_plan_covers_keys(fa, seed):
 
 DW = A + 0x8000000
 DGOOD = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, ws=DW,
-             ws_bytes=1 << 20, B=1, H=4, Hkv=2, N=300, d=64, scale=0.125, splits=0, dtype=1, stream=None)
+             ws_bytes=1 << 20, B=1, H=4, Hkv=2, N=300, d=64, scale=0.125, splits=0, dtype=1, stream=None, sl=None)
 
 
 def dcall(fa, **over):
     a = dict(DGOOD)
     a.update(over)
-    return fa.fa_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["ws_bytes"], a["B"], a["H"],
+    return fa.fa_decode(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"], a["ws"], a["ws_bytes"], a["B"], a["H"],
                         a["Hkv"], a["N"], a["d"], a["scale"], a["splits"], a["dtype"], a["stream"])
 
 
@@ -277,6 +277,7 @@ def dcall(fa, **over):
     (dict(scale=float("nan")), 6),
     (dict(o=A + 0x1000000), 8), (dict(lse=A + 0x3000010), 8), (dict(ws=A + 0x2000000), 8),
     (dict(ws=0), 9), (dict(ws=DW + 64), 9), (dict(ws_bytes=100), 9),
+    (dict(sl=A + 0x6000002), 5), (dict(sl=A + 0x3000000), 8), (dict(o=A + 0x6000000 - 64, sl=A + 0x6000000), 8),
 ])
 def test_decode_validation_rejects_before_launch(fa, over, code):
     assert dcall(fa, **over) == code

@@ -199,3 +199,35 @@ def test_f16_decode(fa, n, d, heads):
 
 def test_f16_decode_long(fa):
     run(fa, 7990, 2, 32, 8, 32768, 128, dtype="f16", heads=synthetic.sample_heads(7990, 2, 32, 8))
+
+
+# ------------------------------------------------------------ per-sequence cache lengths
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 7])
+@pytest.mark.parametrize("d", [64, 128])
+def test_cache_seqlens(fa, num_splits, d):
+    """Sequence b attends to the first cache_seqlens[b] rows of its cache;
+    lengths 0 (o = 0, lse = -inf, the oracle's empty-row reading), 1, the
+    full capacity and values in between; splits past a sequence's end."""
+    import torch
+
+    B, H, Hkv, N = 6, 8, 2, 3000
+    lens = np.array([0, 1, N, 1234, 63, 2049], dtype=np.int32)
+    st = synthetic.decode_storage(7998 + d, B, H, Hkv, N, d)
+    q, k, v = (to_device(st[t]) for t in ("q", "k", "v"))
+    sl = torch.from_numpy(lens).cuda()
+    o, lse = fa.decode(q, k, v, num_splits=num_splits, cache_seqlens=sl)
+    torch.cuda.synchronize()
+    got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+    scale = 1.0 / math.sqrt(d)
+    for b in range(B):
+        n_b = int(lens[b])
+        for h in range(H):
+            if n_b == 0:
+                assert np.all(got_o[b, h] == 0) and got_l[b, h] == -np.inf
+                continue
+            ref_o, ref_l = oracle.naive_attention(vals(st["q"][b, h])[None, :], vals(st["k"][b, h // 4][:n_b]),
+                                                  vals(st["v"][b, h // 4][:n_b]), False, scale)
+            assert np.all(np.abs(got_o[b, h] - ref_o[0]) <= 2.0 ** -8 * np.abs(ref_o[0]) + 1e-4), (b, h)
+            assert abs(got_l[b, h] - ref_l[0]) <= 2e-4 * max(1.0, abs(ref_l[0])), (b, h)
