@@ -18,6 +18,9 @@ __all__ = [
     "fa_fwd_gqa",
     "fa_fwd_varlen",
     "fwd_varlen",
+    "bwd_varlen",
+    "fa_bwd_varlen",
+    "bwd_varlen_workspace_bytes",
     "fa_bwd_gqa",
     "bwd",
     "fa_bwd",
@@ -60,18 +63,22 @@ def _load() -> ctypes.CDLL:
             "(there is no non-HIP fallback)"
         )
     lib = ctypes.CDLL(LIB_PATH)
-    vp, ci = ctypes.c_void_p, ctypes.c_int
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd.restype = ci
     lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd_gqa.restype = ci
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_fwd_varlen.restype = ci
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ci,
+                                  ctypes.c_float, ci, vp]
+    lib.fa_bwd_varlen.restype = ci
+    lib.fa_bwd_varlen_workspace_bytes.argtypes = [ci, ci, ci]
+    lib.fa_bwd_varlen_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [ci]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd_tile.argtypes = [ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci), ctypes.POINTER(ci)]
     lib.fa_fwd_tile.restype = ci
-    sz = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
     lib.fa_bwd.restype = ci
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ctypes.c_float,
@@ -392,3 +399,58 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale:
                          cu_seqlens.data_ptr(), B, H, Hkv, total, max_seqlen, d, causal, scale, dtypes[q.dtype],
                          stream.cuda_stream))
     return out, lse
+
+
+def bwd_varlen_workspace_bytes(H, total, d) -> int:
+    return int(_LIB.fa_bwd_varlen_workspace_bytes(int(H), int(total), int(d)))
+
+
+def fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, cu_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr, ws_bytes, B,
+                  H, Hkv, total, max_seqlen, d, causal, scale, dtype, stream) -> int:
+    """Raw call of the C entry point with integer device addresses."""
+    return _LIB.fa_bwd_varlen(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, cu_ptr, dq_ptr, dk_ptr, dv_ptr, ws_ptr,
+                              int(ws_bytes), int(B), int(H), int(Hkv), int(total), int(max_seqlen), int(d),
+                              int(bool(causal)), float(scale), int(dtype), stream)
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
+               dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of fwd_varlen (the same packed layouts and cu_seqlens)."""
+    import torch
+
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype} for varlen; use torch.bfloat16 or torch.float16")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [H, total, d] and k, v [Hkv, total, d]")
+    H, total, d = q.shape
+    Hkv = k.shape[0]
+    for name, t in (("o", o), ("do", do)):
+        if t.dtype != q.dtype or t.shape != q.shape:
+            raise ValueError(f"{name} must match q in dtype and shape")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype or t.shape != (Hkv, total, d):
+            raise ValueError(f"{name} must be [Hkv, total, d] with the dtype, total and d of q")
+    if lse.shape != (H, total) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [H, total] tensor")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse), ("cu_seqlens", cu_seqlens)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(k) if dv is None else dv
+    need = bwd_varlen_workspace_bytes(H, total, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                         cu_seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), B, H, Hkv, total, max_seqlen, d, causal,
+                         scale, dtypes[q.dtype], stream.cuda_stream))
+    return dq, dk, dv

@@ -239,6 +239,71 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                     dtype, stream);
 }
 
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d) {
+  if (H <= 0 || total <= 0 || (d != 64 && d != 128)) return 0;
+  if ((int64_t)H * total * d > ((int64_t)1 << 40) || total > INT_MAX - 128) return 0;
+  return fa::bwd_varlen_workspace_bytes(H, total, d);
+}
+
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, const int* cu_seqlens, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, int B, int H, int Hkv, int total, int max_seqlen, int d,
+                          int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !cu_seqlens || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || total <= 0 || max_seqlen <= 0 || d <= 0 || H % Hkv != 0)
+    return FA_ERR_SHAPE;
+  if (!is_16bit(dtype)) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX || max_seqlen > total || total > INT_MAX - 128) return FA_ERR_SHAPE;
+  const int64_t elems = (int64_t)H * total * d;
+  if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const int64_t nkb = ((int64_t)max_seqlen + fa::bwd_block_k() - 1) / fa::bwd_block_k();
+  if (bh * nkb * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+        (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t need = fa::bwd_varlen_workspace_bytes(H, total, d);
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = (size_t)elems * 2;
+  const size_t kvb = (size_t)Hkv * total * d * 2;
+  const size_t lb = (size_t)H * total * sizeof(float);
+  const void* ins[7] = {q, k, v, o, dout, lse, cu_seqlens};
+  const size_t in_bytes[7] = {tb, kvb, kvb, tb, tb, lb, (size_t)(B + 1) * sizeof(int)};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_bytes[4] = {tb, kvb, kvb, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 7; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
+    for (int b = a + 1; b < 4; ++b)
+      if (ranges_overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.workspace = workspace;
+  p.BH = (int)bh;
+  p.N = max_seqlen;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.group = H / Hkv;
+  p.cu_seqlens = cu_seqlens;
+  p.H = H;
+  p.total = total;
+  const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f16(p, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, int* splits, int* chunk_keys,
                            size_t* workspace_bytes) {
   if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || num_splits < 0) return FA_ERR_SHAPE;

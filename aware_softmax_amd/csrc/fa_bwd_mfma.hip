@@ -83,6 +83,26 @@ constexpr int kBKdq = 64;     // bwd_dq: keys per streamed tile
 constexpr int kRing = 3;      // LDS buffers per streamed tensor
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Variable-length layout (cu set): B sequences packed into `total` rows per
+// head; q, o, dO, dQ [H][total][D], k, v, dK, dV [H / group][total][D],
+// L [H][total], workspace statistics [H][ld] (ld = total rounded up to 64,
+// plus 64, so that a 64-row statistics tile never leaves its head).
+// Sequence b is rows cu[b] .. cu[b + 1] - 1 (offsets clamped to
+// [0, total], so no access leaves the tensors whatever the array holds).
+// cu null: the fixed-length layouts [BH][N][D] and [BH][Npad].
+inline int varlen_ld(int total) { return (total + kBQ - 1) / kBQ * kBQ + kBQ; }
+
+struct VarLen {
+  const int* cu;
+  int H;
+  int total;
+  int ld;
+};
+__device__ __forceinline__ int seq_start(const VarLen& vl, int b) { return min(max(vl.cu[b], 0), vl.total); }
+__device__ __forceinline__ int seq_len(const VarLen& vl, int b, int r0) {
+  return min(max(vl.cu[b + 1], r0), vl.total) - r0;
+}
+
 // Calls fn(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
 template <class Fn, int... I>
 __device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, I...>) {
@@ -184,17 +204,22 @@ __device__ __forceinline__ void dma_rows(const T* X, int r0, int N, char* tile, 
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, const T* __restrict__ dOg,
                                                       const float* __restrict__ Lg, float* __restrict__ Lsg,
-                                                      float* __restrict__ Dng, int N, int Npad, float l_to_score) {
+                                                      float* __restrict__ Dng, int N, int Npad, float l_to_score,
+                                                      VarLen vl) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
   const int c = tid % LPR;
-  const size_t row = (size_t)blockIdx.x * RPB + tid / LPR;  // in [0, BH * Npad)
-  const int bh = (int)(row / Npad);
-  const int i = (int)(row % Npad);
+  const size_t row = (size_t)blockIdx.x * RPB + tid / LPR;  // in [0, BH * Npad), or [0, H * ld)
+  // fixed length: head bh, row i of N (padded to Npad); variable length:
+  // head bh, packed row i of total (padded to ld)
+  const int stride = vl.cu ? vl.ld : Npad;
+  const int rows = vl.cu ? vl.total : N;
+  const int bh = (int)(row / stride);
+  const int i = (int)(row % stride);
   float acc = 0.f;
-  if (i < N) {
-    const size_t off = ((size_t)bh * N + i) * D + c * 8;
+  if (i < rows) {
+    const size_t off = ((size_t)bh * rows + i) * D + c * 8;
     const vec8<T> a = *(const vec8<T>*)(Og + off);
     const vec8<T> b = *(const vec8<T>*)(dOg + off);
 #pragma unroll
@@ -204,7 +229,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, 
   for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
   if (c == 0) {
     Dng[row] = -acc;
-    Lsg[row] = i < N ? -Lg[(size_t)bh * N + i] * l_to_score : 0.f;
+    Lsg[row] = i < rows ? -Lg[(size_t)bh * rows + i] * l_to_score : 0.f;
   }
 }
 
@@ -234,7 +259,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                      const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
                      T* __restrict__ dKg, T* __restrict__ dVg, int BHkv, int N, int Npad, int nkb, float c,
-                     float scale, int group) {
+                     float scale, int group, VarLen vl) {
   using Ly = DkdvLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -258,9 +283,31 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   int bhk, jb;
   map_block(blockIdx.x, BHkv * nkb, nkb, false, &bhk, &jb);  // key block 0 (the most query tiles) first
   const int kb0 = jb * kBKV;
+  // Rows of this key/value head (and sequence): `head` is the element
+  // offset of its K/V row 0; query head r of the group has Q/dO row 0 at
+  // q_off(r) and statistics row 0 at st_off(r).
+  size_t head;
+  int hk = bhk, r0 = 0;
+  if (vl.cu) {
+    const int n_kv = vl.H / group;
+    const int b = bhk / n_kv;
+    hk = bhk - b * n_kv;
+    r0 = seq_start(vl, b);
+    N = seq_len(vl, b, r0);
+    if (kb0 >= N) return;  // past the end of this sequence (the whole workgroup)
+    Npad = (N + kBQ - 1) / kBQ * kBQ;
+    head = ((size_t)hk * vl.total + r0) * D;
+  } else {
+    head = (size_t)bhk * (size_t)N * D;
+  }
+  auto q_off = [&](int r) -> size_t {
+    return vl.cu ? ((size_t)(hk * group + r) * vl.total + r0) * D : (size_t)(bhk * group + r) * (size_t)N * D;
+  };
+  auto st_off = [&](int r) -> size_t {
+    return vl.cu ? (size_t)(hk * group + r) * vl.ld + r0 : (size_t)(bhk * group + r) * Npad;
+  };
   const int kw0 = kb0 + 32 * wave;  // first key of this wave
   const int key = kw0 + col;        // this lane's key (MFMA column)
-  const size_t head = (size_t)bhk * (size_t)N * D;
   const T* Kh = Kg + head;
   const T* Vh = Vg + head;
 
@@ -288,12 +335,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
     const int b = ring(v);
     const int r = __builtin_amdgcn_readfirstlane(v / span);
     const int it = it0 + v - r * span;
-    const int bh = bhk * group + r;
-    const size_t qhead = (size_t)bh * (size_t)N * D;
+    const size_t qhead = q_off(r);
     // the tile's 64 statistics: -L/scale by waves 0 and 2, -D by waves 1
     // and 3 (the duplicate copy writes the same bytes; it keeps the number
     // of DMA instructions per wave uniform for the waits)
-    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dng : Lsg) + (size_t)bh * Npad + it * kBQ + lane),
+    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dng : Lsg) + st_off(r) + it * kBQ + lane),
                                      (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + (wave & 1) * 4 * kBQ), 4, 0, 0);
     dma_rows<D, kBQ>(Qg + qhead, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
     dma_rows<D, kBQ>(dOg + qhead, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
@@ -515,7 +561,8 @@ template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                    const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
-                   T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group) {
+                   T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group,
+                   VarLen vl) {
   using Ly = DqLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -536,10 +583,25 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);  // causal: the longest blocks first
   const int q0 = qb * kBQdq;
+  // Rows of query head bh (and its sequence): Q/dO/dQ row 0 at `head`, the
+  // K/V rows of its key/value head at `kvhead`, statistics row 0 at `st`.
+  size_t head, kvhead, st;
+  if (vl.cu) {
+    const int b = bh / vl.H, h = bh - b * vl.H;
+    const int r0 = seq_start(vl, b);
+    N = seq_len(vl, b, r0);
+    if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
+    Npad = (N + kBQ - 1) / kBQ * kBQ;
+    head = ((size_t)h * vl.total + r0) * D;
+    kvhead = ((size_t)(h / group) * vl.total + r0) * D;
+    st = (size_t)h * vl.ld + r0;
+  } else {
+    head = (size_t)bh * (size_t)N * D;
+    kvhead = (size_t)(bh / group) * (size_t)N * D;  // key/value head of query head bh
+    st = (size_t)bh * Npad;
+  }
   const int qw = q0 + 32 * wave;
   const int qi = qw + col;  // this lane's query (MFMA column)
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const size_t kvhead = (size_t)(bh / group) * (size_t)N * D;  // key/value head of query head bh
   const T* Qh = Qg + head;
   const T* Kh = Kg + kvhead;
   const T* Vh = Vg + kvhead;
@@ -557,8 +619,8 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
     }
   }
   const int qs = min(qi, Npad - 1);
-  const float ls = Lsg[(size_t)bh * Npad + qs];  // -L / scale
-  const float dn = Dng[(size_t)bh * Npad + qs];  // -D
+  const float ls = Lsg[st + qs];  // -L / scale
+  const float dn = Dng[st + qs];  // -D
 
   int nkt = (N + kBKdq - 1) / kBKdq;
   if (CAUSAL) nkt = min(nkt, (q0 + kBQdq - 1) / kBKdq + 1);
@@ -721,23 +783,26 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
 
 template <class T, int D>
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  // Fixed length: statistics [BH][npad]; variable length: [H][ld].
   const int npad = (p.N + kBQ - 1) / kBQ * kBQ;
+  VarLen vl{p.cu_seqlens, p.H, p.total, p.cu_seqlens ? varlen_ld(p.total) : 0};
+  const size_t stat_rows = p.cu_seqlens ? (size_t)p.H * vl.ld : (size_t)p.BH * npad;
   // P = 2^(c (q.k - L / scale)) with c = scale log2(e).  |c| is kept at
   // least 1e-30 so that L / scale stays finite; below that every
   // c q.k rounds to 0 anyway and P = e^-L as for scale = 0.
   float c = p.scale * kLog2e;
   if (fabsf(c) < 1e-30f) c = c < 0.f ? -1e-30f : 1e-30f;
   float* ls = (float*)p.workspace;
-  float* dn = ls + (size_t)p.BH * npad;
+  float* dn = ls + stat_rows;
   const T* q = (const T*)p.q;
   const T* k = (const T*)p.k;
   const T* v = (const T*)p.v;
   const T* dout = (const T*)p.dout;
   {
     constexpr int RPB = 256 / (D / 8);
-    const size_t rows = (size_t)p.BH * npad;  // a multiple of RPB
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)(rows / RPB)), dim3(256), 0, stream, (const T*)p.o,
-                       dout, p.lse, ls, dn, p.N, npad, kLog2e / c);
+    static_assert(kBQ % RPB == 0, "statistics rows split evenly over the pre kernel's workgroups");
+    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)(stat_rows / RPB)), dim3(256), 0, stream,
+                       (const T*)p.o, dout, p.lse, ls, dn, p.N, npad, kLog2e / c, vl);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -747,10 +812,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)(bhkv * nkb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
-                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
-                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group);
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -759,10 +824,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const dim3 grid((unsigned)(p.BH * nqb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dq,
-                         p.BH, p.N, npad, nqb, c, p.scale, p.group);
+                         p.BH, p.N, npad, nqb, c, p.scale, p.group, vl);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<T, D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dq,
-                         p.BH, p.N, npad, nqb, c, p.scale, p.group);
+                         p.BH, p.N, npad, nqb, c, p.scale, p.group, vl);
     return hipGetLastError();
   }
 }
@@ -773,6 +838,11 @@ size_t bwd_workspace_bytes(int BH, int N, int d) {
   (void)d;
   const size_t npad = ((size_t)N + kBQ - 1) / kBQ * kBQ;
   return (size_t)BH * npad * 2 * sizeof(float);
+}
+
+size_t bwd_varlen_workspace_bytes(int H, int total, int d) {
+  (void)d;
+  return (size_t)H * varlen_ld(total) * 2 * sizeof(float);
 }
 
 int bwd_block_k() { return kBKV; }

@@ -56,6 +56,13 @@ struct BwdParams {
   int causal;
   float scale;
   int group;        // query heads per key/value head; k, v, dk, dv are [B][H / group][N][d]
+  // Variable length: cu_seqlens (device, B + 1 ints) set, N = the longest
+  // sequence, BH = B * H; every tensor is packed per head ([H][total][d],
+  // [H / group][total][d], lse [H][total]); workspace
+  // bwd_varlen_workspace_bytes(H, total, d).
+  const int* cu_seqlens = nullptr;
+  int H = 0;
+  int total = 0;
 };
 
 // Everything a split-K decode launch needs: q, o [B][H][d]; k, v
@@ -105,6 +112,7 @@ hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream);
 // Backward workspace: -L/scale and -D, fp32 [BH][Npad] each; Npad = N
 // rounded up to the query tile of the dK/dV pass.
 size_t bwd_workspace_bytes(int BH, int N, int d);
+size_t bwd_varlen_workspace_bytes(int H, int total, int d);  // -L/scale and -D, fp32 [H][ld] each
 int bwd_block_k();  // keys per workgroup of the dK/dV pass
 int bwd_block_q();  // queries per streamed tile of the dK/dV pass
 

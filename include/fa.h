@@ -202,6 +202,28 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
                        hipStream_t stream);
 
 /*
+ * fa_bwd_varlen_workspace_bytes -- the workspace of fa_bwd_varlen: two
+ * fp32 [H][ld] row vectors, ld = total rounded up to 64, plus 64.  Host-only;
+ * 0 for invalid sizes.
+ */
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d);
+
+/*
+ * fa_bwd_varlen -- the backward of fa_fwd_varlen (same packed layouts,
+ * cu_seqlens and max_seqlen): q, o, dout, dq [H][total][d]; k, v, dk, dv
+ * [Hkv][total][d]; lse [H][total]; every sequence's gradients depend only
+ * on its own rows.  workspace: at least fa_bwd_varlen_workspace_bytes(H,
+ * total, d) bytes, 256-byte aligned.  dtype FA_DTYPE_BF16 or FA_DTYPE_F16;
+ * d 64 or 128; the other arguments and the checks as for fa_bwd_gqa and
+ * fa_fwd_varlen (cu_seqlens clamped to [0, total] on the device).
+ */
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, const int* cu_seqlens, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int total,
+                          int max_seqlen, int d, int causal, float scale, fa_dtype_t dtype,
+                          hipStream_t stream);
+
+/*
  * fa_bwd_tile -- keys per workgroup of the dK/dV pass and queries per
  * streamed tile of it.  Host-only.  Returns FA_OK or FA_ERR_NULL /
  * FA_ERR_UNSUPPORTED_HEADDIM.

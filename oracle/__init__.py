@@ -7,6 +7,7 @@ from .attention import (  # noqa: F401
     attention_batched,
     attention_bwd,
     attention_bwd_gqa,
+    attention_bwd_varlen,
     attention_gqa,
     attention_varlen,
     attention_from_scores,

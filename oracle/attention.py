@@ -62,6 +62,7 @@ __all__ = [
     "attention_gqa",
     "attention_bwd_gqa",
     "attention_varlen",
+    "attention_bwd_varlen",
 ]
 
 
@@ -340,3 +341,25 @@ def attention_varlen(q, k, v, cu_seqlens, causal, scale):
             out[:, r0:r1] = o_b
             lse[:, r0:r1] = l_b
     return out, lse
+
+
+def attention_bwd_varlen(q, k, v, do, cu_seqlens, causal, scale):
+    """Gradients of ``attention_varlen``: each sequence's rows get the
+    gradients of their own attention (``attention_bwd_gqa``); rows of
+    different sequences never interact.  Returns (dQ, dK, dV) in fp64 with
+    the shapes of q, k, v."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(len(cu_seqlens) - 1):
+        r0, r1 = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if r1 > r0:
+            gq, gk, gv = attention_bwd_gqa(q[:, r0:r1], k[:, r0:r1], v[:, r0:r1], do[:, r0:r1], causal, scale)
+            dq[:, r0:r1] = gq
+            dk[:, r0:r1] = gk
+            dv[:, r0:r1] = gv
+    return dq, dk, dv

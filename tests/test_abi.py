@@ -36,7 +36,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     for required in ("fa_fwd", "fa_status_string", "fa_fwd_tile", "fa_version", "fa_bwd",
                      "fa_bwd_workspace_bytes", "fa_bwd_tile", "fa_decode", "fa_decode_plan",
-                     "fa_decode_workspace_bytes", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_varlen"):
+                     "fa_decode_workspace_bytes", "fa_fwd_gqa", "fa_bwd_gqa", "fa_fwd_varlen",
+                     "fa_bwd_varlen", "fa_bwd_varlen_workspace_bytes"):
         assert required in names
 
 
@@ -349,3 +350,24 @@ def vcall(fa, **over):
 ])
 def test_varlen_validation_rejects_before_launch(fa, over, code):
     assert vcall(fa, **over) == code
+
+
+def test_bwd_varlen_workspace_and_validation(fa):
+    # two fp32 [H][ld] vectors, ld = total rounded up to 64, plus 64
+    assert fa.bwd_varlen_workspace_bytes(4, 500, 128) == 4 * (512 + 64) * 2 * 4
+    assert fa.bwd_varlen_workspace_bytes(4, 500, 96) == 0
+    W2 = A + 0x9000000
+    args = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, do=A + 0x5000000,
+                cu=A + 0x6000000, dq=A + 0x6100000, dk=A + 0x7000000, dv=A + 0x8000000, ws=W2, ws_bytes=1 << 20,
+                B=3, H=4, Hkv=2, total=500, mx=300, d=128, causal=1, scale=0.1, dtype=1)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["cu"], a["dq"], a["dk"],
+                                a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["Hkv"], a["total"], a["mx"],
+                                a["d"], a["causal"], a["scale"], a["dtype"], None)
+    for over, code in ((dict(cu=0), 1), (dict(mx=501), 2), (dict(Hkv=3), 2), (dict(dtype=0), 3), (dict(d=96), 4),
+                       (dict(cu=A + 0x6000001), 5), (dict(ws_bytes=100), 9), (dict(dq=A + 0x6000000 - 16), 8),
+                       (dict(ws=A), 8)):
+        assert call(**over) == code, over

@@ -430,6 +430,35 @@ def test_varlen_sequences_are_independent():
     assert np.allclose(l1[:, 12], 0.9 * np.sum(q[:, 12] * k[:, 12], axis=-1), atol=1e-14)
 
 
+def test_varlen_bwd_finite_differences():
+    """Central differences of f = sum <O, dO> over packed sequences (one of
+    them empty): gradients stay inside each sequence."""
+    H, Hkv, d = 2, 1, 3
+    cu = np.array([0, 4, 4, 9])
+    total = cu[-1]
+    q = rnd(720, (H, total, d))
+    k = rnd(721, (Hkv, total, d))
+    v = rnd(722, (Hkv, total, d))
+    do = rnd(723, (H, total, d))
+    dq, dk, dv = oracle.attention_bwd_varlen(q, k, v, do, cu, True, 0.8)
+
+    def f(qq, kk, vv):
+        o, _ = oracle.attention_varlen(qq, kk, vv, cu, True, 0.8)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for grad, which in ((dq, 0), (dk, 1), (dv, 2)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            fp = f(*args)
+            args[which][idx] -= 2 * h
+            fm = f(*args)
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - grad)) < 1e-7
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 
