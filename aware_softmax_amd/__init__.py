@@ -33,6 +33,7 @@ __all__ = [
     "tile_config",
     "version",
     "status_string",
+    "last_hip_error",
     "library",
     "LIB_PATH",
     "DTYPE_F32",
@@ -57,6 +58,15 @@ class FaError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # One HIP runtime per process: torch bundles its own libamdhip64.so.7,
+    # and libfa.so, loaded first, would pull in the system copy next to it;
+    # kernels launched through the second runtime then fail (it reports no
+    # device).  Loading torch first lets libfa.so bind to the runtime already
+    # loaded under the same soname.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python aware_softmax_amd/build.py` "
@@ -95,6 +105,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_decode_plan.restype = ci
     lib.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
+    lib.fa_last_hip_error.restype = ci
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
     return lib
@@ -115,9 +127,20 @@ def version() -> str:
     return _LIB.fa_version().decode()
 
 
+def last_hip_error() -> tuple:
+    """(hipError_t code, message) behind the last FA_ERR_HIP on this thread."""
+    msg = ctypes.c_char_p()
+    code = _LIB.fa_last_hip_error(ctypes.byref(msg))
+    return code, (msg.value or b"").decode()
+
+
 def _check(code: int) -> None:
     if code != FA_OK:
-        raise FaError(code, status_string(code))
+        message = status_string(code)
+        if code == 7:  # FA_ERR_HIP: add what the runtime reported
+            hip_code, hip_msg = last_hip_error()
+            message += f" (hipError_t {hip_code}: {hip_msg})"
+        raise FaError(code, message)
 
 
 def tile_config(d: int, dtype: int) -> tuple:

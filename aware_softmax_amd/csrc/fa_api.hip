@@ -14,6 +14,15 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// The hipError_t behind the last FA_ERR_HIP returned on this thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+fa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = e;
+  return FA_ERR_HIP;
+}
+
 // A launch's work-items in x must fit in 32 bits.
 constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
@@ -48,7 +57,12 @@ const char* fa_status_string(fa_status_t status) {
   return "unknown fa_status_t";
 }
 
-const char* fa_version(void) { return "0.3.0 gfx950"; }
+const char* fa_version(void) { return "0.4.0 gfx950"; }
+
+int fa_last_hip_error(const char** message) {
+  if (message) *message = hipGetErrorString(g_last_hip_error);
+  return (int)g_last_hip_error;
+}
 
 fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves) {
   if (!block_q || !block_k || !waves) return FA_ERR_NULL;
@@ -102,7 +116,7 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
   const hipError_t e = dtype == FA_DTYPE_BF16  ? fa::launch_fwd_bf16(p, stream)
                        : dtype == FA_DTYPE_F16 ? fa::launch_fwd_f16(p, stream)
                                                : fa::launch_fwd_f32(p, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return hip_status(e);
 }
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -159,7 +173,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   p.H = H;
   p.total = total;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(p, stream) : fa::launch_fwd_f16(p, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return hip_status(e);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -229,7 +243,7 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   p.scale = scale;
   p.group = H / Hkv;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f16(p, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return hip_status(e);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -301,7 +315,7 @@ fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const voi
   p.H = H;
   p.total = total;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f16(p, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return hip_status(e);
 }
 
 fa_status_t fa_decode_plan(int B, int H, int Hkv, int N, int d, int num_splits, int* splits, int* chunk_keys,
@@ -367,7 +381,7 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
   p.scale = scale;
   p.num_splits = num_splits;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_decode_bf16(p, stream) : fa::launch_decode_f16(p, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -256,6 +256,59 @@ def time_f16(fa, steps=10, warmup=2):
     return out
 
 
+def varlen_lengths(seed=0xFA0, B=16, lo=256, hi=8192):
+    """Seeded sequence lengths of a packed batch: log-uniform in [lo, hi]."""
+    import numpy as np
+
+    rng = np.random.Generator(np.random.PCG64([0xFA, 50, seed]))
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=B)).astype(np.int64)
+
+
+def time_varlen(fa, steps=10, warmup=2):
+    """Packed variable-length causal forward (16 sequences of seeded
+    log-uniform lengths in 256..8192, H32 d128 bf16) against the same
+    sequences padded to the longest one (fixed-length call on B16 Nmax);
+    TFLOP/s count only the sequences' own causal FLOPs in both."""
+    import numpy as np
+    import torch
+
+    lens = varlen_lengths()
+    total, nmax, B, H, d = int(lens.sum()), int(lens.max()), len(lens), 32, 128
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(0xFA51)
+    q, k, v = (torch.randn(H, total, d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    f = sum(attention_flops(1, H, int(n), d, True) for n in lens)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms_v = timed(lambda: fa.fwd_varlen(q, k, v, cu, nmax, causal=True, out=o, lse=lse))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    qp, kp, vp = (torch.randn(B, H, nmax, d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    op = torch.empty_like(qp)
+    lp = torch.empty((B, H, nmax), dtype=torch.float32, device=dev)
+    ms_p = timed(lambda: fa.fwd(qp, kp, vp, causal=True, out=op, lse=lp))
+    del qp, kp, vp, op, lp
+    torch.cuda.empty_cache()
+    label = f"causal bf16 varlen fwd B{B} H{H} d{d} total {total} (max {nmax})"
+    return {label: {"ms": round(ms_v, 4), "TFLOP/s": round(f / (ms_v * 1e-3) / 1e12, 2),
+                    "padded_ms": round(ms_p, 4), "padded_useful_TFLOP/s": round(f / (ms_p * 1e-3) / 1e12, 2),
+                    "inputs": "torch.randn seeded on the device (values do not affect the timing)"}}
+
+
 def decode_inputs(w, threads=16):
     import numpy as np
     import torch
@@ -477,6 +530,7 @@ def main():
             torch.cuda.empty_cache()
         extra.update(time_gqa(fa))
         extra.update(time_f16(fa))
+        extra.update(time_varlen(fa))
         for cid in (6, 7, 8):
             dw = synthetic.DECODE_WORKLOADS[cid]
             dq_, dk_, dv_ = decode_inputs(dw)

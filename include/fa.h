@@ -293,6 +293,13 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
                       float* lse, void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
                       float scale, int num_splits, fa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * fa_last_hip_error -- the hipError_t behind the last FA_ERR_HIP an entry
+ * point returned on the calling thread (0 if none), and, if message is not
+ * NULL, the runtime's description of it (static storage).  Host-only.
+ */
+int fa_last_hip_error(const char** message);
+
 /* Library version string, e.g. "0.1.0 gfx950" (static storage). */
 const char* fa_version(void);
 

@@ -371,3 +371,16 @@ def test_bwd_varlen_workspace_and_validation(fa):
                        (dict(cu=A + 0x6000001), 5), (dict(ws_bytes=100), 9), (dict(dq=A + 0x6000000 - 16), 8),
                        (dict(ws=A), 8)):
         assert call(**over) == code, over
+
+
+def test_single_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not load a second HIP
+    runtime next to torch's (launches through it fail with 'no device')."""
+    import sys
+
+    code = ("import aware_softmax_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
