@@ -29,10 +29,13 @@
 //             keys each; 64-query tiles of Q and dO (plus L, D) streamed
 //             through triple-buffered LDS; dK, dV in registers;
 //   bwd_dq    one workgroup per (head, 128-query block), 4 wave64s with 32
-//             queries each; 64-key tiles of K and V streamed through
-//             triple-buffered LDS; dQ in registers.
+//             queries each; 32-key tiles of K and V streamed through
+//             triple-buffered LDS (48 KB); dQ in registers.  At 242 VGPRs
+//             two workgroups share a CU (two waves per SIMD).
 //
-// MI355X mapping (v_mfma_f32_32x32x16_bf16 throughout, one wave per SIMD):
+// MI355X mapping (v_mfma_f32_32x32x16_bf16 throughout; one wave per SIMD in
+// bwd_dkdv, whose dK and dV accumulators take 128 registers per lane, two
+// in bwd_dq):
 //   * the MFMA accumulator layout that computes scores is directly the B
 //     operand of the next product: in bwd_dkdv S and dP have queries as rows
 //     and the wave's 32 keys as columns, so P and dS packed to bf16 feed
@@ -79,7 +82,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBKV = 128;     // bwd_dkdv: keys per workgroup (32 per wave)
 constexpr int kBQ = 64;       // bwd_dkdv: queries per streamed tile
 constexpr int kBQdq = 128;    // bwd_dq: queries per workgroup (32 per wave)
-constexpr int kBKdq = 64;     // bwd_dq: keys per streamed tile
+constexpr int kBKdq = 32;     // bwd_dq: keys per streamed tile
 constexpr int kRing = 3;      // LDS buffers per streamed tensor
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -551,14 +554,15 @@ struct DqLayout {
   static_assert(TOTAL <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
-// Per 64-key tile and wave (32 queries; lane = query, registers = keys):
+// Per key tile (32 keys here; the code takes any multiple of 32) and wave
+// (32 queries; lane = query, registers = keys):
 //   A  S^T = K Q^T - L/scale and dP^T = V dO^T - D  (4 DT MFMAs; row
 //      fragments of the K and V tiles; Q and dO fragments resident);
 //   V  P = 2^(c S^T), dS^T = P dP^T, packed to bf16;
 //   C  dQ^T += K^T dS^T                               (4 DB MFMAs, transposing reads).
 // Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                    const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
                    T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group,
@@ -567,11 +571,11 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
   constexpr int ROWB = Ly::ROWB;
-  constexpr int NA = 4 * DT;  // phase A MFMAs
+  constexpr int KB = kBKdq / 32;  // 32-key halves per tile
+  constexpr int NA = 2 * KB * DT;  // phase A MFMAs
   constexpr int LA = 4;
-  constexpr int NC = 4 * DB;  // phase C MFMAs
+  constexpr int NC = 2 * KB * DB;  // phase C MFMAs
   constexpr int LC = 4;
-  static_assert(NA % 8 == 0, "eight VALU groups ride on the phase A MFMAs");
   __shared__ __attribute__((aligned(1024))) char smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
@@ -632,9 +636,9 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
     dma_rows<D, kBKdq>(Vh, j * kBKdq, N, smem + Ly::OFF_V + b * Ly::KTILE, wave, lane);
   };
 
-  unsigned rf_lane[2];  // K / V row fragments: row 32 kb + col, chunk 2t + half
+  unsigned rf_lane[KB];  // K / V row fragments: row 32 kb + col, chunk 2t + half
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int r = 32 * kb + col;
     rf_lane[kb] = (unsigned)(r * ROWB + ((half ^ swz_mask<ROWB>(r)) << 4));
   }
@@ -655,8 +659,8 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   f32x16 dqT[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) dqT[b] = f32x16{};
-  f32x16 S[2], dP[2];  // [32-key half]
-  unsigned dw[2][8];
+  f32x16 S[KB], dP[KB];  // [32-key half]
+  unsigned dw[KB][8];
 
   // visible iff key <= qi (causal) and key < N: key <= hi_key
   const int hi_key = CAUSAL ? min(qi, N - 1) : N - 1;
@@ -688,7 +692,7 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
     const unsigned av = sbase + Ly::OFF_V + b * Ly::KTILE;
     {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           S[kb][r] = ls;
@@ -733,9 +737,9 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
         if constexpr (F + LC < NC) issue(ic<F + LC>{});
         // groups 2 (u + 1) and 2 (u + 1) + 1 ride on step u's MFMAs
         constexpr int f = F % DB;
-        if constexpr (u < 3 && DB >= 2 && (f == DB / 2 - 1 || f == DB - 1))
+        if constexpr (u < 2 * KB - 1 && DB >= 2 && (f == DB / 2 - 1 || f == DB - 1))
           vgroup(ic<2 * (u + 1) + (f == DB - 1 ? 1 : 0)>{}, mask_c, j);
-        if constexpr (u < 3 && DB == 1) {
+        if constexpr (u < 2 * KB - 1 && DB == 1) {
           vgroup(ic<2 * (u + 1)>{}, mask_c, j);
           vgroup(ic<2 * (u + 1) + 1>{}, mask_c, j);
         }
