@@ -556,10 +556,11 @@ struct DqLayout {
 
 // Per key tile (32 keys here; the code takes any multiple of 32) and wave
 // (32 queries; lane = query, registers = keys):
-//   A  S^T = K Q^T - L/scale and dP^T = V dO^T - D  (4 DT MFMAs; row
-//      fragments of the K and V tiles; Q and dO fragments resident);
-//   V  P = 2^(c S^T), dS^T = P dP^T, packed to bf16;
-//   C  dQ^T += K^T dS^T                               (4 DB MFMAs, transposing reads).
+//   A  S^T = K Q^T - L/scale and dP^T = V dO^T - D  (2 KB DT MFMAs, KB =
+//      32-key halves per tile; row fragments of the K and V tiles; Q and
+//      dO fragments resident);
+//   V  P = 2^(c S^T), dS^T = P dP^T, packed to the element type;
+//   C  dQ^T += K^T dS^T                               (2 KB DB MFMAs, transposing reads).
 // Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
