@@ -32,6 +32,8 @@ __all__ = [
     "decode_workspace_bytes",
     "tile_config",
     "version",
+    "mfma_ceiling",
+    "MFMA_CEILING_FLOP_PER_ITER_BLOCK",
     "status_string",
     "last_hip_error",
     "library",
@@ -107,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
     lib.fa_last_hip_error.restype = ci
+    lib.fa_mfma_ceiling.argtypes = [vp, ci, ci, ci, vp]
+    lib.fa_mfma_ceiling.restype = ci
     lib.fa_version.argtypes = []
     lib.fa_version.restype = ctypes.c_char_p
     return lib
@@ -294,6 +298,23 @@ def decode_plan(B, H, Hkv, N, d, num_splits=0) -> tuple:
     _check(_LIB.fa_decode_plan(int(B), int(H), int(Hkv), int(N), int(d), int(num_splits), ctypes.byref(sp),
                                ctypes.byref(ck), ctypes.byref(ws)))
     return sp.value, ck.value, ws.value
+
+
+# FLOPs of one loop iteration of one fa_mfma_ceiling workgroup: 4 waves x 4
+# MFMA 32x32x16 x 32768 FLOP.
+MFMA_CEILING_FLOP_PER_ITER_BLOCK = 4 * 4 * 32768
+
+
+def mfma_ceiling(sink, iters: int, blocks: int, store: bool = False, stream=None) -> None:
+    """Enqueue the matrix-core-only ceiling kernel (a measurement helper):
+    `blocks` workgroups each run `iters` iterations of 16 bf16 MFMAs;
+    `sink` is an fp32 device tensor of at least blocks * 256 elements."""
+    import torch
+
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() < blocks * 256:
+        raise ValueError("sink must be an fp32 device tensor of blocks * 256 elements")
+    stream = stream or torch.cuda.current_stream(sink.device)
+    _check(_LIB.fa_mfma_ceiling(sink.data_ptr(), int(iters), int(blocks), int(bool(store)), stream.cuda_stream))
 
 
 def decode_workspace_bytes(B, H, Hkv, N, d, num_splits=0) -> int:

@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip", "fa_decode.hip",
+           "fa_probe.hip"]
 # Per-source flags.  The forward's 16-bit kernels never see NaN scores from
 # finite inputs; without NaN semantics fmaxf needs no quieting of its
 # operands, which keeps the row max at one v_max3 per two scores.  The

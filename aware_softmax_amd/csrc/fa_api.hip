@@ -384,4 +384,11 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
   return hip_status(e);
 }
 
+fa_status_t fa_mfma_ceiling(float* sink, int iters, int blocks, int store, hipStream_t stream) {
+  if (!sink) return FA_ERR_NULL;
+  if (iters <= 0 || blocks <= 0 || (int64_t)blocks * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
+  if ((uintptr_t)sink % 4 != 0) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_mfma_ceiling(sink, iters, blocks, store, stream));
+}
+
 }  // extern "C"

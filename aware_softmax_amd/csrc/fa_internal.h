@@ -116,4 +116,8 @@ size_t bwd_varlen_workspace_bytes(int H, int total, int d);  // -L/scale and -D,
 int bwd_block_k();  // keys per workgroup of the dK/dV pass
 int bwd_block_q();  // queries per streamed tile of the dK/dV pass
 
+// Matrix-core-only ceiling kernel (4 MFMA 32x32x16 bf16 per iteration per
+// wave, 256 threads per block); `sink` holds blocks*256 floats.
+hipError_t launch_mfma_ceiling(float* sink, int iters, int blocks, int store, hipStream_t stream);
+
 }  // namespace fa

@@ -14,6 +14,13 @@ copy (the byte-count calibration kernel) followed by --steps launches.
 --profile-decode: --steps split-K decode calls on B=8 H=32 N=32768 d=128.
 --profile-bwd: --steps backward calls on B=2 H=16 N=4096 d=128 causal (the
 forward-plus-backward workload), printed as one JSON line.
+
+Next to the timed launches the line carries: the median, min and max
+launch time; a cold-cache timing (1 GiB written between launches, more
+than the 256 MB Infinity Cache); the shader clock read from sysfs while
+the kernel runs, the power cap and the CU count; the rate of a
+matrix-core-only kernel (fa_mfma_ceiling) as the sustained MFMA ceiling;
+and the oracle's per-core rate and extrapolated full-workload time.
 """
 from __future__ import annotations
 
@@ -23,7 +30,10 @@ import json
 import math
 import os
 import re
+import statistics
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -114,6 +124,7 @@ def time_launches(fa, q, k, v, o, lse, causal, scale, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    time_launches.last_per_launch = per
     return t_begin.elapsed_time(t_end) / steps, sum(per) / len(per), min(per), max(per), wall
 
 
@@ -354,6 +365,164 @@ def time_decode(fa, w, q, k, v, num_splits, steps, warmup):
             "kernels": "decode_split + decode_combine"}
 
 
+def device_sysfs(torch):
+    """sysfs directory of the GPU torch calls cuda:0 (from its PCI address),
+    or None where it is not readable."""
+    p = torch.cuda.get_device_properties(0)
+    bus = getattr(p, "pci_bus_id", None)
+    if bus is None:
+        return None
+    path = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (getattr(p, "pci_domain_id", 0), bus,
+                                                      getattr(p, "pci_device_id", 0))
+    return path if os.path.exists(os.path.join(path, "pp_dpm_sclk")) else None
+
+
+def read_sclk_mhz(path):
+    """Current shader clock: pp_dpm_sclk lists the levels and marks the
+    running one (or the actual frequency, on an 'S:' line) with '*'."""
+    try:
+        with open(os.path.join(path, "pp_dpm_sclk")) as f:
+            for line in f:
+                if "*" in line:
+                    m = re.search(r"(\d+)\s*mhz", line, re.I)
+                    return int(m.group(1)) if m else None
+    except OSError:
+        return None
+    return None
+
+
+def read_hwmon(path, name):
+    """A hwmon value of the device (power in microwatts), or None."""
+    import glob
+
+    for f in glob.glob(os.path.join(path, "hwmon", "hwmon*", name)):
+        try:
+            with open(f) as fh:
+                return int(fh.read().strip())
+        except (OSError, ValueError):
+            return None
+    return None
+
+
+class ClockSampler:
+    """Reads the shader clock and the average power from sysfs every
+    `period` seconds on a host thread while GPU work runs."""
+
+    def __init__(self, path, period=0.005):
+        self.path, self.period = path, period
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            c = read_sclk_mhz(self.path)
+            if c is not None:
+                self.sclk.append(c)
+            pw = read_hwmon(self.path, "power1_average")
+            if pw is None:
+                pw = read_hwmon(self.path, "power1_input")
+            if pw is not None:
+                self.power.append(pw / 1e6)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.path:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.sclk:
+            return None
+        out = {"median": statistics.median(self.sclk), "min": min(self.sclk), "max": max(self.sclk),
+               "samples": len(self.sclk)}
+        if self.power:
+            out["power_w_median"] = round(statistics.median(self.power), 1)
+        return out
+
+
+def sustained_clock(fa, torch, path, q, k, v, o, lse, scale, seconds=1.0):
+    """Shader clock sampled while fa_fwd launches run back to back for about
+    `seconds` (outside the timed region)."""
+    if path is None:
+        return None
+    fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with ClockSampler(path) as cs:
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(25):
+                fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse)
+            torch.cuda.synchronize()
+    return cs.summary()
+
+
+def mfma_ceiling(fa, torch, path, iters=1000, blocks=2048, seconds=1.0):
+    """Rate of the matrix-core-only kernel (dense bf16 MFMA, no memory
+    traffic) run back to back for about `seconds`, with the shader clock
+    sampled meanwhile."""
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        fa.mfma_ceiling(sink, iters, blocks)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    total_ms, calls = 0.0, 0
+    t0 = time.perf_counter()
+    with ClockSampler(path) as cs:
+        while time.perf_counter() - t0 < seconds:
+            a.record()
+            for _ in range(20):
+                fa.mfma_ceiling(sink, iters, blocks)
+            b.record()
+            torch.cuda.synchronize()
+            total_ms += a.elapsed_time(b)
+            calls += 20
+    ms = total_ms / calls
+    flops = fa.MFMA_CEILING_FLOP_PER_ITER_BLOCK * iters * blocks
+    out = {"TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 3), "calls": calls,
+           "kernel": f"fa_mfma_ceiling: {blocks} workgroups x 4 waves x {iters} x 4 v_mfma_f32_32x32x16_bf16"}
+    clk = cs.summary()
+    if clk:
+        out["sclk_mhz"] = clk
+    return out
+
+
+def cold_cache(fa, torch, q, k, v, o, lse, scale, launches=10):
+    """fa_fwd time with 1 GiB written between launches (flushes the 256 MB
+    Infinity Cache and the L2s); only the forward is inside the events."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=q.device)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    for i in range(launches):
+        scratch.fill_(float(i))
+        starts[i].record()
+        fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse)
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    del scratch
+    return statistics.median(per)
+
+
+def cpu_per_core(w_id, budget_s=4.0):
+    """The oracle on one host thread, in a child process whose BLAS pools
+    are limited to one thread before NumPy loads (no GPU use)."""
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               BLIS_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-per-core", str(w_id),
+                            str(budget_s)], env=env, capture_output=True, text=True, timeout=120)
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:  # reported, never fatal for the GPU measurement
+        return {"error": repr(e)[:200]}
+
+
 def cpu_baseline(w, budget_s=12.0, rows_per_head=512):
     """The fp64 oracle on the host cores over a bounded sample of the same
     workload: seeded (b, h) heads, 512 seeded query rows each, until the
@@ -391,6 +560,8 @@ def cpu_baseline(w, budget_s=12.0, rows_per_head=512):
         "sample": f"{done} seeded heads x {len(rows)} seeded query rows of B={w.B} H={w.H} N={w.N} "
                   f"d={w.d} causal (naive fp64 NumPy, materialised score rows); {spent:.1f} s",
         "seconds": spent,
+        "extrapolated_full_workload_s": round(
+            attention_flops(w.B, w.H, w.N, w.d, w.causal) / (flops / spent), 1),
     }
 
 
@@ -406,7 +577,14 @@ def main():
                     help="run --steps fa_decode calls on B=8 H=32 N=32768 d=128 (for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="run --steps fa_bwd calls on B=2 H=16 N=4096 d=128 causal (for rocprofv3)")
+    ap.add_argument("--cpu-per-core", nargs=2, metavar=("WORKLOAD", "SECONDS"), help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_per_core:
+        import synthetic
+
+        r = cpu_baseline(synthetic.WORKLOADS[int(args.cpu_per_core[0])], budget_s=float(args.cpu_per_core[1]))
+        print(json.dumps({"value": r["value"], "unit": r["unit"], "cores": r["cores"], "sample": r["sample"]}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the attention forward is sharded over heads with no "
               f"communication, and this build runs on a single MI355X; --gpus {args.gpus} is not "
@@ -455,8 +633,15 @@ def main():
     flops = attention_flops(w.B, w.H, w.N, w.d, True)
     tflops = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
+    per_launch = time_launches.last_per_launch
     bq, bk, waves = fa.tile_config(w.d, fa.DTYPE_BF16)
     traffic = read_traffic()
+    path = device_sysfs(torch)
+    props = torch.cuda.get_device_properties(0)
+    clock = sustained_clock(fa, torch, path, q, k, v, o, lse, w.scale)
+    ceiling = mfma_ceiling(fa, torch, path)
+    cold_ms = cold_cache(fa, torch, q, k, v, o, lse, w.scale)
+    power_cap = read_hwmon(path, "power1_cap") if path else None
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -484,8 +669,18 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel_ms": {"mean": round(ms_kernel, 4), "min": round(ms_min, 4), "max": round(ms_max, 4)},
+            "kernel_ms": {"mean": round(ms_kernel, 4), "median": round(statistics.median(per_launch), 4),
+                          "min": round(ms_min, 4), "max": round(ms_max, 4)},
             "flops_per_launch": flops,
+            "mfma_ceiling": dict(ceiling, frac=round(achieved / ceiling["TFLOP/s"], 4)),
+        },
+        "cold_cache": {"ms": round(cold_ms, 4), "TFLOP/s": round(flops / (cold_ms * 1e-3) / 1e12, 2),
+                       "how": "1 GiB device write between launches, median of 10"},
+        "device": {
+            "name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cu_count": props.multi_processor_count,
+            "sclk_mhz_under_fwd": clock,
+            "power_cap_w": round(power_cap / 1e6, 1) if power_cap else None,
         },
     }
     if args.extra:
@@ -541,6 +736,7 @@ def main():
         result["other_workloads"] = extra
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline"]["per_core"] = cpu_per_core(w.config_id)
     print(json.dumps(result), flush=True)
 
 

@@ -300,6 +300,23 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
  */
 int fa_last_hip_error(const char** message);
 
+/*
+ * fa_mfma_ceiling -- measurement helper, not part of attention: `blocks`
+ * workgroups of four waves each run `iters` x 4 dependent-chain
+ * v_mfma_f32_32x32x16_bf16 instructions (32768 FLOP each) with no memory
+ * traffic, so that the attention kernels' rate can be set against the
+ * dense bf16 rate the chip sustains under matrix load (clock and power
+ * included) as well as against the nominal peak.  FLOPs per call:
+ * blocks * 4 * iters * 4 * 32768.
+ *   sink    device buffer of blocks * 256 floats, written only if store != 0
+ *           (the flag keeps the compiler from dropping the loop).
+ *   stream  HIP stream; one kernel is enqueued on it.
+ * Returns FA_ERR_NULL (sink NULL), FA_ERR_SHAPE (iters or blocks <= 0, or
+ * blocks * 256 beyond 2^32 - 1), FA_ERR_ALIGN (sink not 4-byte aligned),
+ * FA_ERR_HIP (launch failed) or FA_OK.
+ */
+fa_status_t fa_mfma_ceiling(float* sink, int iters, int blocks, int store, hipStream_t stream);
+
 /* Library version string, e.g. "0.1.0 gfx950" (static storage). */
 const char* fa_version(void);
 
