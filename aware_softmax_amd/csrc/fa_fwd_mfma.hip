@@ -94,16 +94,21 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = kBQ / kWaves;  // 32 = one MFMA column block
 static_assert(kRowsPerWave == 32, "one 32-wide MFMA block of queries per wave");
 
-template <int D>
+// One LDS stage holds G consecutive key tiles, one per wave group: with
+// G = 2 the workgroup's two groups of 4 waves take alternate tiles of the
+// same query rows and merge their (m, l, O) once at the end.
+template <int D, int G>
 struct Layout {
-  static constexpr int KS = D + 8;   // K tile row stride in elements (+16 B)
-  static constexpr int VS = D + 16;  // V tile row stride in elements (+32 B)
-  static constexpr int K_ELEMS = kBK * KS;
-  static constexpr int V_ELEMS = kBK * VS;
+  static constexpr int THREADS = kThreads * G;
+  static constexpr int KEYS = kBK * G;  // keys per stage
+  static constexpr int KS = D + 8;      // K tile row stride in elements (+16 B)
+  static constexpr int VS = D + 16;     // V tile row stride in elements (+32 B)
+  static constexpr int K_ELEMS = KEYS * KS;
+  static constexpr int V_ELEMS = KEYS * VS;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
   static constexpr int CHUNKS_PER_ROW = D / 8;                    // 16-byte chunks
-  static constexpr int CHUNKS_PER_THREAD = kBK * D / 8 / kThreads;
-  static_assert(kBK * D / 8 % kThreads == 0, "tile splits evenly over threads");
+  static constexpr int CHUNKS_PER_THREAD = KEYS * D / 8 / THREADS;
+  static_assert(KEYS * D / 8 % THREADS == 0, "tile splits evenly over threads");
 };
 
 __device__ inline float swap_halves(float x, bool want_max) {
@@ -231,19 +236,27 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
 // Any d that is a multiple of 32 (one 32-wide output block per step); two
 // workgroups per CU up to d = 128, one at d = 256 (O^T alone is 128 fp32
 // per lane there, and two K/V stages take 137 KB of LDS).
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
+//
+// G = 2 (grids too small to fill the chip): 8 waves in two groups of 4 over
+// the same 128 query rows; group g takes the key tiles 2j + g, so the
+// longest chain of dependent tiles -- the last causal row block scans every
+// key -- is halved.  At the end group 1 hands its running max, partial sums
+// and O^T to group 0 through LDS, which rescales both to the common max
+// (the merge rule of the online softmax) and writes the output.
+template <class T, int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(kThreads * G, (D >= 256 || G == 2) ? 1 : 2) void fwd_mfma_kernel(
     const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
     T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group, const int* __restrict__ cu_seqlens, int H, int total) {
-  using Ly = Layout<D>;
+  using Ly = Layout<D, G>;
   constexpr int DT = D / 16;  // 16-wide d steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide d blocks of the output
   __shared__ __attribute__((aligned(16))) T smem[2 * Ly::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = (tid >> 6) & (kWaves - 1);  // query rows of the wave
+  const int grp = G == 1 ? 0 : tid >> 8;       // key tiles of the wave
   const int col = lane & 31;   // query column of the transposed tiles
   const int half = lane >> 5;  // which 4-key group of each 8 (MFMA layout)
 
@@ -280,8 +293,8 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
     }
   }
 
-  int nkt = (N + kBK - 1) / kBK;
-  if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / kBK + 1);
+  int nkt = (N + Ly::KEYS - 1) / Ly::KEYS;  // LDS stages
+  if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / Ly::KEYS + 1);
 
   // ---- running state: O^T blocks (d x queries), m in log2 units, partial l
   f32x16 oacc[DB];
@@ -293,10 +306,10 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
   // ---- global -> register prefetch, register -> LDS store
   vec8<T> kreg[Ly::CHUNKS_PER_THREAD], vreg[Ly::CHUNKS_PER_THREAD];
   auto gload = [&](int j) {
-    const int kt0 = j * kBK;
+    const int kt0 = j * Ly::KEYS;
 #pragma unroll
     for (int i = 0; i < Ly::CHUNKS_PER_THREAD; ++i) {
-      const int ci = tid + kThreads * i;
+      const int ci = tid + Ly::THREADS * i;
       const int row = ci / Ly::CHUNKS_PER_ROW;
       const int c8 = ci % Ly::CHUNKS_PER_ROW;
       const int key = kt0 + row;
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
     T* Vl = Kl + Ly::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < Ly::CHUNKS_PER_THREAD; ++i) {
-      const int ci = tid + kThreads * i;
+      const int ci = tid + Ly::THREADS * i;
       const int row = ci / Ly::CHUNKS_PER_ROW;
       const int c8 = ci % Ly::CHUNKS_PER_ROW;
       *(vec8<T>*)(Kl + row * Ly::KS + c8 * 8) = kreg[i];
@@ -337,11 +350,11 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
   for (int j = 0; j < nkt; ++j) {
     const int buf = j & 1;
     if (j + 1 < nkt) gload(j + 1);
-    const int kt0 = j * kBK;
-    const bool skip = CAUSAL && kt0 > qw + kRowsPerWave - 1;
+    const int kt0 = j * Ly::KEYS + grp * kBK;  // this group's tile
+    const bool skip = (CAUSAL && kt0 > qw + kRowsPerWave - 1) || (G > 1 && kt0 >= N);
     if (!skip) {
-      const T* Kl = smem + buf * Ly::STAGE;
-      const T* Vl = Kl + Ly::K_ELEMS;
+      const T* Kl = smem + buf * Ly::STAGE + grp * kBK * Ly::KS;
+      const T* Vl = smem + buf * Ly::STAGE + Ly::K_ELEMS + grp * kBK * Ly::VS;
 
       // S^T[key][query] for two 32-key halves of the tile.
       f32x16 s[2];
@@ -390,6 +403,38 @@ __global__ __launch_bounds__(kThreads, D >= 256 ? 1 : 2) void fwd_mfma_kernel(
     }
     if (j + 1 < nkt) lstore(buf ^ 1);
     __syncthreads();
+  }
+
+  if constexpr (G == 2) {
+    // Merge the two groups (the stages are free after the loop's last
+    // barrier): [16 DB + 2][4 waves][64 lanes] fp32, lane-consecutive so
+    // that every write and read is conflict-free.  Both groups hold the same
+    // rows in the same lanes; a row's max is the same in its two lanes.
+    constexpr int NV = 16 * DB + 2;
+    static_assert(NV * kThreads * 4 <= (int)sizeof(smem), "merge buffer fits the stages");
+    float* xb = (float*)smem + wave * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xb[(b * 16 + r) * kThreads] = oacc[b][r];
+      xb[16 * DB * kThreads] = m_run;
+      xb[(16 * DB + 1) * kThreads] = l_part;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xb[16 * DB * kThreads];
+    const float l1 = xb[(16 * DB + 1) * kThreads];
+    const float mm = fmaxf(m_run, m1);
+    const float mu = mm == -INFINITY ? 0.f : mm;  // a row no group saw: both factors 0
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mu);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
+    l_part = a0 * l_part + a1 * l1;
+    m_run = mm;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] = a0 * oacc[b][r] + a1 * xb[(b * 16 + r) * kThreads];
   }
 
   // ---- epilogue: one reciprocal per row, bf16 store, L = ln2 (m + log2 l)
@@ -1001,15 +1046,26 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 // copies), the 4-wave kernel for d = 32, 64, 96 and 256 (at d <= 96 the
 // 2d/16 + 2d/16 MFMAs per tile leave too few slots to hide the softmax of a
 // 64-key tile; at d = 256 two waves per SIMD do not fit the registers).
+// Grids of at most this many workgroups run the d <= 96 kernel with two
+// wave groups over the keys (G = 2): with few workgroups per CU there is no
+// later workgroup to balance the causal row blocks, and the run takes as
+// long as the longest block's chain of key tiles.  Measured (causal bf16,
+// same box): +22 % at B1 H16 N2048 d64 (256 workgroups), +47 % at B1 H16
+// N4096 d64, +6 % at B2 H16 N4096 d64 (1024), -5 % at B4 H16 N2048 d64
+// (1024), -12 % at B2 H32 N8192 d64 (4096).
+constexpr int kSplitMaxBlocks = 1024;
+
 template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr bool kDuo = D == 128;
   const int bq = kDuo ? duo::kBQ : kBQ;
   const int nqb = (p.N + bq - 1) / bq;
+  constexpr bool kCanSplit = D <= 96;
+  const bool split = kCanSplit && (int64_t)p.BH * nqb <= kSplitMaxBlocks;
   const float c_signed = p.scale * 1.44269504088896340736f;
   const int negate = p.scale < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
-  dim3 grid(p.BH * nqb), block(kDuo ? duo::kThreads : kThreads);
+  dim3 grid(p.BH * nqb), block(kDuo ? duo::kThreads : split ? 2 * kThreads : kThreads);
   const T* q = (const T*)p.q;
   const T* k = (const T*)p.k;
   const T* v = (const T*)p.v;
@@ -1026,8 +1082,10 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   if constexpr (kDuo)
     fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
                                : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
+  else if (split)
+    fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, kCanSplit ? 2 : 1>;
   else
-    fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL>;
+    fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

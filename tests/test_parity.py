@@ -142,6 +142,18 @@ def test_head_dims_bf16_long(fa, d):
                           heads=synthetic.sample_heads(1600 + d, 2, 8, 4)), "bf16")
 
 
+@pytest.mark.parametrize("d", [32, 64, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_grid_single_group(fa, d, causal):
+    """B8 H32 N1000: 2048 workgroups, more than the grid size up to which
+    the d <= 96 kernel splits the key tiles over two wave groups, so the
+    one-group variant runs (the smaller cases above take the two-group
+    one); 6 seeded heads, ragged last tile."""
+    cid = 1700 + d + causal
+    heads = synthetic.sample_heads(cid, 8, 32, 6)
+    assert_close(run_case(fa, cid, 8, 32, 1000, d, "bf16", causal, heads=heads), "bf16")
+
+
 @pytest.mark.parametrize("n", [1, 5, 64, 100, 257])
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
