@@ -284,7 +284,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // the `group` query heads that share the key/value head (consecutive
   // query heads bhk * group .. bhk * group + group - 1).
   int bhk, jb;
-  map_block(blockIdx.x, BHkv * nkb, nkb, false, &bhk, &jb);  // key block 0 (the most query tiles) first
+  map_block(blockIdx.x, BHkv * nkb, nkb, CAUSAL ? Order::HeavyFirst : Order::Plain, &bhk, &jb);
   const int kb0 = jb * kBKV;
   // Rows of this key/value head (and sequence): `head` is the element
   // offset of its K/V row 0; query head r of the group has Q/dO row 0 at
@@ -586,7 +586,7 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   const int half = lane >> 5;
 
   int bh, qb;
-  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);  // causal: the longest blocks first
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQdq;
   // Rows of query head bh (and its sequence): Q/dO/dQ row 0 at `head`, the
   // K/V rows of its key/value head at `kvhead`, statistics row 0 at `st`.

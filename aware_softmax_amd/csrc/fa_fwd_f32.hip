@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   const int row = tid >> 2;
   const int sub = tid & 3;
   int bh, qb;
-  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQ;
   const int qi = q0 + row;
   const size_t head = (size_t)bh * (size_t)N * D;

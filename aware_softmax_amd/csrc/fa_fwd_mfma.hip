@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kThreads * G, (D >= 256 || G == 2) ? 1 : 2) void fw
   const int half = lane >> 5;  // which 4-key group of each 8 (MFMA layout)
 
   int bh, qb;
-  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQ;
   HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
   if (cu_seqlens) {
@@ -669,7 +669,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   const int half = lane >> 5;
 
   int bh, qb;
-  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL, &bh, &qb);
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQ;
   HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
   if (cu_seqlens) {

@@ -126,21 +126,35 @@ def test_schedule_is_a_bijection(tmp_path):
 #include <vector>
 #include "fa_schedule.h"
 int main() {
-  const int cases[][2] = {{1,1},{1,3},{7,1},{16,16},{256,64},{16,256},{3,5},{13,9},{32,128},{5,1}};
+  const int cases[][2] = {{1,1},{1,3},{7,1},{16,16},{256,64},{16,256},{3,5},{13,9},{32,128},{5,1},
+                           {32,16},{16,8},{8,128},{64,16},{24,4}};
   for (auto& c : cases) {
     const int heads = c[0], nqb = c[1], total = heads * nqb;
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 3; ++hf) {
+      const fa::Order order = hf == 0 ? fa::Order::Plain : hf == 1 ? fa::Order::HeavyLast : fa::Order::HeavyFirst;
       std::vector<int> seen(total, 0);
       for (int id = 0; id < total; ++id) {
-        int bh, qb; fa::map_block(id, total, nqb, hf != 0, &bh, &qb);
+        int bh, qb; fa::map_block(id, total, nqb, order, &bh, &qb);
         if (bh < 0 || bh >= heads || qb < 0 || qb >= nqb) { printf("out of range\n"); return 1; }
         seen[bh * nqb + qb]++;
       }
       for (int x : seen) if (x != 1) { printf("not a bijection\n"); return 1; }
       // every XCD (id % 8) gets a contiguous run of (head, block) pairs
       if (hf) {
-        int bh, qb; fa::map_block(0, total, nqb, true, &bh, &qb);
-        if (bh != 0 || qb != nqb - 1) { printf("heavy block not first\n"); return 1; }
+        // the heaviest block comes first: nqb - 1 (query blocks) or 0 (key blocks)
+        auto weight = [&](int q) { return hf == 1 ? q : nqb - 1 - q; };
+        int bh, qb; fa::map_block(0, total, nqb, order, &bh, &qb);
+        if (bh != 0 || weight(qb) != nqb - 1) { printf("heavy block not first\n"); return 1; }
+        // within each XCD the issue order never puts a lighter block of a
+        // head before a heavier block of the same head
+        for (int x = 0; x < 8; ++x) {
+          std::vector<int> last(heads, nqb);
+          for (int id = x; id < total; id += 8) {
+            fa::map_block(id, total, nqb, order, &bh, &qb);
+            if (weight(qb) >= last[bh]) { printf("order\n"); return 1; }
+            last[bh] = weight(qb);
+          }
+        }
       }
     }
   }
