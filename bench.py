@@ -69,6 +69,23 @@ def kernel_source_hash(path=KERNEL_SOURCE):
     return hashlib.sha256(text.encode()).hexdigest()
 
 
+def traffic_models(w, bq, lds_bytes=160 * 1024):
+    """HBM bytes per launch under three models, next to the measured
+    traffic: compulsory (read Q, K, V, write O and L once); the pages'
+    Theta(N^2 d^2 / M) bound with M = one CU's 160 KB of LDS in elements;
+    and re-reading every visible K/V tile once per query block of bq rows
+    with no cache reuse."""
+    s = 2  # bytes per element
+    heads = w.B * w.H
+    compulsory = heads * (4 * w.N * w.d * s + 4 * w.N)
+    theta = heads * w.N * w.N * w.d * w.d * s / (lds_bytes / s)
+    nqb = -(-w.N // bq)
+    tiles = sum(min(w.N, (i + 1) * bq) for i in range(nqb)) if w.causal else nqb * w.N
+    no_reuse = heads * (2 * s * w.d * tiles + 2 * w.N * w.d * s + 4 * w.N)
+    return {"compulsory": compulsory, "theta_N2d2_over_M": round(theta), "no_reuse_per_query_block": no_reuse,
+            "M_bytes": lds_bytes, "block_q": bq}
+
+
 def read_traffic():
     """HBM bytes per launch from the committed counter summary, or None if
     the summary is missing or the kernel source changed since."""
@@ -673,6 +690,7 @@ def main():
                           "min": round(ms_min, 4), "max": round(ms_max, 4)},
             "flops_per_launch": flops,
             "mfma_ceiling": dict(ceiling, frac=round(achieved / ceiling["TFLOP/s"], 4)),
+            "traffic_models": traffic_models(w, bq),
         },
         "cold_cache": {"ms": round(cold_ms, 4), "TFLOP/s": round(flops / (cold_ms * 1e-3) / 1e12, 2),
                        "how": "1 GiB device write between launches, median of 10"},
