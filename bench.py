@@ -748,7 +748,9 @@ def main():
             dw = synthetic.DECODE_WORKLOADS[cid]
             dq_, dk_, dv_ = decode_inputs(dw)
             for ns, tag in ((0, "split-K"), (1, "unsplit")):
-                extra[f"{dw.name} {tag}"] = time_decode(fa, dw, dq_, dk_, dv_, ns, 20, 3)
+                # 30 untimed calls: the first calls after the inputs are
+                # copied in run up to 10 % slower
+                extra[f"{dw.name} {tag}"] = time_decode(fa, dw, dq_, dk_, dv_, ns, 20, 30)
             del dq_, dk_, dv_
             torch.cuda.empty_cache()
         result["other_workloads"] = extra
