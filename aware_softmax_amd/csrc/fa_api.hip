@@ -37,6 +37,9 @@ fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
   return ok ? FA_OK : FA_ERR_UNSUPPORTED_HEADDIM;
 }
 
+// Head dims of the backward kernels.
+bool bwd_headdim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
 }  // namespace
 
 extern "C" {
@@ -177,7 +180,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
+  if (B <= 0 || H <= 0 || N <= 0 || !bwd_headdim(d)) return 0;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX || bh * N * d > ((int64_t)1 << 40)) return 0;
   return fa::bwd_workspace_bytes((int)bh, N, d);
@@ -185,7 +188,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
 
 fa_status_t fa_bwd_tile(int d, int* block_k, int* block_q) {
   if (!block_k || !block_q) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!bwd_headdim(d)) return FA_ERR_UNSUPPORTED_HEADDIM;
   *block_k = fa::bwd_block_k();
   *block_q = fa::bwd_block_q();
   return FA_OK;
@@ -197,7 +200,7 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
   if (!is_16bit(dtype)) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!bwd_headdim(d)) return FA_ERR_UNSUPPORTED_HEADDIM;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   const int64_t elems = bh * N * d;
@@ -254,7 +257,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
 }
 
 size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d) {
-  if (H <= 0 || total <= 0 || (d != 64 && d != 128)) return 0;
+  if (H <= 0 || total <= 0 || !bwd_headdim(d)) return 0;
   if ((int64_t)H * total * d > ((int64_t)1 << 40) || total > INT_MAX - 128) return 0;
   return fa::bwd_varlen_workspace_bytes(H, total, d);
 }
@@ -267,7 +270,7 @@ fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const voi
   if (B <= 0 || H <= 0 || Hkv <= 0 || total <= 0 || max_seqlen <= 0 || d <= 0 || H % Hkv != 0)
     return FA_ERR_SHAPE;
   if (!is_16bit(dtype)) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!bwd_headdim(d)) return FA_ERR_UNSUPPORTED_HEADDIM;
   const int64_t bh = (int64_t)B * H;
   if (bh > INT_MAX || max_seqlen > total || total > INT_MAX - 128) return FA_ERR_SHAPE;
   const int64_t elems = (int64_t)H * total * d;

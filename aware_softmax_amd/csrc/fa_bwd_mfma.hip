@@ -118,6 +118,15 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 template <int I>
 using ic = std::integral_constant<int, I>;
 
+// Elements per LDS tile row: d rounded up to a power-of-two number of
+// 16-byte chunks (d = 32 -> 64, 96 -> 128), so that the XOR swizzle below
+// permutes whole rows.  The pad chunks are filled with copies of real
+// chunks and never read: the MFMA loops run over d only.
+template <int D>
+constexpr int lds_row_elems() {
+  return D == 32 ? 64 : D == 96 ? 128 : D;
+}
+
 // Physical 16-byte chunk mask of row r of an LDS tile whose rows are ROWB
 // bytes (chunk c is stored at c ^ mask).  Conflict-free for
 //   * 16 lanes reading one chunk of 16 consecutive rows (ds_read_b128), and
@@ -186,21 +195,27 @@ typedef __attribute__((address_space(3))) void lds_void;
 // chunk each lane fetches.  Wave w issues instructions [w IPW, (w + 1) IPW).
 template <int D, int kRows, class T>
 __device__ __forceinline__ void dma_rows(const T* X, int r0, int N, char* tile, int wave, int lane) {
-  constexpr int ROWB = 2 * D, CPR = D / 8, RPI = 1024 / ROWB;
+  constexpr int ROWB = 2 * lds_row_elems<D>(), CPR = ROWB / 16, RPI = 1024 / ROWB;
   constexpr int IPW = kRows * ROWB / 1024 / kWaves;
   static_assert(kRows * ROWB % (1024 * kWaves) == 0, "DMA splits evenly over waves");
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int inst = wave * IPW + i;
     const int row = inst * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz_mask<ROWB>(row);
+    const int slot = (lane % CPR) ^ swz_mask<ROWB>(row);  // logical chunk of this LDS slot
+    const int chunk = slot < D / 8 ? slot : slot - D / 8;   // pad slots: a copy of a real chunk
     const size_t off = (size_t)min(r0 + row, N - 1) * D + chunk * 8;
     __builtin_amdgcn_global_load_lds((const void*)(X + off), (lds_void*)(tile + inst * 1024), 16, 0, 0);
   }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_pre: one row per LPR lanes (one 16-byte chunk of dO and O each).
+// bwd_pre: one row per LPR lanes (CPL 16-byte chunks of dO and O each; LPR
+// the largest power of two dividing the row's chunk count).
+template <int D>
+constexpr int pre_lanes_per_row() {
+  return (D / 8) & -(D / 8);
+}
 // Writes -D_i and -L_i / scale (in the units of the raw score q.k): the
 // initial values of the dP and S accumulators of the two main kernels, so
 // that their MFMAs produce dP - D and q.k - L / scale directly.
@@ -209,7 +224,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, 
                                                       const float* __restrict__ Lg, float* __restrict__ Lsg,
                                                       float* __restrict__ Dng, int N, int Npad, float l_to_score,
                                                       VarLen vl) {
-  constexpr int LPR = D / 8;
+  constexpr int LPR = pre_lanes_per_row<D>();
+  constexpr int CPL = D / 8 / LPR;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
   const int c = tid % LPR;
@@ -222,11 +238,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, 
   const int i = (int)(row % stride);
   float acc = 0.f;
   if (i < rows) {
-    const size_t off = ((size_t)bh * rows + i) * D + c * 8;
-    const vec8<T> a = *(const vec8<T>*)(Og + off);
-    const vec8<T> b = *(const vec8<T>*)(dOg + off);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    for (int x = 0; x < CPL; ++x) {
+      const size_t off = ((size_t)bh * rows + i) * D + (c + x * LPR) * 8;
+      const vec8<T> a = *(const vec8<T>*)(Og + off);
+      const vec8<T> b = *(const vec8<T>*)(dOg + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
+    }
   }
 #pragma unroll
   for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
@@ -240,7 +259,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, 
 // bwd_dkdv.
 template <int D>
 struct DkdvLayout {
-  static constexpr int ROWB = 2 * D;
+  static constexpr int ROWB = 2 * lds_row_elems<D>();
   static constexpr int QTILE = kBQ * ROWB;    // one Q or dO tile
   static constexpr int STTILE = 2 * kBQ * 4;  // -L/scale[64], -D[64]
   static constexpr int OFF_Q = 0;
@@ -546,7 +565,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
 // bwd_dq.
 template <int D>
 struct DqLayout {
-  static constexpr int ROWB = 2 * D;
+  static constexpr int ROWB = 2 * lds_row_elems<D>();
   static constexpr int KTILE = kBKdq * ROWB;  // one K or V tile
   static constexpr int OFF_K = 0;
   static constexpr int OFF_V = OFF_K + kRing * KTILE;
@@ -804,7 +823,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   const T* v = (const T*)p.v;
   const T* dout = (const T*)p.dout;
   {
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / pre_lanes_per_row<D>();
     static_assert(kBQ % RPB == 0, "statistics rows split evenly over the pre kernel's workgroups");
     hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)(stat_rows / RPB)), dim3(256), 0, stream,
                        (const T*)p.o, dout, p.lse, ls, dn, p.N, npad, kLog2e / c, vl);
@@ -853,11 +872,22 @@ size_t bwd_varlen_workspace_bytes(int H, int total, int d) {
 int bwd_block_k() { return kBKV; }
 int bwd_block_q() { return kBQ; }
 
+template <class T>
+hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 32: return launch_bwd<T, 32>(p, stream);
+    case 64: return launch_bwd<T, 64>(p, stream);
+    case 96: return launch_bwd<T, 96>(p, stream);
+    case 128: return launch_bwd<T, 128>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
-  return p.d == 64 ? launch_bwd<__bf16, 64>(p, stream) : launch_bwd<__bf16, 128>(p, stream);
+  return launch_bwd_t<__bf16>(p, stream);
 }
 hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream) {
-  return p.d == 64 ? launch_bwd<_Float16, 64>(p, stream) : launch_bwd<_Float16, 128>(p, stream);
+  return launch_bwd_t<_Float16>(p, stream);
 }
 
 }  // namespace fa

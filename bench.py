@@ -717,6 +717,14 @@ def main():
             if cid == 5:
                 extra[f"causal bf16 bwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"] = time_backward(
                     fa, ww, qq, kk, vv, oo, ll, 20, 3)
+                for d in (32, 64, 96):  # the other backward head dims, same shape otherwise
+                    hw = synthetic.Workload(5, "", ww.B, ww.H, ww.N, d, "bf16", True)
+                    q2, k2, v2 = make_inputs(hw)
+                    o2 = torch.empty_like(q2)
+                    l2 = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=q2.device)
+                    extra[f"causal bf16 bwd B{hw.B} H{hw.H} N{hw.N} d{d}"] = time_backward(
+                        fa, hw, q2, k2, v2, o2, l2, 20, 3)
+                    del q2, k2, v2, o2, l2
             del qq, kk, vv, oo, ll
             torch.cuda.empty_cache()
         qq, kk, vv = make_inputs(w)

@@ -174,7 +174,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *                     bytes (passed as workspace_bytes), 256-byte aligned,
  *                     owned by the caller; overwritten, contents undefined
  *                     afterwards.  It needs no initialisation.
- *   B, H, N, d, causal, scale   as for fa_fwd.
+ *   B, H, N, causal, scale   as for fa_fwd.
+ *   d         head dimension: 32, 64, 96 or 128 (else
+ *             FA_ERR_UNSUPPORTED_HEADDIM).
  *   dtype     FA_DTYPE_BF16 or FA_DTYPE_F16 (P and dS are rounded to it for
  *             the MFMAs); FA_DTYPE_F32 returns FA_ERR_DTYPE.
  *   stream    HIP stream; three kernels are enqueued in order on it.
@@ -214,7 +216,7 @@ size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d);
  * [Hkv][total][d]; lse [H][total]; every sequence's gradients depend only
  * on its own rows.  workspace: at least fa_bwd_varlen_workspace_bytes(H,
  * total, d) bytes, 256-byte aligned.  dtype FA_DTYPE_BF16 or FA_DTYPE_F16;
- * d 64 or 128; the other arguments and the checks as for fa_bwd_gqa and
+ * d 32, 64, 96 or 128; the other arguments and the checks as for fa_bwd_gqa and
  * fa_fwd_varlen (cu_seqlens clamped to [0, total] on the device).
  */
 fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,

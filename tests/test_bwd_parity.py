@@ -108,6 +108,27 @@ def test_ragged_bwd(fa, n, d, causal):
     run_bwd(fa, cid, 1, 2, n, d, causal)
 
 
+@pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 333, 513])
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_bwd_head_dims(fa, n, d, causal):
+    """d = 32 and 96: LDS rows padded to 64 / 128 elements, the MFMA loops
+    over d only."""
+    run_bwd(fa, 9000 + n * 4 + (d == 96) * 2 + causal, 1, 2, n, d, causal)
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_bwd_head_dims_long(fa, d):
+    """B2 H4 N2048 causal: many query and key tiles per workgroup; 3 seeded
+    heads."""
+    run_bwd(fa, 9100 + d, 2, 4, 2048, d, True, heads=synthetic.sample_heads(9100 + d, 2, 4, 3))
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_f16_bwd_head_dims(fa, d):
+    run_bwd(fa, 9200 + d, 1, 2, 333, d, True, dtype="f16")
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.35])
 def test_other_scales_bwd(fa, scale):
     run_bwd(fa, 6500 + int(scale * 100), 1, 2, 300, 64, True, scale=scale)
@@ -179,7 +200,7 @@ def test_outputs_untouched_outside_bounds(fa):
 
 
 @pytest.mark.parametrize("shape", [(2, 8, 2, 333, 128), (1, 12, 4, 1000, 64), (1, 6, 1, 257, 128),
-                                   (1, 8, 2, 2048, 128)])
+                                   (1, 8, 2, 2048, 128), (1, 6, 2, 300, 96), (1, 4, 1, 200, 32)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_backward(fa, shape, causal):
     """fa_bwd_gqa: dK, dV of a key/value head sum over the query heads of
@@ -187,7 +208,7 @@ def test_gqa_backward(fa, shape, causal):
     import torch
 
     B, H, Hkv, N, d = shape
-    cid = 6950 + H * 8 + Hkv + (d == 128)
+    cid = 6950 + H * 8 + Hkv + (d == 128) + 3 * (d in (32, 96))
     st = {"q": synthetic.full_storage(cid, "q", B, H, N, d, "bf16"),
           "do": synthetic.full_storage(cid, "do", B, H, N, d, "bf16"),
           "k": synthetic.full_storage(cid, "k", B, Hkv, N, d, "bf16"),
@@ -273,6 +294,11 @@ def varlen_bwd_case(fa, cid, lengths, H, Hkv, d, causal, dtype="bf16"):
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_backward(fa, lengths, d, causal):
     varlen_bwd_case(fa, 8200 + len(lengths) * 8 + (d == 128) * 2 + causal, lengths, 4, 2, d, causal)
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_varlen_backward_head_dims(fa, d):
+    varlen_bwd_case(fa, 8250 + d, [5, 0, 130, 64, 1, 257], 4, 2, d, True)
 
 
 def test_varlen_backward_f16(fa):
