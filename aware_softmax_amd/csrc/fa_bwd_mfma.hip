@@ -312,8 +312,9 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   int hk = bhk, r0 = 0;
   if (vl.cu) {
     const int n_kv = vl.H / group;
-    const int b = bhk / n_kv;
-    hk = bhk - b * n_kv;
+    const int B = BHkv / n_kv;  // head-major: hk = bhk / B (each XCD gets the same heads of every sequence)
+    hk = bhk / B;
+    const int b = bhk - hk * B;
     r0 = seq_start(vl, b);
     N = seq_len(vl, b, r0);
     if (kb0 >= N) return;  // past the end of this sequence (the whole workgroup)
@@ -611,7 +612,8 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   // K/V rows of its key/value head at `kvhead`, statistics row 0 at `st`.
   size_t head, kvhead, st;
   if (vl.cu) {
-    const int b = bh / vl.H, h = bh - b * vl.H;
+    const int B = BH / vl.H;  // head-major, as in bwd_dkdv
+    const int h = bh / B, b = bh - h * B;
     const int r0 = seq_start(vl, b);
     N = seq_len(vl, b, r0);
     if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)

@@ -142,17 +142,22 @@ __device__ constexpr int score_key_offset(int i) { return (i >> 4) * 32 + ((i >>
 // Where the rows of query head bh live.  Fixed length: q, o [BH][N][D],
 // k, v [BH / group][N][D], L [BH][N].  Variable length (cu_seqlens, B + 1
 // offsets into `total` packed rows per head): q, o [H][total][D], k, v
-// [H / group][total][D], L [H][total]; bh = b H + h, and sequence b holds
-// rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1 of every head.  Query heads of
-// a group are consecutive, so head h reads key/value head h / group.
+// [H / group][total][D], L [H][total]; bh = h B + b (head-major: the
+// schedule gives each XCD a contiguous range of bh, so every XCD gets the
+// same heads of every sequence and the same share of the work whatever the
+// lengths), and sequence b holds rows cu_seqlens[b] .. cu_seqlens[b + 1] - 1
+// of every head.  Query heads of a group are consecutive, so head h reads
+// key/value head h / group.
 struct HeadRows {
   size_t q, kv, l;  // element offsets of row 0 of the Q/O head, the K/V head, the L row
   int n;            // rows of the sequence
 };
-__device__ inline HeadRows head_rows(int bh, int group, int N, int D, const int* cu_seqlens, int H, int total) {
+__device__ inline HeadRows head_rows(int bh, int BH, int group, int N, int D, const int* cu_seqlens, int H,
+                                     int total) {
   HeadRows r;
   if (cu_seqlens) {
-    const int b = bh / H, h = bh - b * H;
+    const int B = BH / H;
+    const int h = bh / B, b = bh - h * B;
     // offsets clamped to [0, total], so no row outside the packed tensors is
     // ever addressed, whatever the array holds
     const int r0 = min(max(cu_seqlens[b], 0), total);
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(kThreads * G, (D >= 256 || G == 2) ? 1 : 2) void fw
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQ;
-  HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
+  HeadRows hr = head_rows(bh, BH, group, N, D, cu_seqlens, H, total);
   if (cu_seqlens) {
     N = hr.n;
     if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
@@ -671,7 +676,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
   const int q0 = qb * kBQ;
-  HeadRows hr = head_rows(bh, group, N, D, cu_seqlens, H, total);
+  HeadRows hr = head_rows(bh, BH, group, N, D, cu_seqlens, H, total);
   if (cu_seqlens) {
     N = hr.n;
     if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)

@@ -323,7 +323,12 @@ def time_varlen(fa, steps=10, warmup=2):
         return t0.elapsed_time(t1) / steps
 
     ms_v = timed(lambda: fa.fwd_varlen(q, k, v, cu, nmax, causal=True, out=o, lse=lse))
-    del q, k, v, o, lse
+    do = torch.randn(H, total, d, generator=gen, device=dev).to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_varlen_workspace_bytes(H, total, d), dtype=torch.uint8, device=dev)
+    ms_b = timed(lambda: fa.bwd_varlen(q, k, v, o, lse, do, cu, nmax, causal=True, dq=dq, dk=dk, dv=dv,
+                                       workspace=ws))
+    del q, k, v, o, lse, do, dq, dk, dv, ws
     torch.cuda.empty_cache()
     qp, kp, vp = (torch.randn(B, H, nmax, d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
     op = torch.empty_like(qp)
@@ -334,7 +339,8 @@ def time_varlen(fa, steps=10, warmup=2):
     label = f"causal bf16 varlen fwd B{B} H{H} d{d} total {total} (max {nmax})"
     return {label: {"ms": round(ms_v, 4), "TFLOP/s": round(f / (ms_v * 1e-3) / 1e12, 2),
                     "padded_ms": round(ms_p, 4), "padded_useful_TFLOP/s": round(f / (ms_p * 1e-3) / 1e12, 2),
-                    "inputs": "torch.randn seeded on the device (values do not affect the timing)"}}
+                    "inputs": "torch.randn seeded on the device (values do not affect the timing)"},
+            label.replace("fwd", "bwd"): {"ms": round(ms_b, 4), "TFLOP/s": round(2.5 * f / (ms_b * 1e-3) / 1e12, 2)}}
 
 
 def decode_inputs(w, threads=16):
