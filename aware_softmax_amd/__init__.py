@@ -18,6 +18,8 @@ __all__ = [
     "fa_fwd_gqa",
     "fa_fwd_varlen",
     "fwd_varlen",
+    "fwd_fp8",
+    "fa_fwd_fp8",
     "bwd_varlen",
     "fa_bwd_varlen",
     "bwd_varlen_workspace_bytes",
@@ -109,6 +111,9 @@ def _load() -> ctypes.CDLL:
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
     lib.fa_last_hip_error.restype = ci
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ctypes.c_float,
+                               ctypes.c_float, ctypes.c_float, vp]
+    lib.fa_fwd_fp8.restype = ci
     lib.fa_mfma_ceiling.argtypes = [vp, ci, ci, ci, vp]
     lib.fa_mfma_ceiling.restype = ci
     lib.fa_version.argtypes = []
@@ -208,6 +213,54 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
         stream = torch.cuda.current_stream(q.device)
     _check(fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, H, Hkv, N, d, causal, scale, dtype, stream.cuda_stream))
+    return out, lse
+
+
+def fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, causal, scale, q_descale, k_descale,
+               v_descale, stream) -> int:
+    """Raw call of the C entry point with integer device addresses; returns
+    the fa_status_t code."""
+    return _LIB.fa_fwd_fp8(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(Hkv), int(N), int(d),
+                           int(bool(causal)), float(scale), float(q_descale), float(k_descale), float(v_descale),
+                           stream)
+
+
+def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, causal: bool = True,
+            scale: float | None = None, out=None, lse=None, stream=None):
+    """O, L = attention forward of e4m3 inputs: q [B, H, N, d] and k, v
+    [B, Hkv, N, d] device tensors of torch.float8_e4m3fn (or uint8 holding
+    e4m3 bytes), element value = byte value x the tensor's descale factor.
+    Returns (o, lse): o bfloat16 [B, H, N, d], lse float32 [B, H, N].
+    d 64 or 128."""
+    import torch
+
+    allowed = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in allowed:
+            raise TypeError(f"{name} must be torch.float8_e4m3fn or uint8 e4m3 bytes, not {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != (B, Hkv, N, d):
+            raise ValueError(f"{name} must be [B, Hkv, N, d] with the B, N and d of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != (B, H, N, d) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [B, H, N, d] tensor")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
+                      causal, scale, q_descale, k_descale, v_descale, stream.cuda_stream))
     return out, lse
 
 

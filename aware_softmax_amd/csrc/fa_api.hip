@@ -122,6 +122,52 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
   return hip_status(e);
 }
 
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int N, int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+                       hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || H % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t elems = bh * N * d;
+  if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  const fa::TileConfig tile = fa::mfma_tile(64);  // the fp8 kernel's workgroup shape (128 rows, 4 or 8 waves)
+  const int64_t nqb = ((int64_t)N + tile.block_q - 1) / tile.block_q;
+  if (bh * nqb * 64 * 2 * tile.waves > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (!isfinite(scale) || !isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale) ||
+      !(q_descale > 0.f) || !(k_descale > 0.f) || !(v_descale > 0.f))
+    return FA_ERR_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t qbytes = (size_t)elems;                      // e4m3: one byte per element
+  const size_t kvbytes = (size_t)B * Hkv * N * d;
+  const size_t obytes = (size_t)elems * 2;                  // bf16 output
+  const size_t lbytes = (size_t)bh * N * sizeof(float);
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kvbytes) ||
+      ranges_overlap(o, obytes, v, kvbytes) || ranges_overlap(o, obytes, lse, lbytes) ||
+      ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+      ranges_overlap(lse, lbytes, v, kvbytes))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.BH = (int)bh;
+  p.N = N;
+  p.d = d;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.group = H / Hkv;
+  p.q_descale = q_descale;
+  p.k_descale = k_descale;
+  p.v_descale = v_descale;
+  return hip_status(fa::launch_fwd_fp8(p, stream));
+}
+
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int N, int d, int causal, float scale, fa_dtype_t dtype, hipStream_t stream) {
   return fa_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, dtype, stream);

@@ -461,6 +461,250 @@ __global__ __launch_bounds__(kThreads * G, (D >= 256 || G == 2) ? 1 : 2) void fw
 }
 
 // ---------------------------------------------------------------------------
+// FP8 forward (d = 64 or 128): q, k, v are OCP e4m3 bytes, each tensor with
+// one dequantisation factor (its values are byte value x factor).  The
+// attention computed is that of the dequantised tensors:
+//   * S^T = K Q^T on v_mfma_f32_32x32x64_f8f6f4 -- the products of two e4m3
+//     values are exact in fp32 -- with the Q and K factors folded into c;
+//   * V is widened to bf16 (exact: every e4m3 value is a bf16 value) while
+//     it is staged into LDS, so the softmax, P.V (P in bf16, as in the
+//     16-bit kernels) and the merge run as in fwd_mfma_kernel;
+//   * the V factor joins the final 1/l.
+// Same workgroup shape as fwd_mfma_kernel (4 waves x 32 query rows, 64-key
+// tiles, G = 2 splitting the key tiles on small grids).  The MFMA takes 64
+// contraction values per lane pair: lane (row, half) holds bytes
+// 64 t + 32 half .. + 31 of its row of K (A) or Q (B); any assignment of
+// contraction indices to (half, byte) gives the same sum as long as A and B
+// use the same one.
+template <int D, int G>
+struct LayoutF8 {
+  static constexpr int THREADS = kThreads * G;
+  static constexpr int KEYS = kBK * G;           // keys per stage
+  static constexpr int KSB = D + 16;             // K tile row stride in bytes (fp8)
+  static constexpr int VS = D + 16;              // V tile row stride in bf16 elements
+  static constexpr int K_BYTES = KEYS * KSB;
+  static constexpr int STAGE_BYTES = K_BYTES + KEYS * VS * 2;
+  static constexpr int CHUNKS_PER_ROW = D / 16;  // 16-byte chunks of fp8
+  static constexpr int CHUNKS_PER_THREAD = KEYS * D / 16 / THREADS;
+  static_assert(KEYS * D / 16 % THREADS == 0, "tile splits evenly over threads");
+  static_assert(STAGE_BYTES % 16 == 0, "stages stay 16-byte aligned");
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // formats of A and B: fp8 e4m3 (cbsz = blgp = 0); no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL, int G>
+__global__ __launch_bounds__(kThreads * G, G == 2 ? 1 : 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Qg, const uint8_t* __restrict__ Kg, const uint8_t* __restrict__ Vg,
+    __bf16* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate, float v_descale,
+    int group) {
+  using T = __bf16;
+  using Ly = LayoutF8<D, G>;
+  constexpr int DT8 = D / 64;  // 64-wide d steps of the QK^T contraction
+  constexpr int DB = D / 32;   // 32-wide d blocks of the output
+  __shared__ __attribute__((aligned(16))) char smem[2 * Ly::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = (tid >> 6) & (kWaves - 1);  // query rows of the wave
+  const int grp = G == 1 ? 0 : tid >> 8;       // key tiles of the wave
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  int bh, qb;
+  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
+  const int q0 = qb * kBQ;
+  const size_t head = (size_t)bh * N * D;                 // Q/O rows (elements = bytes for fp8)
+  const size_t kvhead = (size_t)(bh / group) * N * D;
+  const uint8_t* Qh = Qg + head;
+  const uint8_t* Kh = Kg + kvhead;
+  const uint8_t* Vh = Vg + kvhead;
+
+  // ---- Q fragments (B operand): 32 bytes of the lane's query row per d step
+  const int qw = q0 + wave * kRowsPerWave;
+  const int qi = qw + col;
+  i32x8 qf[DT8];
+#pragma unroll
+  for (int t = 0; t < DT8; ++t) {
+    if (qi < N) {
+      const u32x4* src = (const u32x4*)(Qh + (size_t)qi * D + 64 * t + 32 * half);
+      const u32x4 lo = src[0], hi = src[1];
+      qf[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
+      qf[t] = i32x8{};
+    }
+    if (negate) qf[t] ^= (int)0x80808080u;  // scale < 0: -Q (flips the sign bits; exact)
+  }
+
+  int nkt = (N + Ly::KEYS - 1) / Ly::KEYS;  // LDS stages
+  if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / Ly::KEYS + 1);
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) oacc[b] = f32x16{};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  // ---- global -> register prefetch (16 fp8 per chunk), register -> LDS
+  u32x4 kreg[Ly::CHUNKS_PER_THREAD], vreg[Ly::CHUNKS_PER_THREAD];
+  auto gload = [&](int j) {
+    const int kt0 = j * Ly::KEYS;
+#pragma unroll
+    for (int i = 0; i < Ly::CHUNKS_PER_THREAD; ++i) {
+      const int ci = tid + Ly::THREADS * i;
+      const int row = ci / Ly::CHUNKS_PER_ROW;
+      const int c16 = ci % Ly::CHUNKS_PER_ROW;
+      const int key = kt0 + row;
+      if (key < N) {
+        const size_t off = (size_t)key * D + c16 * 16;
+        kreg[i] = *(const u32x4*)(Kh + off);
+        vreg[i] = *(const u32x4*)(Vh + off);
+      } else {
+        kreg[i] = u32x4{};
+        vreg[i] = u32x4{};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* Kl = smem + buf * Ly::STAGE_BYTES;
+    T* Vl = (T*)(Kl + Ly::K_BYTES);
+#pragma unroll
+    for (int i = 0; i < Ly::CHUNKS_PER_THREAD; ++i) {
+      const int ci = tid + Ly::THREADS * i;
+      const int row = ci / Ly::CHUNKS_PER_ROW;
+      const int c16 = ci % Ly::CHUNKS_PER_ROW;
+      *(u32x4*)(Kl + row * Ly::KSB + c16 * 16) = kreg[i];
+      // 16 e4m3 -> 16 bf16 (exact): decode pairs to fp32, pack pairs to bf16
+      unsigned w[8];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(vreg[i][x], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(vreg[i][x], true);
+        w[2 * x] = __builtin_bit_cast(unsigned, cvt2<T>(lo[0], lo[1]));
+        w[2 * x + 1] = __builtin_bit_cast(unsigned, cvt2<T>(hi[0], hi[1]));
+      }
+      u32x4* dst = (u32x4*)(Vl + row * Ly::VS + c16 * 16);
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
+  };
+
+  const int tr_e = (lane & 15) >> 2;
+  const int tr_t = lane & 3;
+  const int tr_cg = (lane >> 4) & 1;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkt) gload(j + 1);
+    const int kt0 = j * Ly::KEYS + grp * kBK;
+    const bool skip = (CAUSAL && kt0 > qw + kRowsPerWave - 1) || (G > 1 && kt0 >= N);
+    if (!skip) {
+      const char* Kl = smem + buf * Ly::STAGE_BYTES + grp * kBK * Ly::KSB;
+      const T* Vl = (const T*)(smem + buf * Ly::STAGE_BYTES + Ly::K_BYTES) + grp * kBK * Ly::VS;
+
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const char* krow = Kl + (kb * 32 + col) * Ly::KSB + 32 * half;
+#pragma unroll
+        for (int t = 0; t < DT8; ++t) {
+          const u32x4 lo = *(const u32x4*)(krow + 64 * t);
+          const u32x4 hi = *(const u32x4*)(krow + 64 * t + 16);
+          const i32x8 kf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          s[kb] = mfma_f8(kf, qf[t], s[kb]);
+        }
+      }
+
+      float sv[32];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = s[0][r];
+        sv[16 + r] = s[1][r];
+      }
+      const bool need_mask = (CAUSAL && kt0 + kBK - 1 > qw) || (kt0 + kBK > N);
+      const int lim_causal = qi - kt0 - half * 4;
+      const int lim_n = N - kt0 - half * 4;
+      vec8<T> pfrag[4];
+      const float alpha = need_mask
+                              ? tile_softmax<true, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag)
+                              : tile_softmax<false, CAUSAL>(sv, c, lim_causal, lim_n, m_run, l_part, pfrag);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b) oacc[b] *= alpha;
+      }
+
+#pragma unroll
+      for (int u = 0; u < kBK / 16; ++u) {
+        const vec8<T> pf = pfrag[u];
+        const T* vrow = Vl + (u * 16 + half * 4 + tr_e) * Ly::VS + tr_cg * 16 + 4 * tr_t;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const vec8<T> vf = read_vt(vrow + b * 32, vrow + b * 32 + 8 * Ly::VS);
+          oacc[b] = mfma32(vf, pf, oacc[b]);
+        }
+      }
+    }
+    if (j + 1 < nkt) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if constexpr (G == 2) {
+    // Merge the two groups, as in fwd_mfma_kernel.
+    constexpr int NV = 16 * DB + 2;
+    static_assert(NV * kThreads * 4 <= (int)sizeof(smem), "merge buffer fits the stages");
+    float* xb = (float*)smem + wave * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xb[(b * 16 + r) * kThreads] = oacc[b][r];
+      xb[16 * DB * kThreads] = m_run;
+      xb[(16 * DB + 1) * kThreads] = l_part;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xb[16 * DB * kThreads];
+    const float l1 = xb[(16 * DB + 1) * kThreads];
+    const float mm = fmaxf(m_run, m1);
+    const float mu = mm == -INFINITY ? 0.f : mm;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mu);
+    const float a1 = __builtin_amdgcn_exp2f(m1 - mu);
+    l_part = a0 * l_part + a1 * l1;
+    m_run = mm;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[b][r] = a0 * oacc[b][r] + a1 * xb[(b * 16 + r) * kThreads];
+  }
+
+  // ---- epilogue: O = V factor x O~ / l -> bf16, L = ln2 (m + log2 l)
+  const float l_tot = swap_halves(l_part, false);
+  if (qi < N) {
+    const float inv = v_descale / l_tot;
+    T* orow = Og + head + (size_t)qi * D + half * 4;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        vec4<T> out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (T)(oacc[b][g * 4 + e] * inv);
+        *(vec4<T>*)(orow + b * 32 + g * 8) = out;
+      }
+    if (half == 0) Lg[(size_t)bh * N + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Helpers of the d = 128 kernel.
 
 constexpr float kRaise = 8.f;  // reference-max slack, log2 units (P <= 2^8)
@@ -1106,7 +1350,37 @@ hipError_t launch_t(const FwdParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_f8(const FwdParams& p, hipStream_t stream) {
+  const int nqb = (p.N + kBQ - 1) / kBQ;
+  const bool split = (int64_t)p.BH * nqb <= kSplitMaxBlocks;
+  // the Q and K factors join the softmax scale; a negative product runs
+  // as -Q with |c|
+  const float c_signed = p.scale * p.q_descale * p.k_descale * 1.44269504088896340736f;
+  const int negate = c_signed < 0.f ? 1 : 0;
+  const float c = negate ? -c_signed : c_signed;
+  dim3 grid(p.BH * nqb), block(split ? 2 * kThreads : kThreads);
+  const uint8_t* q = (const uint8_t*)p.q;
+  const uint8_t* k = (const uint8_t*)p.k;
+  const uint8_t* v = (const uint8_t*)p.v;
+  __bf16* o = (__bf16*)p.o;
+  float* lse = p.lse;
+  int bh = p.BH, n = p.N, group = p.group;
+  float vd = p.v_descale;
+  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &vd, &group};
+  const void* fn = split ? (const void*)fwd_fp8_kernel<D, CAUSAL, 2> : (const void*)fwd_fp8_kernel<D, CAUSAL, 1>;
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 }  // namespace
+
+hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
+  switch (p.d) {
+    case 64: return p.causal ? launch_f8<64, true>(p, stream) : launch_f8<64, false>(p, stream);
+    case 128: return p.causal ? launch_f8<128, true>(p, stream) : launch_f8<128, false>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 TileConfig mfma_tile(int d) {
   return d == 128 ? TileConfig{duo::kBQ, kBK, duo::kWaves} : TileConfig{kBQ, kBK, kWaves};

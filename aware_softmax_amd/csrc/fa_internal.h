@@ -26,6 +26,10 @@ struct FwdParams {
   const int* cu_seqlens = nullptr;
   int H = 0;
   int total = 0;
+  // FP8 forward only: q, k, v are e4m3 bytes whose values are byte x factor.
+  float q_descale = 1.f;
+  float k_descale = 1.f;
+  float v_descale = 1.f;
 };
 
 // Tile shape per (dtype, d).
@@ -103,6 +107,8 @@ int decode_rows_per_iter(int d, int heads_per_wg);
 // hipError_t a launch reported.
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams& p, hipStream_t stream);
+// e4m3 q, k, v (fixed length, d 64 or 128), bf16 o.
+hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream);

@@ -100,6 +100,31 @@ fa_status_t fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
                        fa_dtype_t dtype, hipStream_t stream);
 
 /*
+ * fa_fwd_fp8 -- the forward on 8-bit inputs ("FlashAttention: Move Less,
+ * Not Compute Less", section "FA1 to FA3", names FP8 as the next step;
+ * the pages fix no quantisation, so this entry point takes the plainest
+ * one): q, k, v hold OCP FP8 E4M3 bytes (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; 0x7F / 0xFF are NaN; largest finite 448), and each
+ * tensor has one dequantisation factor, so element x means byte(x) times
+ * its tensor's factor.  The result is the attention of the dequantised
+ * tensors, as fa_fwd_gqa computes it: S = scale (q_descale q)(k_descale k)^T
+ * with exact products and fp32 sums, P rounded to bf16 for P.V, V
+ * dequantised exactly to bf16, O = v_descale P V / l.
+ *   q         [in]  device, [B][H][N][d] e4m3 bytes, 16-byte aligned.
+ *   k, v      [in]  device, [B][Hkv][N][d] e4m3 bytes, 16-byte aligned.
+ *   o         [out] device, [B][H][N][d] bf16, 16-byte aligned.
+ *   lse       [out] device, [B][H][N] float32 (natural log), 4-byte aligned.
+ *   d         64 or 128 (else FA_ERR_UNSUPPORTED_HEADDIM).
+ *   q_descale, k_descale, v_descale  finite and > 0 (else FA_ERR_SCALE).
+ *   the other arguments and checks as for fa_fwd_gqa (outputs must not
+ *   overlap the inputs or each other: FA_ERR_ALIAS).
+ * Allocates nothing; one kernel is enqueued on `stream`.
+ */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, float scale,
+                       float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
+/*
  * fa_fwd_varlen -- the forward over a batch of B sequences of different
  * lengths packed without padding ("FlashAttention: Move Less, Not Compute
  * Less", "What It Changes--and What It Does Not": the reference

@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
     split_kv_partials,
     tiled_attention,
 )
+from .fp8 import attention_fp8, e4m3_to_f64  # noqa: F401

@@ -2,7 +2,8 @@
 
 This module holds no attention arithmetic: it draws i.i.d. N(0, 1) values
 from counter-addressed NumPy PCG64 streams and rounds them to bfloat16
-(round to nearest, ties to even) when a config asks for bf16 inputs.  Both
+(round to nearest, ties to even) when a config asks for bf16 inputs, or
+encodes 32 times them as OCP FP8 E4M3 codes for the 8-bit forward.  Both
 the fp64 oracle and the HIP path consume exactly the values produced here.
 
 Streams: one per (config, tensor, batch index, head index), seeded with the
@@ -104,6 +105,36 @@ def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
+# e4m3 inputs: the N(0, 1) draw times 32, rounded to OCP FP8 E4M3, so each
+# e4m3 tensor's dequantisation factor is 1/32 (|x| up to 14 is representable,
+# values near 1 keep 3 mantissa bits; N(0, 1) draws never saturate).
+E4M3_GAIN = 32.0
+E4M3_DESCALE = 1.0 / E4M3_GAIN
+
+
+def e4m3_round_bits(x: np.ndarray) -> np.ndarray:
+    """float -> OCP FP8 E4M3 codes (uint8): round to nearest, ties to even,
+    saturating at +-448 (exponent bias 7, 3 mantissa bits, subnormals
+    below 2^-6).  Inputs are finite."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    neg = np.signbit(np.asarray(x, dtype=np.float64))
+    a = np.minimum(a, 448.0)
+    # binade of a (subnormals share the quantum of the lowest binade, 2^-9)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.clip(e, -6, 8)
+    quantum = np.exp2(e - 3)
+    v = np.rint(a / quantum) * quantum  # np.rint: ties to even
+    v = np.minimum(v, 448.0)
+    # encode the rounded value (which may have moved up one binade)
+    ev = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    normal = v >= 2.0 ** -6
+    exp_field = np.where(normal, ev + 7, 0)
+    mant = np.where(normal, v / np.exp2(ev - 3) - 8, v / 2.0 ** -9)
+    code = (exp_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(v == 0, 0, code)
+    return (code | (neg.astype(np.int64) << 7)).astype(np.uint8)
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns -> the exactly equal fp32 values."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
@@ -124,10 +155,13 @@ def head_values(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dty
 
 
 def head_storage(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dtype: str) -> np.ndarray:
-    """One head's (n, d) tensor in storage form: uint16 bf16 bits, float16 or float32."""
+    """One head's (n, d) tensor in storage form: uint16 bf16 bits, uint8
+    e4m3 codes (of the draw times E4M3_GAIN), float16 or float32."""
     x = head_stream(config_id, tensor, b, h).standard_normal((n, d), dtype=np.float32)
     if dtype == "bf16":
         return bf16_round_bits(x)
+    if dtype == "e4m3":
+        return e4m3_round_bits(x * E4M3_GAIN)
     if dtype == "f16":
         return x.astype(np.float16)
     return x
@@ -135,8 +169,9 @@ def head_storage(config_id: int, tensor: str, b: int, h: int, n: int, d: int, dt
 
 def full_storage(config_id: int, tensor: str, B: int, H: int, N: int, d: int, dtype: str,
                  threads: int = 8) -> np.ndarray:
-    """The whole [B][H][N][d] tensor in storage form (uint16 bf16 bits, float16 or float32)."""
-    out = np.empty((B, H, N, d), dtype={"bf16": np.uint16, "f16": np.float16}.get(dtype, np.float32))
+    """The whole [B][H][N][d] tensor in storage form (uint16 bf16 bits, uint8
+    e4m3 codes, float16 or float32)."""
+    out = np.empty((B, H, N, d), dtype={"bf16": np.uint16, "f16": np.float16, "e4m3": np.uint8}.get(dtype, np.float32))
 
     def fill(bh):
         b, h = divmod(bh, H)

@@ -400,3 +400,22 @@ def test_single_hip_runtime_whatever_the_import_order():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr[-2000:]
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+# ------------------------------------------------------------ fa_fwd_fp8
+
+
+def test_fp8_validation_rejects_before_launch(fa):
+    good = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, B=1, H=2, Hkv=1, N=64,
+                d=128, causal=1, scale=0.1, qd=1.0, kd=1.0, vd=1.0)
+
+    def call(**over):
+        a = dict(good)
+        a.update(over)
+        return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                             a["causal"], a["scale"], a["qd"], a["kd"], a["vd"], None)
+    for over, code in ((dict(q=0), 1), (dict(lse=0), 1), (dict(N=0), 2), (dict(Hkv=3), 2), (dict(d=96), 4),
+                       (dict(d=32), 4), (dict(d=256), 4), (dict(qd=0.0), 6), (dict(kd=-1.0), 6),
+                       (dict(vd=float("inf")), 6), (dict(scale=float("nan")), 6), (dict(o=A + 0x3000008), 5),
+                       (dict(o=A + 0x1000), 8), (dict(lse=A + 0x3000100), 8)):
+        assert call(**over) == code, over

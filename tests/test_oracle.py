@@ -522,3 +522,80 @@ def test_pins_catch_planted_mistake(kind):
         except (AssertionError, ValueError, FloatingPointError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {kind}"
+
+
+# ------------------------------------------------------------ 8-bit inputs
+
+# OCP 8-bit floating point specification (OFP8), E4M3: (code, value).
+E4M3_PINS = [(0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0x30, 0.5),
+             (0x38, 1.0), (0x39, 1.125), (0x3C, 1.5), (0x40, 2.0), (0x58, 16.0), (0x77, 240.0),
+             (0x7E, 448.0), (0x80, -0.0), (0xB8, -1.0), (0xFE, -448.0)]
+
+
+@pytest.mark.parametrize("code,value", E4M3_PINS)
+def test_e4m3_decode_pins(code, value):
+    got = float(oracle.e4m3_to_f64(np.array([code], dtype=np.uint8))[0])
+    assert got == value and math.copysign(1.0, got) == math.copysign(1.0, value)
+
+
+def test_e4m3_nan_codes_and_order():
+    vals = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF]) and int(np.isnan(vals).sum()) == 2
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)                     # codes 0x00..0x7E increase strictly
+    assert np.array_equal(vals[0x80:0xFF], -pos)        # sign bit negates
+
+
+def test_e4m3_values_are_bf16_values():
+    """Every finite E4M3 value is a bfloat16 value: the 8-bit forward may
+    widen V to bf16 without rounding."""
+    vals = oracle.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    fin = vals[np.isfinite(vals)]
+    as_bf16 = torch.from_numpy(fin).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(as_bf16, fin)
+
+
+def test_e4m3_codes_round_trip_through_the_input_encoder():
+    import synthetic
+
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    back = synthetic.e4m3_round_bits(oracle.e4m3_to_f64(codes))
+    assert np.array_equal(back, codes)
+
+
+def test_e4m3_encoder_rounds_to_nearest_even():
+    import synthetic
+
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(20000) * 40
+    codes = synthetic.e4m3_round_bits(x)
+    dec = oracle.e4m3_to_f64(codes)
+    grid = oracle.e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))  # non-negative finite values
+    a = np.minimum(np.abs(x), 448.0)
+    nearest = grid[np.argmin(np.abs(grid[None, :] - a[:, None]), axis=1)]
+    assert np.array_equal(np.abs(dec), nearest)  # no ties occur in continuous draws
+
+
+def test_fp8_attention_constant_keys_give_mean_of_v():
+    """All keys equal: every visible score of a row is the same, so O is the
+    mean of the visible dequantised V rows (closed form), whatever the Q and
+    K factors; the V factor scales it."""
+    rng = np.random.default_rng(3)
+    n, d = 37, 16
+    q = rng.integers(0, 0x7F, size=(n, d)).astype(np.uint8)
+    k = np.tile(rng.integers(0, 0x7F, size=(1, d)).astype(np.uint8), (n, 1))
+    v = rng.integers(0, 0x7F, size=(n, d)).astype(np.uint8)
+    vd = oracle.e4m3_to_f64(v) * 0.25
+    for causal in (False, True):
+        o, _ = oracle.attention_fp8(q, k, v, 0.5, 3.0, 0.25, causal, 0.125)
+        for i in (0, 5, n - 1):
+            ref = vd[: i + 1].mean(axis=0) if causal else vd.mean(axis=0)
+            assert np.allclose(o[i], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_attention_q_factor_acts_as_scale():
+    rng = np.random.default_rng(4)
+    q, k, v = (rng.integers(0, 0x7F, size=(20, 8)).astype(np.uint8) for _ in range(3))
+    o1, l1 = oracle.attention_fp8(q, k, v, 2.0, 0.5, 1.0, True, 0.1)
+    o2, l2 = oracle.attention_fp8(q, k, v, 1.0, 1.0, 1.0, True, 0.1)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-14) and np.allclose(l1, l2, rtol=1e-12, atol=1e-12)
