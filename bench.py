@@ -284,6 +284,43 @@ def time_f16(fa, steps=10, warmup=2):
     return out
 
 
+def time_fp8(fa, steps=10, warmup=3):
+    """fa_fwd_fp8 (e4m3 inputs, bf16 output) on B8 H32 N8192 d128 and
+    B2 H16 N4096 d128 causal; FLOPs counted as for the bf16 forward."""
+    import numpy as np
+    import torch
+
+    import synthetic
+
+    out = {}
+    for (B, H, N, d) in ((8, 32, 8192, 128), (2, 16, 4096, 128)):
+        w = synthetic.Workload(3, "", B, H, N, d, "e4m3", True)
+        q, k, v = (torch.from_numpy(synthetic.full_storage(w.config_id, t, B, H, N, d, "e4m3", threads=16)).cuda()
+                   for t in ("q", "k", "v"))
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        ds = synthetic.E4M3_DESCALE
+
+        def step():
+            fa.fwd_fp8(q, k, v, ds, ds, ds, causal=True, scale=w.scale, out=o, lse=lse)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        out[f"causal fp8 (e4m3) fwd B{B} H{H} N{N} d{d}"] = {
+            "ms": round(ms, 4), "TFLOP/s": round(attention_flops(B, H, N, d, True) / (ms * 1e-3) / 1e12, 2)}
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
 def varlen_lengths(seed=0xFA0, B=16, lo=256, hi=8192):
     """Seeded sequence lengths of a packed batch: log-uniform in [lo, hi]."""
     import numpy as np
@@ -757,6 +794,7 @@ def main():
             torch.cuda.empty_cache()
         extra.update(time_gqa(fa))
         extra.update(time_f16(fa))
+        extra.update(time_fp8(fa))
         extra.update(time_varlen(fa))
         for cid in (6, 7, 8):
             dw = synthetic.DECODE_WORKLOADS[cid]
