@@ -14,6 +14,8 @@ copy (the byte-count calibration kernel) followed by --steps launches.
 --profile-decode: --steps split-K decode calls on B=8 H=32 N=32768 d=128.
 --profile-bwd: --steps backward calls on B=2 H=16 N=4096 d=128 causal (the
 forward-plus-backward workload), printed as one JSON line.
+--profile-fp8: --steps fa_fwd_fp8 calls on B8 H32 N8192 and B2 H16 N4096
+d=128 causal (e4m3 inputs).
 
 Next to the timed launches the line carries: the median, min and max
 launch time; a cold-cache timing (1 GiB written between launches, more
@@ -635,6 +637,8 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run --steps fa_decode calls on B=8 H=32 N=32768 d=128 (for rocprofv3)")
+    ap.add_argument("--profile-fp8", action="store_true",
+                    help="run the fp8 legs (B8 H32 N8192 and B2 H16 N4096 d=128 causal, for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="run --steps fa_bwd calls on B=2 H=16 N=4096 d=128 causal (for rocprofv3)")
     ap.add_argument("--cpu-per-core", nargs=2, metavar=("WORKLOAD", "SECONDS"), help=argparse.SUPPRESS)
@@ -661,6 +665,10 @@ def main():
         dq_, dk_, dv_ = decode_inputs(dw)
         r = time_decode(fa, dw, dq_, dk_, dv_, 0, args.steps, 2)
         print(json.dumps({"profile-decode": dw.name, **r}), flush=True)
+        return
+
+    if args.profile_fp8:
+        print(json.dumps({"profile-fp8": time_fp8(fa, steps=args.steps, warmup=2)}), flush=True)
         return
 
     if args.profile_bwd:
