@@ -249,13 +249,17 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
 // and O^T to group 0 through LDS, which rescales both to the common max
 // (the merge rule of the online softmax) and writes the output.
 //
+// Register budget (launch bound): 4 workgroups per CU at d = 32, 3 at
+// d = 64, 2 up to d = 128 -- without it hipcc gave the non-causal d = 64
+// kernel 178 VGPRs (two workgroups per CU) and ran it 15 % slower.
+//
 // OS = 2 (d = 256): 8 waves, two per 32 query rows; both compute S and the
 // softmax of their rows, and each keeps O^T for one half of d (64 fp32 per
 // lane instead of 128), which fits two waves per SIMD without spilling.
 // Q.K^T is done twice (1.5x the MFMA work); measured 521 -> 640 TFLOP/s on
 // B8 H32 N8192 d256 causal (same box, identical output bits).
 template <class T, int D, bool CAUSAL, int G, int OS = 1>
-__global__ __launch_bounds__(kThreads * G * OS, (D >= 256 || G == 2 || OS == 2) ? 1 : 2) void fwd_mfma_kernel(
+__global__ __launch_bounds__(kThreads * G * OS, (D >= 256 || G == 2 || OS == 2) ? 1 : D <= 32 ? 4 : D <= 64 ? 3 : 2) void fwd_mfma_kernel(
     const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
     T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group, const int* __restrict__ cu_seqlens, int H, int total) {
