@@ -582,8 +582,11 @@ struct DqLayout {
 //   V  P = 2^(c S^T), dS^T = P dP^T, packed to the element type;
 //   C  dQ^T += K^T dS^T                               (2 KB DB MFMAs, transposing reads).
 // Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
+// Three waves per SIMD at d = 32 (+8 % on B2 H16 N4096 d32 causal); at
+// d = 64 the same bound costs spills and 5 %.
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(D <= 32 ? 3 : 2, D <= 32 ? 3 : 2)))
 void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                    const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
                    T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group,
