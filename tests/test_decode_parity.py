@@ -231,3 +231,9 @@ def test_cache_seqlens(fa, num_splits, d):
                                                   vals(st["v"][b, h // 4][:n_b]), False, scale)
             assert np.all(np.abs(got_o[b, h] - ref_o[0]) <= 2.0 ** -8 * np.abs(ref_o[0]) + 1e-4), (b, h)
             assert abs(got_l[b, h] - ref_l[0]) <= 2e-4 * max(1.0, abs(ref_l[0])), (b, h)
+
+
+def test_decode_million_key_cache(fa):
+    """A 2^20-row cache (B1 H2 Hkv1 d128, 512 MiB of K and V): many keys per
+    split at the automatic plan, the sums and maxima over a long range."""
+    run(fa, 7100, 1, 2, 1, 1 << 20, 128)

@@ -399,3 +399,11 @@ def test_varlen_matches_fixed_length(fa):
     torch.cuda.synchronize()
     assert torch.equal(pack(o).view(torch.int16), o2.view(torch.int16))
     assert torch.equal(lse.permute(1, 0, 2).reshape(H, B * N), l2)
+
+
+def test_long_sequence_sampled(fa):
+    """B1 H2 N131072 d128 causal (twice the longest workload): 64 seeded
+    rows plus edge rows, last row included, in each head."""
+    rows = synthetic.sample_rows(1990, 131072, 64)
+    assert 131071 in set(int(r) for r in rows)
+    assert_close(run_case(fa, 1990, 1, 2, 131072, 128, "bf16", True, rows=rows), "bf16")
