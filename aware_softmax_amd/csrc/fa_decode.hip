@@ -47,6 +47,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kMfmaMaxHeads = 32;  // heads per workgroup of the MFMA decode (one MFMA column block)
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Row split per head dim: CPL 16-byte chunks per lane, LPR lanes per row
@@ -342,10 +343,267 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
 }
 
 // Largest divisor of the query-head group that one workgroup serves.
+// d = 128 with 5 or more heads per key/value head runs the MFMA decode,
+// which serves up to 32 heads of a group per workgroup.  Measured on B8
+// N32768 d128 (same box): 8 heads per key/value head 4.1-4.3 -> 6.0-6.3
+// TB/s, 6 heads 5.1 -> 6.2; at 4 heads the VALU kernel stays ahead (6.45
+// against 6.3 TB/s).
+bool mfma_path(int group, int d) { return d == 128 && group >= 5; }
+
 int heads_per_wg(int group, int d) {
+  if (mfma_path(group, d)) {
+    for (int g = kMfmaMaxHeads; g > 1; --g)
+      if (group % g == 0) return g;
+  }
   for (int g = max_group_rt(d); g > 1; --g)
     if (group % g == 0) return g;
   return 1;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA decode (d = 128, 5 to 32 query heads of a group per workgroup).  The
+// VALU kernel above spends about 11 VALU instructions per head and key on
+// the dot product, its lane reduction, the softmax and P.V; with 8 heads per
+// key/value head that issue rate, not HBM, bounds it.  Here the group's
+// heads are the 32 query columns of the forward's tiles: S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16 (columns past the group are zero),
+// the softmax runs in-lane per head column as in the forward, and P is
+// rounded to the element type for the MFMA (the forward's precision, not
+// the VALU kernel's fp32 P).  Each of the 4 waves takes its own 32-key tile
+// of a 128-key LDS stage (staged through registers, the next stage's loads
+// in flight during the current one); the waves' (m, l, o~) are merged once
+// at the end and written as the split's partial for the combine kernel.
+namespace mf {
+constexpr int D = 128;
+constexpr int kKeys = 32;                 // keys per wave tile
+constexpr int kStage = kWaves * kKeys;    // keys per LDS stage
+constexpr int KS = D + 8;                 // K row stride (elements, +16 B)
+constexpr int VS = D + 16;                // V row stride (elements, +32 B)
+constexpr int K_ELEMS = kStage * KS;
+constexpr int STAGE = K_ELEMS + kStage * VS;
+constexpr int CPR = D / 8;                // 16-byte chunks per row
+constexpr int CPT = kStage * CPR / kThreads;
+static_assert(kStage * CPR % kThreads == 0, "stage splits evenly over threads");
+}  // namespace mf
+
+template <class T>
+using vec8 = T __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x16 mfma32(const vec8<__bf16>& a, const vec8<__bf16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const vec8<_Float16>& a, const vec8<_Float16>& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// Lane l receives x from lane l ^ 32; returns the max or the sum of the two.
+__device__ __forceinline__ float swap_halves(float x, bool want_max) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]);
+  const float b = __uint_as_float(r[1]);
+  return want_max ? fmaxf(a, b) : a + b;
+}
+// Two transposing 8-byte LDS reads -> the 8 elements of one V^T operand.
+template <class T>
+__device__ __forceinline__ vec8<T> read_vt(const T* p0, const T* p1) {
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  return __builtin_bit_cast(vec8<T>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int* __restrict__ seqlens,
+    float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c,
+    int G) {
+  using namespace mf;
+  constexpr float kNegInf = -__builtin_inff();
+  constexpr int DT = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) T smem[STAGE];
+
+  const int group = H / Hkv;
+  const int n_hg = group / G;
+  int wg = blockIdx.x;
+  const int s = wg % S;
+  wg /= S;
+  const int hg = wg % n_hg;
+  const int bhk = wg / n_hg;  // b * Hkv + hk
+  const int b = bhk / Hkv;
+  const int hk = bhk - b * Hkv;
+  const int h0 = hk * group + hg * G;  // first query head of this workgroup
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 31;   // head column h0 + col
+  const int half = lane >> 5;
+
+  // Q^T fragments (B operand): head h0 + col, d = 16 t + 8 half .. + 7.
+  vec8<T> qf[DT];
+  if (col < G) {
+    const vec8<T>* src = (const vec8<T>*)(q + ((size_t)b * H + h0 + col) * D + half * 8);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) qf[t] = vec8<T>{};
+  }
+
+  const int n_b = seqlens ? min(max(seqlens[b], 0), N) : N;
+  const int k_begin = s * chunk;
+  const int k_end = min(n_b, k_begin + chunk);
+  const int nst = k_end > k_begin ? (k_end - k_begin + kStage - 1) / kStage : 0;
+  const size_t head_off = (size_t)bhk * N * D;
+  const T* kh = k + head_off;
+  const T* vh = v + head_off;
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int bb = 0; bb < DB; ++bb) oacc[bb] = f32x16{};
+  float m_run = kNegInf;
+  float l_part = 0.f;
+
+  vec8<T> kreg[CPT], vreg[CPT];
+  auto gload = [&](int j) {
+    const int r0 = k_begin + j * kStage;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + kThreads * i;
+      const int row = ci / CPR;
+      const int c8 = ci % CPR;
+      const int key = r0 + row;
+      if (key < k_end) {
+        const size_t off = (size_t)key * D + c8 * 8;
+        kreg[i] = __builtin_nontemporal_load((const vec8<T>*)(kh + off));
+        vreg[i] = __builtin_nontemporal_load((const vec8<T>*)(vh + off));
+      } else {
+        kreg[i] = vec8<T>{};
+        vreg[i] = vec8<T>{};
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ci = tid + kThreads * i;
+      const int row = ci / CPR;
+      const int c8 = ci % CPR;
+      *(vec8<T>*)(smem + row * KS + c8 * 8) = kreg[i];
+      *(vec8<T>*)(smem + K_ELEMS + row * VS + c8 * 8) = vreg[i];
+    }
+  };
+
+  const int tr_e = (lane & 15) >> 2;
+  const int tr_t = lane & 3;
+  const int tr_cg = (lane >> 4) & 1;
+  const vec2<T> one = vec2<T>{(T)1.0f, (T)1.0f};
+
+  if (nst > 0) {
+    gload(0);
+    lstore();
+  }
+  __syncthreads();
+  for (int j = 0; j < nst; ++j) {
+    if (j + 1 < nst) gload(j + 1);
+    const int kt0 = k_begin + j * kStage + wave * kKeys;  // this wave's 32 keys
+    if (kt0 < k_end) {
+      // S^T[key][head]: register r of lane (col, half) is key kt0 + 8 (r/4) + 4 half + r%4.
+      const T* krow = smem + (wave * kKeys + col) * KS + half * 8;
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) sacc = mfma32(*(const vec8<T>*)(krow + 16 * t), qf[t], sacc);
+      const int lim = k_end - kt0 - half * 4;  // key offsets >= lim lie past the split
+      float sv[16];  // scaled scores (log2 units); c may be negative
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        sv[r] = off < lim ? sacc[r] * c : kNegInf;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = swap_halves(mx, true);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float lsum = l_part * alpha;
+      vec8<T> pf[2];  // B operands of the two 16-key steps
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        unsigned w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float x0 = sv[u * 8 + e], x1 = sv[u * 8 + e + 1];
+          const float p0 = x0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x0 - m_use);
+          const float p1 = x1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x1 - m_use);
+          const vec2<T> pr = __builtin_convertvector((f32x2){p0, p1}, vec2<T>);
+          lsum = dot2(T{}, __builtin_bit_cast(unsigned, pr), __builtin_bit_cast(unsigned, one), lsum);
+          w[e >> 1] = __builtin_bit_cast(unsigned, pr);
+        }
+        pf[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
+      }
+      l_part = lsum;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) oacc[bb] *= alpha;
+      }
+      const T* vl = smem + K_ELEMS + wave * kKeys * VS;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const T* vrow = vl + (u * 16 + half * 4 + tr_e) * VS + tr_cg * 16 + 4 * tr_t;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) oacc[bb] = mfma32(read_vt(vrow + bb * 32, vrow + bb * 32 + 8 * VS), pf[u], oacc[bb]);
+      }
+    }
+    __syncthreads();
+    if (j + 1 < nst) lstore();
+    __syncthreads();
+  }
+
+  // Merge the 4 waves: [16 DB + 2][4 waves][64 lanes] fp32 in the stage
+  // (free after the loop's last barrier); wave w then merges d block w.
+  constexpr int NV = 16 * DB + 2;
+  static_assert(NV * kThreads * 4 <= (int)sizeof(smem), "merge buffer fits the stage");
+  static_assert(DB == kWaves, "one output block per wave");
+  float* xb = (float*)smem;
+#pragma unroll
+  for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xb[(bb * 16 + r) * kThreads + tid] = oacc[bb][r];
+  xb[16 * DB * kThreads + tid] = m_run;
+  xb[(16 * DB + 1) * kThreads + tid] = l_part;
+  __syncthreads();
+  float mw[kWaves], mm = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    mw[w] = xb[16 * DB * kThreads + w * 64 + lane];
+    mm = fmaxf(mm, mw[w]);
+  }
+  const float mref = mm == kNegInf ? 0.f : mm;  // no key in the split: all weights 0
+  float ll = 0.f, oo[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) oo[r] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float wt = __builtin_amdgcn_exp2f(mw[w] - mref);
+    ll = fmaf(wt, xb[(16 * DB + 1) * kThreads + w * 64 + lane], ll);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oo[r] = fmaf(wt, xb[(wave * 16 + r) * kThreads + w * 64 + lane], oo[r]);
+  }
+  const float l_tot = swap_halves(ll, false);
+  if (col < G) {
+    const size_t row = ((size_t)b * H + h0 + col) * S + s;
+    float* dst = part_o + row * D + wave * 32 + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *(float4*)(dst + 8 * g) = make_float4(oo[4 * g], oo[4 * g + 1], oo[4 * g + 2], oo[4 * g + 3]);
+    if (wave == 0 && half == 0) {
+      part_ml[row * 2] = mm;
+      part_ml[row * 2 + 1] = l_tot;
+    }
+  }
 }
 
 template <int D>
@@ -363,6 +621,7 @@ int rows_per_iter_rt(int G) {
 }
 
 int rows_per_iter_d(int d, int G) {
+  if (d == 128 && G >= 5) return mf::kStage;  // the MFMA decode's LDS stage
   switch (d) {
     case 32: return rows_per_iter_rt<32>(G);
     case 64: return rows_per_iter_rt<64>(G);
@@ -387,8 +646,26 @@ hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t s
   return hipGetLastError();
 }
 
+template <class T>
+hipError_t launch_mfma(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
+  const float c = p.scale * kLog2e;
+  float* po = (float*)p.workspace;
+  float* pml = (float*)((char*)p.workspace + plan.ml_offset);
+  hipLaunchKernelGGL((decode_mfma_kernel<T>), dim3(plan.split_wgs), dim3(kThreads), 0, stream, (const T*)p.q,
+                     (const T*)p.k, (const T*)p.v, p.seqlens, po, pml, p.H, p.Hkv, p.N, plan.splits, plan.chunk, c,
+                     plan.heads_per_wg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, mf::D>), dim3(p.B * p.H), dim3(mf::D), 0, stream, (const float*)po,
+                     (const float*)pml, (T*)p.o, p.lse, plan.splits);
+  return hipGetLastError();
+}
+
 template <class T, int D>
 hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (plan.heads_per_wg >= 5) return launch_mfma<T>(p, plan, stream);
+  }
   if constexpr (max_group<D>() == 4) {
     switch (plan.heads_per_wg) {
       case 1: return launch_g<T, D, 1>(p, plan, stream);

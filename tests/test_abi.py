@@ -235,6 +235,11 @@ def test_decode_plan_values(fa):
     assert fa.decode_plan(1, 32, 32, 32768, 128)[:2] == (16, 2048)
     # four query heads per key/value head: one workgroup serves all four
     assert fa.decode_plan(8, 32, 8, 32768, 128)[:2] == (8, 4096)
+    # 8 heads per key/value head (MFMA decode, 128-key stages): 64 workgroups
+    # per split, 8 splits of 4096 keys
+    assert fa.decode_plan(8, 64, 8, 32768, 128)[:2] == (8, 4096)
+    # 40 heads per key/value head: two workgroups of 20 heads each
+    assert fa.decode_plan(1, 40, 1, 4096, 128)[:2] == (32, 128)
     # one split: one workgroup walks the whole cache
     assert fa.decode_plan(8, 32, 32, 32768, 128, 1)[:2] == (1, 32768)
     # requests beyond the number of chunks are reduced
