@@ -804,8 +804,8 @@ def main():
         extra.update(time_f16(fa))
         extra.update(time_fp8(fa))
         extra.update(time_varlen(fa))
-        for cid in (6, 7, 8):
-            dw = synthetic.DECODE_WORKLOADS[cid]
+        gqa8 = synthetic.DecodeWorkload(8, "decode bf16 B8 H64 Hkv8 N32768 d128", 8, 64, 8, 32768, 128)
+        for dw in [synthetic.DECODE_WORKLOADS[cid] for cid in (6, 7, 8)] + [gqa8]:
             dq_, dk_, dv_ = decode_inputs(dw)
             for ns, tag in ((0, "split-K"), (1, "unsplit")):
                 # 200 untimed calls: the first ~100 calls after the inputs
