@@ -220,6 +220,13 @@ def test_f16_decode_long(fa):
     run(fa, 7990, 2, 32, 8, 32768, 128, dtype="f16", heads=synthetic.sample_heads(7990, 2, 32, 8))
 
 
+@pytest.mark.parametrize("n", [1, 200, 4097])
+@pytest.mark.parametrize("num_splits", [0, 1])
+def test_f16_decode_mfma_groups(fa, n, num_splits):
+    """fp16 through the MFMA decode (8 heads per key/value head, d = 128)."""
+    run(fa, 7995 + n, 2, 16, 2, n, 128, dtype="f16", num_splits=num_splits)
+
+
 # ------------------------------------------------------------ per-sequence cache lengths
 
 
