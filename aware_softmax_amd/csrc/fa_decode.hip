@@ -343,12 +343,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
 }
 
 // Largest divisor of the query-head group that one workgroup serves.
-// d = 128 with 5 or more heads per key/value head runs the MFMA decode,
+// d = 64 or 128 with 5 or more heads per key/value head runs the MFMA decode,
 // which serves up to 32 heads of a group per workgroup.  Measured on B8
 // N32768 d128 (same box): 8 heads per key/value head 4.1-4.3 -> 6.0-6.3
-// TB/s, 6 heads 5.1 -> 6.2; at 4 heads the VALU kernel stays ahead (6.45
-// against 6.3 TB/s).
-bool mfma_path(int group, int d) { return d == 128 && group >= 5; }
+// TB/s, 6 heads 5.1 -> 6.2 (d = 64, 8 heads: 3.8 -> 5.2-5.5); at 4 heads
+// the VALU kernel stays ahead (6.45 against 6.3 TB/s).
+bool mfma_path(int group, int d) { return (d == 64 || d == 128) && group >= 5; }
 
 int heads_per_wg(int group, int d) {
   if (mfma_path(group, d)) {
@@ -361,7 +361,7 @@ int heads_per_wg(int group, int d) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA decode (d = 128, 5 to 32 query heads of a group per workgroup).  The
+// MFMA decode (d = 64 or 128, 5 to 32 query heads of a group per workgroup).  The
 // VALU kernel above spends about 11 VALU instructions per head and key on
 // the dot product, its lane reduction, the softmax and P.V; with 8 heads per
 // key/value head that issue rate, not HBM, bounds it.  Here the group's
@@ -374,16 +374,18 @@ int heads_per_wg(int group, int d) {
 // in flight during the current one); the waves' (m, l, o~) are merged once
 // at the end and written as the split's partial for the combine kernel.
 namespace mf {
-constexpr int D = 128;
-constexpr int kKeys = 32;                 // keys per wave tile
-constexpr int kStage = kWaves * kKeys;    // keys per LDS stage
-constexpr int KS = D + 8;                 // K row stride (elements, +16 B)
-constexpr int VS = D + 16;                // V row stride (elements, +32 B)
-constexpr int K_ELEMS = kStage * KS;
-constexpr int STAGE = K_ELEMS + kStage * VS;
-constexpr int CPR = D / 8;                // 16-byte chunks per row
-constexpr int CPT = kStage * CPR / kThreads;
-static_assert(kStage * CPR % kThreads == 0, "stage splits evenly over threads");
+constexpr int kKeys = 32;               // keys per wave tile
+constexpr int kStage = kWaves * kKeys;  // keys per LDS stage
+template <int D>
+struct Layout {
+  static constexpr int KS = D + 8;   // K row stride (elements, +16 B)
+  static constexpr int VS = D + 16;  // V row stride (elements, +32 B)
+  static constexpr int K_ELEMS = kStage * KS;
+  static constexpr int STAGE = K_ELEMS + kStage * VS;
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static constexpr int CPT = kStage * CPR / kThreads;
+  static_assert(kStage * CPR % kThreads == 0, "stage splits evenly over threads");
+};
 }  // namespace mf
 
 template <class T>
@@ -414,12 +416,14 @@ __device__ __forceinline__ vec8<T> read_vt(const T* p0, const T* p1) {
   return __builtin_bit_cast(vec8<T>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <class T>
+template <class T, int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int* __restrict__ seqlens,
     float* __restrict__ part_o, float* __restrict__ part_ml, int H, int Hkv, int N, int S, int chunk, float c,
     int G) {
   using namespace mf;
+  using Ly = Layout<D>;
+  constexpr int KS = Ly::KS, VS = Ly::VS, K_ELEMS = Ly::K_ELEMS, STAGE = Ly::STAGE, CPR = Ly::CPR, CPT = Ly::CPT;
   constexpr float kNegInf = -__builtin_inff();
   constexpr int DT = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) T smem[STAGE];
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
   // (free after the loop's last barrier); wave w then merges d block w.
   constexpr int NV = 16 * DB + 2;
   static_assert(NV * kThreads * 4 <= (int)sizeof(smem), "merge buffer fits the stage");
-  static_assert(DB == kWaves, "one output block per wave");
+  static_assert(DB <= kWaves, "at most one output block per wave");
   float* xb = (float*)smem;
 #pragma unroll
   for (int bb = 0; bb < DB; ++bb)
@@ -590,11 +594,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
   for (int w = 0; w < kWaves; ++w) {
     const float wt = __builtin_amdgcn_exp2f(mw[w] - mref);
     ll = fmaf(wt, xb[(16 * DB + 1) * kThreads + w * 64 + lane], ll);
+    if (wave < DB) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oo[r] = fmaf(wt, xb[(wave * 16 + r) * kThreads + w * 64 + lane], oo[r]);
+      for (int r = 0; r < 16; ++r) oo[r] = fmaf(wt, xb[(wave * 16 + r) * kThreads + w * 64 + lane], oo[r]);
+    }
   }
   const float l_tot = swap_halves(ll, false);
-  if (col < G) {
+  if (wave < DB && col < G) {
     const size_t row = ((size_t)b * H + h0 + col) * S + s;
     float* dst = part_o + row * D + wave * 32 + 4 * half;
 #pragma unroll
@@ -621,7 +627,7 @@ int rows_per_iter_rt(int G) {
 }
 
 int rows_per_iter_d(int d, int G) {
-  if (d == 128 && G >= 5) return mf::kStage;  // the MFMA decode's LDS stage
+  if ((d == 64 || d == 128) && G >= 5) return mf::kStage;  // the MFMA decode's LDS stage
   switch (d) {
     case 32: return rows_per_iter_rt<32>(G);
     case 64: return rows_per_iter_rt<64>(G);
@@ -646,25 +652,25 @@ hipError_t launch_g(const DecodeParams& p, const DecodePlan& plan, hipStream_t s
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, int D>
 hipError_t launch_mfma(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
   const float c = p.scale * kLog2e;
   float* po = (float*)p.workspace;
   float* pml = (float*)((char*)p.workspace + plan.ml_offset);
-  hipLaunchKernelGGL((decode_mfma_kernel<T>), dim3(plan.split_wgs), dim3(kThreads), 0, stream, (const T*)p.q,
+  hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(plan.split_wgs), dim3(kThreads), 0, stream, (const T*)p.q,
                      (const T*)p.k, (const T*)p.v, p.seqlens, po, pml, p.H, p.Hkv, p.N, plan.splits, plan.chunk, c,
                      plan.heads_per_wg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<T, mf::D>), dim3(p.B * p.H), dim3(mf::D), 0, stream, (const float*)po,
+  hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(p.B * p.H), dim3(D), 0, stream, (const float*)po,
                      (const float*)pml, (T*)p.o, p.lse, plan.splits);
   return hipGetLastError();
 }
 
 template <class T, int D>
 hipError_t launch_d(const DecodeParams& p, const DecodePlan& plan, hipStream_t stream) {
-  if constexpr (D == 128) {
-    if (plan.heads_per_wg >= 5) return launch_mfma<T>(p, plan, stream);
+  if constexpr (D == 64 || D == 128) {
+    if (plan.heads_per_wg >= 5) return launch_mfma<T, D>(p, plan, stream);
   }
   if constexpr (max_group<D>() == 4) {
     switch (plan.heads_per_wg) {

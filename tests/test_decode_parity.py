@@ -51,14 +51,14 @@ def vals(x):
 def mfma_decode(d, group):
     """Whether fa_decode runs these sizes on its MFMA kernel (P rounded to
     the element type) rather than the VALU kernel (P in fp32)."""
-    return d == 128 and group >= 5
+    return d in (64, 128) and group >= 5
 
 
 def check_heads(st, o, lse, heads, H, Hkv, scale):
     group = H // Hkv
     d = st["q"].shape[-1]
     u = ROUND["f16" if st["q"].dtype == np.float16 else "bf16"]
-    # d = 128 with 5 or more heads per key/value head runs on MFMA and rounds
+    # d = 64 or 128 with 5 or more heads per key/value head runs on MFMA and rounds
     # P to the element type (relative error <= u per probability, the row
     # sum taken over the rounded values): o moves by at most
     # u / (1 - u) * max_j |v_j - o| <= 2u max_j |v_j - o| on top of the
@@ -222,9 +222,18 @@ def test_f16_decode_long(fa):
 
 @pytest.mark.parametrize("n", [1, 200, 4097])
 @pytest.mark.parametrize("num_splits", [0, 1])
-def test_f16_decode_mfma_groups(fa, n, num_splits):
-    """fp16 through the MFMA decode (8 heads per key/value head, d = 128)."""
-    run(fa, 7995 + n, 2, 16, 2, n, 128, dtype="f16", num_splits=num_splits)
+@pytest.mark.parametrize("d", [64, 128])
+def test_f16_decode_mfma_groups(fa, n, num_splits, d):
+    """fp16 through the MFMA decode (8 heads per key/value head)."""
+    run(fa, 7995 + n + d, 2, 16, 2, n, d, dtype="f16", num_splits=num_splits)
+
+
+@pytest.mark.parametrize("group", [5, 8, 16, 32])
+@pytest.mark.parametrize("n", [1, 130, 5000])
+def test_mfma_decode_d64(fa, group, n):
+    """d = 64 through the MFMA decode: groups of 5 to 32 heads, ragged key
+    counts (a partial 32-key tile, a partial 128-key stage)."""
+    run(fa, 8400 + group * 8 + n % 7, 2, 2 * group, 2, n, 64)
 
 
 # ------------------------------------------------------------ per-sequence cache lengths
