@@ -1345,8 +1345,8 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   if constexpr (kDuo)
     fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
                                : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
-  else if (split)
-    fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, kCanSplit ? 2 : 1>;
+  else if constexpr (kCanSplit)
+    fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
   else
     fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1, kOS>;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
