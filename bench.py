@@ -14,6 +14,8 @@ copy (the byte-count calibration kernel) followed by --steps launches.
 --profile-decode: --steps split-K decode calls on B=8 H=32 N=32768 d=128.
 --profile-bwd: --steps backward calls on B=2 H=16 N=4096 d=128 causal (the
 forward-plus-backward workload), printed as one JSON line.
+--profile-decode-gqa: --steps decode calls on B8 H64 Hkv8 N32768 d128
+(8 query heads per key/value head, the MFMA decode kernel).
 --profile-fp8: --steps fa_fwd_fp8 calls on B8 H32 N8192 and B2 H16 N4096
 d=128 causal (e4m3 inputs).
 
@@ -637,6 +639,8 @@ def main():
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run --steps fa_decode calls on B=8 H=32 N=32768 d=128 (for rocprofv3)")
+    ap.add_argument("--profile-decode-gqa", action="store_true",
+                    help="run --steps fa_decode calls on B=8 H=64 Hkv=8 N=32768 d=128 (the MFMA decode)")
     ap.add_argument("--profile-fp8", action="store_true",
                     help="run the fp8 legs (B8 H32 N8192 and B2 H16 N4096 d=128 causal, for rocprofv3)")
     ap.add_argument("--profile-bwd", action="store_true",
@@ -665,6 +669,13 @@ def main():
         dq_, dk_, dv_ = decode_inputs(dw)
         r = time_decode(fa, dw, dq_, dk_, dv_, 0, args.steps, 2)
         print(json.dumps({"profile-decode": dw.name, **r}), flush=True)
+        return
+
+    if args.profile_decode_gqa:
+        dw = synthetic.DecodeWorkload(8, "decode bf16 B8 H64 Hkv8 N32768 d128", 8, 64, 8, 32768, 128)
+        dq_, dk_, dv_ = decode_inputs(dw)
+        r = time_decode(fa, dw, dq_, dk_, dv_, 0, args.steps, 2)
+        print(json.dumps({"profile-decode-gqa": dw.name, **r}), flush=True)
         return
 
     if args.profile_fp8:
