@@ -27,6 +27,7 @@ __all__ = [
     "bwd",
     "fa_bwd",
     "bwd_workspace_bytes",
+    "bwd_gqa_workspace_bytes",
     "bwd_tile_config",
     "decode",
     "fa_decode",
@@ -98,6 +99,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ctypes.c_float,
                                ci, vp]
     lib.fa_bwd_gqa.restype = ci
+    lib.fa_bwd_gqa_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+    lib.fa_bwd_gqa_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_tile.argtypes = [ci, ctypes.POINTER(ci), ctypes.POINTER(ci)]
@@ -264,6 +267,12 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, causa
     return out, lse
 
 
+def bwd_gqa_workspace_bytes(B, H, Hkv, N, d) -> int:
+    """Device workspace bytes with which fa_bwd_gqa may split each group's
+    heads over several dK/dV workgroups (0 for unsupported sizes)."""
+    return int(_LIB.fa_bwd_gqa_workspace_bytes(int(B), int(H), int(Hkv), int(N), int(d)))
+
+
 def bwd_workspace_bytes(B, H, N, d) -> int:
     """Device workspace bytes fa_bwd needs (0 for unsupported sizes)."""
     return int(_LIB.fa_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
@@ -303,7 +312,8 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
     o and lse are the outputs of fwd() for the same q, k, v, causal and
     scale; do is the upstream gradient of o.  dq / dk / dv / workspace may
     be passed to reuse buffers (workspace: a uint8 device tensor of at least
-    bwd_workspace_bytes(B, H, N, d) bytes).  Runs on `stream` (default:
+    bwd_workspace_bytes(B, H, N, d) bytes; bwd_gqa_workspace_bytes(B, H,
+    Hkv, N, d) bytes let grouped heads use the head-split dK/dV pass).  Runs on `stream` (default:
     torch's current stream).
     """
     import torch
@@ -333,8 +343,9 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
     for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
         if t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous tensor of q's dtype and shape {tuple(like.shape)}")
-    need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
+        # the grouped-head size enables the head-split dK/dV pass where it applies
+        need = bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)

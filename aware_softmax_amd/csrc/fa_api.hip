@@ -258,8 +258,14 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
         (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
     return FA_ERR_ALIGN;
-  const size_t need = fa::bwd_workspace_bytes((int)bh, N, d);
-  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t stats = fa::bwd_workspace_bytes((int)bh, N, d);
+  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < stats) return FA_ERR_WORKSPACE;
+  // a workspace of fa_bwd_gqa_workspace_bytes also holds the partials of
+  // the head-split dK/dV pass
+  const int hsplit = fa::bwd_head_split(B, H, Hkv, N);
+  const size_t big = hsplit > 1 ? fa::bwd_gqa_workspace_bytes(B, H, Hkv, N, d) : stats;
+  const bool split = hsplit > 1 && workspace_bytes >= big;
+  const size_t need = split ? big : stats;
   const size_t tb = (size_t)elems * 2;
   const size_t kvb = (size_t)B * Hkv * N * d * 2;
   const size_t lb = (size_t)bh * N * sizeof(float);
@@ -291,8 +297,18 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   p.causal = causal ? 1 : 0;
   p.scale = scale;
   p.group = H / Hkv;
+  if (split) {
+    p.hsplit = hsplit;
+    p.part = (float*)((char*)workspace + fa::bwd_part_offset(stats));
+  }
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_bwd_bf16(p, stream) : fa::launch_bwd_f16(p, stream);
   return hip_status(e);
+}
+
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || N <= 0 || H % Hkv != 0 || !bwd_headdim(d)) return 0;
+  if ((int64_t)B * H > INT_MAX || (int64_t)B * H * N * d > ((int64_t)1 << 40)) return 0;
+  return fa::bwd_gqa_workspace_bytes(B, H, Hkv, N, d);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

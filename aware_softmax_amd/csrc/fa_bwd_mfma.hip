@@ -84,6 +84,7 @@ constexpr int kBQ = 64;       // bwd_dkdv: queries per streamed tile
 constexpr int kBQdq = 128;    // bwd_dq: queries per workgroup (32 per wave)
 constexpr int kBKdq = 32;     // bwd_dq: keys per streamed tile
 constexpr int kRing = 3;      // LDS buffers per streamed tensor
+constexpr int64_t kHeadSplitMaxWgs = 256;  // dK/dV grids up to one round on 256 CUs split the group's heads
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Variable-length layout (cu set): B sequences packed into `total` rows per
@@ -281,7 +282,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgp
 void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                      const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
                      T* __restrict__ dKg, T* __restrict__ dVg, int BHkv, int N, int Npad, int nkb, float c,
-                     float scale, int group, VarLen vl) {
+                     float scale, int group, VarLen vl, int hsplit, float* __restrict__ part) {
   using Ly = DkdvLayout<D>;
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
@@ -302,8 +303,16 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // One workgroup per (key/value head, key block); it sums dK and dV over
   // the `group` query heads that share the key/value head (consecutive
   // query heads bhk * group .. bhk * group + group - 1).
-  int bhk, jb;
-  map_block(blockIdx.x, BHkv * nkb, nkb, CAUSAL ? Order::HeavyFirst : Order::Plain, &bhk, &jb);
+  // With hsplit > 1 (fixed length only) the group's query heads are split
+  // into hsplit subsets of hc heads, one workgroup per (key/value head,
+  // subset, key block), and each writes its partial dK, dV in fp32 to
+  // `part` ([hsplit][BHkv][N][D] each) for bwd_reduce_kernel to sum.
+  int vbh, jb;
+  map_block(blockIdx.x, BHkv * hsplit * nkb, nkb, CAUSAL ? Order::HeavyFirst : Order::Plain, &vbh, &jb);
+  const int bhk = vbh / hsplit;
+  const int sub = vbh - bhk * hsplit;
+  const int hc = group / hsplit;  // query heads of this workgroup: hs .. hs + hc - 1 of the group
+  const int hs = sub * hc;
   const int kb0 = jb * kBKV;
   // Rows of this key/value head (and sequence): `head` is the element
   // offset of its K/V row 0; query head r of the group has Q/dO row 0 at
@@ -351,13 +360,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   const int nqt = Npad / kBQ;
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
   const int span = nqt - it0;
-  const int total = group * span;
+  const int total = hc * span;
   auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % kRing); };
   constexpr int kDmaPerWave = 1 + 2 * (Ly::QTILE / 1024 / kWaves);  // statistics, Q, dO
   auto dma_tile = [&](int v) {
     const int b = ring(v);
-    const int r = __builtin_amdgcn_readfirstlane(v / span);
-    const int it = it0 + v - r * span;
+    const int rr = __builtin_amdgcn_readfirstlane(v / span);
+    const int r = hs + rr;
+    const int it = it0 + v - rr * span;
     const size_t qhead = q_off(r);
     // the tile's 64 statistics: -L/scale by waves 0 and 2, -D by waves 1
     // and 3 (the duplicate copy writes the same bytes; it keeps the number
@@ -534,8 +544,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   } else {
     dma_barrier<0>();
   }
-  for (int r = 0; r < group; ++r) {
-    int v = r * span;
+  for (int rr = 0; rr < hc; ++rr) {
+    int v = rr * span;
     int it = it0;
     for (; it < it_s; ++it, ++v) iteration(v, it, std::true_type{});
     for (; it < it_e; ++it, ++v) iteration(v, it, std::false_type{});
@@ -543,7 +553,24 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   }
 
   // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
-  if (key < N) {
+  if (part && key < N) {  // fp32 partials of this head subset
+    const size_t plane = (size_t)hsplit * BHkv * N * D;
+    float* pk = part + (((size_t)sub * BHkv + bhk) * N + key) * D + 4 * half;
+    float* pv = pk + plane;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 ok, ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ok[e] = dkT[b][4 * g + e] * scale;
+          ov[e] = dvT[b][4 * g + e];
+        }
+        *(f32x4*)(pk + 32 * b + 8 * g) = ok;
+        *(f32x4*)(pv + 32 * b + 8 * g) = ov;
+      }
+  } else if (key < N) {
     T* dkrow = dKg + head + (size_t)key * D + 4 * half;
     T* dvrow = dVg + head + (size_t)key * D + 4 * half;
 #pragma unroll
@@ -559,6 +586,34 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         *(vec4<T>*)(dkrow + 32 * b + 8 * g) = ok;
         *(vec4<T>*)(dvrow + 32 * b + 8 * g) = ov;
       }
+  }
+}
+
+// dK, dV = the sums of the hsplit fp32 partials, rounded once to T
+// (`part` as written by bwd_dkdv_kernel with hsplit > 1).  Eight
+// consecutive elements per thread; the subsets are added in order, so the
+// result is deterministic.
+template <class T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, T* __restrict__ dK,
+                                                         T* __restrict__ dV, size_t elems, int hsplit) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= elems) return;
+  const size_t plane = (size_t)hsplit * elems;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* src = part + t * plane + i;
+    f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+    for (int s = 1; s < hsplit; ++s) {
+      a += *(const f32x4*)(src + s * elems);
+      b += *(const f32x4*)(src + s * elems + 4);
+    }
+    vec8<T> out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = (T)a[e];
+      out[4 + e] = (T)b[e];
+    }
+    *(vec8<T>*)((t ? dV : dK) + i) = out;
   }
 }
 
@@ -838,15 +893,24 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   {
     const int nkb = (p.N + kBKV - 1) / kBKV;
     const int bhkv = p.BH / p.group;
-    const dim3 grid((unsigned)(bhkv * nkb)), block(kThreads);
+    const int hsplit = p.part ? p.hsplit : 1;
+    const dim3 grid((unsigned)(bhkv * hsplit * nkb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
-                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl);
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl, hsplit, p.part);
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
-                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl);
-    const hipError_t e = hipGetLastError();
+                         (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl, hsplit, p.part);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (hsplit > 1) {
+      const size_t elems = (size_t)bhkv * p.N * D;
+      const unsigned blocks = (unsigned)((elems / 8 + 255) / 256);
+      hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(blocks), dim3(256), 0, stream, (const float*)p.part, (T*)p.dk,
+                         (T*)p.dv, elems, hsplit);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   {
     const int nqb = (p.N + kBQdq - 1) / kBQdq;
@@ -867,6 +931,27 @@ size_t bwd_workspace_bytes(int BH, int N, int d) {
   (void)d;
   const size_t npad = ((size_t)N + kBQ - 1) / kBQ * kBQ;
   return (size_t)BH * npad * 2 * sizeof(float);
+}
+
+// Head split of the grouped-head dK/dV pass: with few (key/value head,
+// key block) workgroups the heaviest causal blocks -- which stream every
+// query tile of every head of the group -- set the run time, so the group's
+// heads are divided over hsplit workgroups that write fp32 partials.
+int bwd_head_split(int B, int H, int Hkv, int N) {
+  if (Hkv <= 0 || H % Hkv != 0) return 1;
+  const int group = H / Hkv;
+  const int64_t wgs = (int64_t)B * Hkv * (((int64_t)N + kBKV - 1) / kBKV);
+  if (group % 2 != 0 || wgs > kHeadSplitMaxWgs) return 1;
+  return (group % 4 == 0 && wgs * 4 <= 2 * kHeadSplitMaxWgs) ? 4 : 2;
+}
+
+size_t bwd_part_offset(size_t stats_bytes) { return (stats_bytes + 255) & ~(size_t)255; }
+
+size_t bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  const size_t stats = bwd_workspace_bytes(B * H, N, d);
+  const int hs = bwd_head_split(B, H, Hkv, N);
+  if (hs == 1) return stats;
+  return bwd_part_offset(stats) + 2 * (size_t)hs * B * Hkv * N * d * sizeof(float);
 }
 
 size_t bwd_varlen_workspace_bytes(int H, int total, int d) {

@@ -67,6 +67,11 @@ struct BwdParams {
   const int* cu_seqlens = nullptr;
   int H = 0;
   int total = 0;
+  // Grouped heads, fixed length: with part set, the dK/dV pass splits each
+  // group's query heads over hsplit workgroups that write fp32 partials to
+  // part ([2][hsplit][B * Hkv][N][d]), summed by a reduction kernel.
+  int hsplit = 1;
+  float* part = nullptr;
 };
 
 // Everything a split-K decode launch needs: q, o [B][H][d]; k, v
@@ -120,6 +125,12 @@ hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream);
 size_t bwd_workspace_bytes(int BH, int N, int d);
 size_t bwd_varlen_workspace_bytes(int H, int total, int d);  // -L/scale and -D, fp32 [H][ld] each
 int bwd_block_k();  // keys per workgroup of the dK/dV pass
+// Head split of the grouped-head dK/dV pass (1: none) and the workspace it
+// needs: the statistics, then (256-byte aligned, at bwd_part_offset) the
+// fp32 partials.
+int bwd_head_split(int B, int H, int Hkv, int N);
+size_t bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
+size_t bwd_part_offset(size_t stats_bytes);
 int bwd_block_q();  // queries per streamed tile of the dK/dV pass
 
 // Matrix-core-only ceiling kernel (4 MFMA 32x32x16 bf16 per iteration per

@@ -176,6 +176,22 @@ fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
+ * fa_bwd_gqa_workspace_bytes -- the workspace with which fa_bwd_gqa (and
+ * fa_bwd) may split the query heads of each key/value-head group over
+ * several workgroups of the dK/dV pass ("FA2 change #2" parallelises that
+ * pass over key blocks; with grouped heads a key block also sums over the
+ * group's heads, and on small grids the heaviest causal blocks would
+ * otherwise set the run time).  It is fa_bwd_workspace_bytes(B, H, N, d)
+ * rounded up to 256 bytes plus fp32 partial dK and dV for each head
+ * subset, or exactly fa_bwd_workspace_bytes when these sizes do not split
+ * (a group of odd size, or more than 256 dK/dV workgroups).  Passing at
+ * least this many bytes enables the split; passing fa_bwd_workspace_bytes
+ * keeps the one-workgroup-per-key-block pass.  Either way the result is
+ * deterministic.  Host-only; 0 for invalid sizes or head dimension.
+ */
+size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
+
+/*
  * fa_bwd -- attention backward for all B*H heads: given the upstream
  * gradient dO of O, writes dQ, dK and dV.
  *

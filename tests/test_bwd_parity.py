@@ -321,3 +321,35 @@ def test_varlen_backward_matches_fixed_length(fa):
     torch.cuda.synchronize()
     for a, b in zip(g, g2):
         assert torch.equal(pack(a).view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 700, 128), (1, 6, 1, 300, 64)])
+def test_gqa_backward_head_split_matches_unsplit(fa, shape):
+    """The head-split dK/dV pass (workspace of fa_bwd_gqa_workspace_bytes)
+    and the one-workgroup-per-key-block pass (fa_bwd_workspace_bytes)
+    agree with the oracle and, up to fp32 summation order, with each other;
+    each is deterministic."""
+    import torch
+
+    B, H, Hkv, N, d = shape
+    assert fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, d) > fa.bwd_workspace_bytes(B, H, N, d)
+    st = {"q": synthetic.full_storage(6995, "q", B, H, N, d, "bf16"),
+          "do": synthetic.full_storage(6995, "do", B, H, N, d, "bf16"),
+          "k": synthetic.full_storage(6995, "k", B, Hkv, N, d, "bf16"),
+          "v": synthetic.full_storage(6995, "v", B, Hkv, N, d, "bf16")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    small = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    big = torch.empty(fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    g_small = fa.bwd(q, k, v, o, lse, do, causal=True, workspace=small)
+    g_big = fa.bwd(q, k, v, o, lse, do, causal=True, workspace=big)
+    g_big2 = fa.bwd(q, k, v, o, lse, do, causal=True, workspace=big)
+    torch.cuda.synchronize()
+    vals64 = [synthetic.bf16_bits_to_f32(st[t][0]) for t in ("q", "k", "v", "do")]
+    ref = oracle.attention_bwd_gqa(*vals64, True, 1.0 / math.sqrt(d))
+    for grads in (g_small, g_big):
+        for name, got, r in zip(("dq", "dk", "dv"), grads, ref):
+            for h in range(r.shape[0]):
+                assert_grad_close(f"{name}[{h}]", got[0, h].float().cpu().numpy().astype(np.float64), r[h])
+    for x, y in zip(g_big, g_big2):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
