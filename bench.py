@@ -222,7 +222,7 @@ def time_gqa(fa, steps=10, warmup=2):
         out[f"{label} fwd"] = {"ms": round(ms, 4), "TFLOP/s": round(f / (ms * 1e-3) / 1e12, 2)}
         if with_bwd:
             dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(k)
-            ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+            ws = torch.empty(fa.bwd_gqa_workspace_bytes(B, H, Hkv, N, d), dtype=torch.uint8, device=dev)
             ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale, dq=dq, dk=dk, dv=dv,
                                       workspace=ws))
             out[f"{label} bwd"] = {"ms": round(ms, 4), "TFLOP/s": round(2.5 * f / (ms * 1e-3) / 1e12, 2)}
