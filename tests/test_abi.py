@@ -424,3 +424,18 @@ def test_fp8_validation_rejects_before_launch(fa):
                        (dict(vd=float("inf")), 6), (dict(scale=float("nan")), 6), (dict(o=A + 0x3000008), 5),
                        (dict(o=A + 0x1000), 8), (dict(lse=A + 0x3000100), 8)):
         assert call(**over) == code, over
+
+
+def test_bwd_gqa_workspace_bytes(fa):
+    stats = fa.bwd_workspace_bytes(2, 16, 4096, 128)
+    # group 4, 2*4*32 = 256 dK/dV workgroups: two head subsets, fp32 dK and dV partials each
+    assert fa.bwd_gqa_workspace_bytes(2, 16, 4, 4096, 128) == stats + 2 * 2 * 2 * 4 * 4096 * 128 * 4
+    # group 4 on at most 128 workgroups: four subsets
+    st1 = fa.bwd_workspace_bytes(1, 8, 2048, 64)
+    assert fa.bwd_gqa_workspace_bytes(1, 8, 2, 2048, 64) == (st1 + 255) // 256 * 256 + 2 * 4 * 1 * 2 * 2048 * 64 * 4
+    # no split: one head per group, an odd group, or a large grid
+    assert fa.bwd_gqa_workspace_bytes(2, 16, 16, 4096, 128) == stats
+    assert fa.bwd_gqa_workspace_bytes(1, 12, 4, 1000, 64) == fa.bwd_workspace_bytes(1, 12, 1000, 64)
+    assert fa.bwd_gqa_workspace_bytes(8, 32, 8, 8192, 128) == fa.bwd_workspace_bytes(8, 32, 8192, 128)
+    for bad in ((0, 8, 2, 64, 64), (1, 8, 3, 64, 64), (1, 8, 2, 64, 256), (1, 8, 2, 0, 64)):
+        assert fa.bwd_gqa_workspace_bytes(*bad) == 0
