@@ -97,12 +97,19 @@ static_assert(kRowsPerWave == 32, "one 32-wide MFMA block of queries per wave");
 // One LDS stage holds G consecutive key tiles, one per wave group: with
 // G = 2 the workgroup's two groups of 4 waves take alternate tiles of the
 // same query rows and merge their (m, l, O) once at the end.
+// V tile row stride in elements.  A transposing 8-byte read is served 32
+// lanes at a time over the LDS's 64 banks, and those lanes read 64 bytes
+// from each of 4 consecutive rows; they are conflict-free when the row
+// stride is 64 or 192 bytes modulo 256, so rows of 32 or 96 elements are
+// left as they are and the others get 32 elements of pad.
+constexpr int v_row_elems(int d) { return (d % 128 == 32 || d % 128 == 96) ? d : d + 32; }
+
 template <int D, int G, int OS = 1>
 struct Layout {
   static constexpr int THREADS = kThreads * G * OS;
   static constexpr int KEYS = kBK * G;  // keys per stage
   static constexpr int KS = D + 8;      // K tile row stride in elements (+16 B)
-  static constexpr int VS = D + 16;     // V tile row stride in elements (+32 B)
+  static constexpr int VS = v_row_elems(D);  // V tile row stride in elements
   static constexpr int K_ELEMS = KEYS * KS;
   static constexpr int V_ELEMS = KEYS * VS;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
@@ -494,7 +501,7 @@ struct LayoutF8 {
   static constexpr int THREADS = kThreads * G;
   static constexpr int KEYS = kBK * G;           // keys per stage
   static constexpr int KSB = D + 16;             // K tile row stride in bytes (fp8)
-  static constexpr int VS = D + 16;              // V tile row stride in bf16 elements
+  static constexpr int VS = v_row_elems(D);      // V tile row stride in bf16 elements
   static constexpr int K_BYTES = KEYS * KSB;
   static constexpr int STAGE_BYTES = K_BYTES + KEYS * VS * 2;
   static constexpr int CHUNKS_PER_ROW = D / 16;  // 16-byte chunks of fp8
@@ -893,9 +900,11 @@ constexpr int kRingV = 4;  // V ring: as K (equal rings make the buffers of an i
 // each row:
 //   K: chunk c of row r is stored at c ^ (r mod CPR) -- the 16 lanes reading
 //      one logical chunk of 16 consecutive rows hit 16 distinct chunks;
-//   V: chunk c of row r is stored at c ^ 2(r mod 4) -- a 16-lane group of a
-//      transposing read touches 4 consecutive rows x 2 chunks, which land
-//      on 8 distinct chunks.
+//   V: chunk c of row r is stored at c ^ 4(r mod 4) -- the LDS serves a
+//      transposing 8-byte read 32 lanes (256 bytes over its 64 banks) at a
+//      time, and those lanes touch 4 consecutive rows x 4 chunks, which land
+//      on 16 distinct chunks (a factor of 2 instead of 4 spreads them over
+//      only half the banks: a two-way conflict on every V read).
 template <int D>
 struct Layout {
   static constexpr int CPR = D / 8;
@@ -996,7 +1005,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * Ly::ROWS_PER_INSTR + dma_row;
     dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (row % CPR)) * 16));
-    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (2 * (row & 3))) * 16));
+    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (4 * (row & 3))) * 16));
   }
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
@@ -1008,7 +1017,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       off = decltype(is_v)::value ? dv_lane[i] : dk_lane[i];
     } else {
       const int row = r0 + dma_row;
-      const int chunk = decltype(is_v)::value ? (dma_chunk ^ (2 * (row & 3))) : (dma_chunk ^ (row % CPR));
+      const int chunk = decltype(is_v)::value ? (dma_chunk ^ (4 * (row & 3))) : (dma_chunk ^ (row % CPR));
       off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
     }
     __builtin_amdgcn_global_load_lds((const void*)(src + off),
@@ -1040,7 +1049,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   unsigned v_off[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
-    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (2 * tr_e)) * 8) +
+    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (4 * tr_e)) * 8) +
                           (tr_t & 1) * 4) * 2u;
   const unsigned smem_base = lds_addr(smem);
   // Absolute LDS addresses of buffer 0 of each ring; the buffer, the
