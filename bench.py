@@ -655,7 +655,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the attention forward is sharded over heads with no "
-              f"communication, and this build runs on a single MI355X; --gpus {args.gpus} is not "
+              f"communication, and the benchmark runs on a single MI355X; --gpus {args.gpus} is not "
               f"supported.", file=sys.stderr)
         sys.exit(2)
 
