@@ -155,6 +155,41 @@ def _check(code: int) -> None:
         raise FaError(code, message)
 
 
+def _check_out(name, t, shape, dtype, device) -> None:
+    """A caller-supplied output must be a contiguous tensor of the given
+    shape and dtype on the inputs' device: the C ABI sees only its address,
+    so a wrong size would be written past its end and a host tensor would
+    be dereferenced by the kernel."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(t, device) -> int:
+    """A workspace is a contiguous uint8 device tensor on the inputs'
+    device; returns its size in bytes (the library checks the size)."""
+    import torch
+
+    if t.dtype != torch.uint8 or t.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"workspace must be a device tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return t.numel()
+
+
+def _check_inputs(device, **tensors) -> None:
+    for name, t in tensors.items():
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a device tensor on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def tile_config(d: int, dtype: int) -> tuple:
     """(block_q, block_k, waves) that fa_fwd uses for head dim d and dtype."""
     bq, bk, w = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
@@ -197,21 +232,15 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     for name, t in (("k", k), ("v", v)):
         if t.dtype != q.dtype or t.shape != (B, Hkv, N, d):
             raise ValueError(f"{name} must be [B, Hkv, N, d] with the dtype, B, N and d of q")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _check_inputs(q.device, q=q, k=k, v=v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_out("out", out, q.shape, q.dtype, q.device)
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -245,8 +274,7 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, causa
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype not in allowed:
             raise TypeError(f"{name} must be torch.float8_e4m3fn or uint8 e4m3 bytes, not {t.dtype}")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    _check_inputs(q.device, q=q, k=k, v=v)
     for name, t in (("k", k), ("v", v)):
         if t.shape != (B, Hkv, N, d):
             raise ValueError(f"{name} must be [B, Hkv, N, d] with the B, N and d of q")
@@ -256,10 +284,8 @@ def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, causa
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != (B, H, N, d) or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 [B, H, N, d] tensor")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_out("out", out, (B, H, N, d), torch.bfloat16, q.device)
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
@@ -329,29 +355,26 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, dq
         want = (B, Hkv, N, d) if name in ("k", "v") else q.shape
         if t.dtype != q.dtype or t.shape != want:
             raise ValueError(f"{name} must be a {q.dtype} tensor of shape {tuple(want)}")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _check_inputs(q.device, q=q, k=k, v=v, o=o, do=do)
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
-    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, k)):
-        if t.shape != like.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor of q's dtype and shape {tuple(like.shape)}")
+    _check_out("dq", dq, q.shape, q.dtype, q.device)
+    _check_out("dk", dk, k.shape, q.dtype, q.device)
+    _check_out("dv", dv, k.shape, q.dtype, q.device)
     if workspace is None:
         # the grouped-head size enables the head-split dK/dV pass where it applies
         need = bwd_gqa_workspace_bytes(B, H, Hkv, N, d)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, causal, scale,
+                      ws_bytes, B, H, Hkv, N, d, causal, scale,
                       dtypes[q.dtype], stream.cuda_stream))
     return dq, dk, dv
 
@@ -416,10 +439,7 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t.dtype != q.dtype:
             raise ValueError(f"{name} must have the dtype of q")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _check_inputs(q.device, q=q, k=k, v=v)
     if v.shape != k.shape:
         raise ValueError("v must match k in shape")
     B, H, d = q.shape
@@ -433,23 +453,19 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    _check_out("out", out, q.shape, q.dtype, q.device)
+    _check_out("lse", lse, (B, H), torch.float32, q.device)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
     seq_ptr = None
     if cache_seqlens is not None:
-        if (cache_seqlens.dtype != torch.int32 or cache_seqlens.shape != (B,) or not cache_seqlens.is_cuda
-                or not cache_seqlens.is_contiguous()):
-            raise ValueError("cache_seqlens must be a contiguous int32 device tensor of shape [B]")
+        _check_out("cache_seqlens", cache_seqlens, (B,), torch.int32, q.device)
         seq_ptr = cache_seqlens.data_ptr()
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_ptr, out.data_ptr(), lse.data_ptr(),
-                     workspace.data_ptr(),
-                     workspace.numel() * workspace.element_size(), B, H, Hkv, N, d, scale, num_splits,
+                     workspace.data_ptr(), ws_bytes, B, H, Hkv, N, d, scale, num_splits,
                      dtypes[q.dtype], stream.cuda_stream))
     return out, lse
 
@@ -485,11 +501,7 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale:
             raise ValueError(f"{name} must be [Hkv, total, d] with the dtype, total and d of q")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of B + 1 offsets")
-    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    _check_inputs(q.device, q=q, k=k, v=v, cu_seqlens=cu_seqlens)
     B = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -497,10 +509,8 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (H, total) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [H, total] tensor")
+    _check_out("out", out, q.shape, q.dtype, q.device)
+    _check_out("lse", lse, (H, total), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -539,26 +549,27 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = 
     for name, t in (("k", k), ("v", v)):
         if t.dtype != q.dtype or t.shape != (Hkv, total, d):
             raise ValueError(f"{name} must be [Hkv, total, d] with the dtype, total and d of q")
-    if lse.shape != (H, total) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a float32 [H, total] tensor")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be a 1-D int32 tensor")
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("lse", lse), ("cu_seqlens", cu_seqlens)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    _check_inputs(q.device, q=q, k=k, v=v, o=o, do=do, cu_seqlens=cu_seqlens)
+    _check_out("lse", lse, (H, total), torch.float32, q.device)
     B = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(k) if dv is None else dv
+    _check_out("dq", dq, q.shape, q.dtype, q.device)
+    _check_out("dk", dk, k.shape, q.dtype, q.device)
+    _check_out("dv", dv, k.shape, q.dtype, q.device)
     need = bwd_varlen_workspace_bytes(H, total, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     _check(fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                          cu_seqlens.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(), B, H, Hkv, total, max_seqlen, d, causal,
+                         ws_bytes, B, H, Hkv, total, max_seqlen, d, causal,
                          scale, dtypes[q.dtype], stream.cuda_stream))
     return dq, dk, dv

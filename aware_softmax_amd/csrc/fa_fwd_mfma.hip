@@ -1405,8 +1405,12 @@ hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Waves per workgroup as launched on large grids (d <= 96 runs 8 waves, in
+// two key groups, only on grids of at most kSplitMaxBlocks workgroups).
 TileConfig mfma_tile(int d) {
-  return d == 128 ? TileConfig{duo::kBQ, kBK, duo::kWaves} : TileConfig{kBQ, kBK, kWaves};
+  if (d == 128) return TileConfig{duo::kBQ, kBK, duo::kWaves};
+  if (d == 256) return TileConfig{kBQ, kBK, 2 * kWaves};  // two waves per 32 query rows
+  return TileConfig{kBQ, kBK, kWaves};
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) { return launch_t<__bf16>(p, stream); }

@@ -161,7 +161,9 @@ const char* fa_status_string(fa_status_t status);
 /*
  * fa_fwd_tile -- the tile configuration fa_fwd uses for (d, dtype):
  * query rows per workgroup, keys per streamed tile and wavefronts per
- * workgroup.  Host-only; makes no HIP call.  Returns FA_OK or
+ * workgroup (as launched on large grids: at d <= 96 a grid of at most 1024
+ * workgroups runs twice as many waves, two groups splitting the keys).
+ * Host-only; makes no HIP call.  Returns FA_OK or
  * FA_ERR_NULL / FA_ERR_DTYPE / FA_ERR_UNSUPPORTED_HEADDIM.
  */
 fa_status_t fa_fwd_tile(int d, fa_dtype_t dtype, int* block_q, int* block_k, int* waves);
@@ -237,7 +239,12 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
  * through the shared K and V); they are summed on chip by the workgroup
  * that owns the key block, so the result stays free of atomics and
  * deterministic.  Every other argument as for fa_bwd; H must be a
- * multiple of Hkv (else FA_ERR_SHAPE).
+ * multiple of Hkv (else FA_ERR_SHAPE).  With a workspace of at least
+ * fa_bwd_gqa_workspace_bytes(B, H, Hkv, N, d) bytes on a small grid the
+ * heads of a group may be split over several dK/dV workgroups that write
+ * fp32 partial sums to the workspace; a fourth kernel then adds the
+ * partials in a fixed order and rounds once (four kernels are enqueued
+ * instead of three).
  */
 fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
                        const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,

@@ -4,7 +4,6 @@ Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``; the product path never touches it.
 """
 from .attention import (  # noqa: F401
-    attention_batched,
     attention_bwd,
     attention_bwd_gqa,
     attention_bwd_varlen,

@@ -58,7 +58,6 @@ __all__ = [
     "attention_bwd",
     "split_kv_partials",
     "combine_partials",
-    "attention_batched",
     "attention_gqa",
     "attention_bwd_gqa",
     "attention_varlen",
@@ -258,24 +257,6 @@ def combine_partials(m, l, o):
     l_tot = np.sum(w * l, axis=0)
     o_tot = np.sum(w[:, :, None] * o, axis=0)
     return o_tot / l_tot[:, None], big_m + np.log(l_tot)
-
-
-def attention_batched(q, k, v, causal, scale, heads=None, rows=None):
-    """naive_attention over [B][H][N][d] arrays for selected heads and rows.
-
-    heads: iterable of (b, h); default every head.  rows: 1-D query indices
-    shared by all heads; default all rows.  Returns dicts keyed by (b, h)
-    of O and L (fp64).
-    """
-    bsz, nh = q.shape[0], q.shape[1]
-    if heads is None:
-        heads = [(b, h) for b in range(bsz) for h in range(nh)]
-    o_out, l_out = {}, {}
-    for b, h in heads:
-        o, lse = naive_attention(q[b, h], k[b, h], v[b, h], causal, scale, rows=rows)
-        o_out[(b, h)] = o
-        l_out[(b, h)] = lse
-    return o_out, l_out
 
 
 def attention_gqa(q, k, v, causal, scale):

@@ -186,13 +186,21 @@ def workload_storage(w: Workload, tensors=("q", "k", "v"), threads: int = 8) -> 
     return {t: full_storage(w.config_id, t, w.B, w.H, w.N, w.d, w.dtype, threads) for t in tensors}
 
 
-def sample_rows(config_id: int, n: int, count: int, salt: int = 0, edge_block: int = 128) -> np.ndarray:
-    """Sorted query-row sample: `count` seeded rows plus the edge rows
-    {0, 1, edge_block - 1, edge_block, n - 1} (those inside 0..n-1)."""
+def sample_rows(config_id: int, n: int, count: int, salt: int = 0) -> np.ndarray:
+    """Sorted query-row sample: `count` seeded rows plus the edge rows of
+    every query block size in use (64, 128 and 256 rows: the last row of the
+    first and second blocks and the first of the next ones), the first two
+    rows, and the rows around the start of the last 128- and 256-row blocks
+    and at the end (those inside 0..n-1)."""
     rng = np.random.Generator(np.random.PCG64([0xFA, config_id, 99, salt]))
     count = min(count, n)
     picked = rng.choice(n, size=count, replace=False)
-    edges = [r for r in (0, 1, edge_block - 1, edge_block, n - 1) if 0 <= r < n]
+    edges = [0, 1, n - 2, n - 1]
+    for b in (64, 128, 256):
+        edges += [b - 1, b, 2 * b - 1, 2 * b]
+        last = (n - 1) // b * b  # first row of the last b-row block
+        edges += [last - 1, last]
+    edges = [r for r in edges if 0 <= r < n]
     return np.unique(np.concatenate([picked, np.array(edges, dtype=np.int64)]))
 
 

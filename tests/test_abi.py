@@ -69,6 +69,10 @@ def test_tile_config(fa):
     assert fa.tile_config(64, fa.DTYPE_F32)[0] > 0
     for d in (32, 96, 256):
         assert fa.tile_config(d, fa.DTYPE_BF16)[0] > 0
+    # d = 256 launches two waves per 32 query rows
+    bq, bk, w = fa.tile_config(256, fa.DTYPE_BF16)
+    assert w == 8 and bq == 128 and bk == 64
+    assert fa.tile_config(64, fa.DTYPE_BF16)[2] == 4
     with pytest.raises(fa.FaError) as e:
         fa.tile_config(80, fa.DTYPE_BF16)
     assert e.value.code == 4
@@ -439,3 +443,66 @@ def test_bwd_gqa_workspace_bytes(fa):
     assert fa.bwd_gqa_workspace_bytes(8, 32, 8, 8192, 128) == fa.bwd_workspace_bytes(8, 32, 8192, 128)
     for bad in ((0, 8, 2, 64, 64), (1, 8, 3, 64, 64), (1, 8, 2, 64, 256), (1, 8, 2, 0, 64)):
         assert fa.bwd_gqa_workspace_bytes(*bad) == 0
+
+
+def test_library_imports_no_allocator(fa):
+    """Memory O(N), owned by the caller ("PidokuInfra 10 -- FlashAttention",
+    section 10, the hands-on exercise on memory): libfa.so never allocates,
+    frees or clears device or host memory through the HIP runtime -- it does
+    not even import those routines.  The imported HIP symbols are limited to
+    kernel registration and launch, error reporting and the address lookup
+    of a static device array."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    hip = sorted({line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()})
+    assert hip, "expected the HIP launch symbols in the dynamic symbol table"
+    for name in hip:
+        low = name.lower()
+        for bad in ("malloc", "free", "memset", "memcpy", "alloc", "register"):
+            if bad == "register" and name in ("__hipRegisterFatBinary", "__hipRegisterFunction",
+                                              "__hipUnregisterFatBinary", "__hipRegisterVar"):
+                continue
+            assert bad not in low, f"libfa.so imports {name}"
+    allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+               "__hipRegisterFunction", "__hipUnregisterFatBinary", "__hipRegisterVar", "hipGetErrorString",
+               "hipGetLastError", "hipLaunchKernel", "hipGetSymbolAddress", "hipGetDevice"}
+    assert set(hip) <= allowed, f"unexpected HIP imports: {sorted(set(hip) - allowed)}"
+
+
+def test_binding_output_checks(fa):
+    """The binding's checks of caller-supplied outputs and workspaces
+    (run before any launch; the C ABI sees only addresses): wrong shape,
+    wrong dtype, a host tensor or a tensor on another device, and a
+    non-contiguous view are each rejected."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    host = torch.zeros(2, 3, dtype=torch.float32)
+    with pytest.raises(ValueError, match="device"):
+        fa._check_out("dq", host, (2, 3), torch.float32, dev)
+    with pytest.raises(ValueError, match="shape"):
+        fa._check_out("dq", host, (2, 4), torch.float32, dev)
+    with pytest.raises(ValueError, match="shape"):
+        fa._check_out("dq", host, (2, 3), torch.bfloat16, dev)
+    with pytest.raises(ValueError, match="device"):
+        fa._check_workspace(torch.zeros(16, dtype=torch.uint8), dev)
+    with pytest.raises(ValueError, match="uint8"):
+        fa._check_workspace(torch.zeros(16, dtype=torch.float32), dev)
+    with pytest.raises(ValueError, match="device"):
+        fa._check_inputs(dev, q=host)
+    # contiguity (checked last, so the target device here is the host's)
+    with pytest.raises(ValueError):
+        fa._check_out("o", host.t(), (3, 2), torch.float32, torch.device("cpu"))
+
+
+def test_bwd_varlen_binding_rejects_host_outputs(fa):
+    """bwd_varlen checks dq / dk / dv / workspace like bwd (host inputs are
+    rejected first; the outputs' own checks are exercised through the
+    helpers above and on the GPU)."""
+    import torch
+
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(2, 8)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa.bwd_varlen(q, q, q, q, lse, q, cu, 8, dq=torch.zeros(1, 8, 64, dtype=torch.bfloat16))

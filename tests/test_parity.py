@@ -93,13 +93,70 @@ def test_workload2_bf16_causal_d64(fa):
     assert_close(run_case(fa, 2, w.B, w.H, w.N, w.d, w.dtype, w.causal), w.dtype)
 
 
-def test_workload3_sampled(fa):
+def test_raw_fa_fwd_symbol_workload2(fa):
+    """The C entry point fa_fwd itself (not the grouped-head entry the
+    Python wrapper uses), called with device addresses on B=1, H=16,
+    N=2048, d=64 causal bf16; every row against the oracle."""
+    import torch
+
+    w = synthetic.WORKLOADS[2]
+    tensors = synthetic.workload_storage(w)
+    q, k, v = (to_device(tensors[t], w.dtype) for t in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device="cuda")
+    status = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d,
+                       w.causal, w.scale, fa.DTYPE_BF16, torch.cuda.current_stream().cuda_stream)
+    assert status == 0, fa.status_string(status)
+    torch.cuda.synchronize()
+    err_o = err_l = 0.0
+    for h in range(w.H):
+        ref_o, ref_l = oracle.naive_attention(*(values(tensors[t][0, h], w.dtype) for t in ("q", "k", "v")),
+                                              w.causal, w.scale)
+        err_o = max(err_o, float(np.max(np.abs(o[0, h].float().cpu().numpy() - ref_o))))
+        err_l = max(err_l, float(np.max(np.abs(lse[0, h].cpu().numpy() - ref_l))))
+    assert_close((err_o, err_l), w.dtype)
+
+
+@pytest.fixture(scope="module")
+def workload3_tensors():
+    return synthetic.workload_storage(synthetic.WORKLOADS[3])
+
+
+def test_workload3_sampled(fa, workload3_tensors):
     """B=8, H=32, N=8192, d=128 causal: 4 seeded heads x 512 seeded rows
     (plus edge rows), in the launch configuration the bench times."""
     w = synthetic.WORKLOADS[3]
     heads = synthetic.sample_heads(3, w.B, w.H, 4)
     rows = synthetic.sample_rows(3, w.N, 512)
-    assert_close(run_case(fa, 3, w.B, w.H, w.N, w.d, w.dtype, w.causal, heads=heads, rows=rows), w.dtype)
+    assert_close(run_case(fa, 3, w.B, w.H, w.N, w.d, w.dtype, w.causal, heads=heads, rows=rows,
+                          tensors=workload3_tensors), w.dtype)
+
+
+def test_workload3_every_head(fa, workload3_tensors):
+    """B=8, H=32, N=8192, d=128 causal: every one of the 256 heads of the
+    full launch (the bench's grid and schedule) at 8 seeded rows per head,
+    plus rows in the first and the last query block of every head."""
+    import torch
+
+    w = synthetic.WORKLOADS[3]
+    tensors = workload3_tensors
+    q, k, v = (to_device(tensors[t], w.dtype) for t in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    err_o = err_l = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            rng = np.random.Generator(np.random.PCG64([0xFA, 3, 97, b, h]))
+            rows = np.unique(np.concatenate([rng.choice(w.N, 8, replace=False),
+                                             [0, 255, 256, w.N - 256, w.N - 1]]))
+            ref_o, ref_l = oracle.naive_attention(values(tensors["q"][b, h], w.dtype),
+                                                  values(tensors["k"][b, h], w.dtype),
+                                                  values(tensors["v"][b, h], w.dtype), w.causal, w.scale, rows=rows)
+            err_o = max(err_o, float(np.max(np.abs(o[b, h][rows] - ref_o))))
+            err_l = max(err_l, float(np.max(np.abs(lse[b, h][rows] - ref_l))))
+    assert_close((err_o, err_l), w.dtype)
 
 
 def test_workload4_long_context_sampled(fa):

@@ -35,7 +35,8 @@ def test_normal_moments():
 def test_row_and_head_samples():
     r = synthetic.sample_rows(3, 8192, 512)
     assert len(r) >= 512 and r.min() == 0 and r.max() == 8191 and np.all(np.diff(r) > 0)
-    assert {1, 127, 128}.issubset(set(r.tolist()))
+    # edges of the 64-, 128- and 256-row query blocks, first and last blocks
+    assert {1, 63, 64, 127, 128, 255, 256, 511, 512, 7935, 7936, 8063, 8064, 8190}.issubset(set(r.tolist()))
     assert np.array_equal(r, synthetic.sample_rows(3, 8192, 512))
     heads = synthetic.sample_heads(3, 8, 32, 4)
     assert len(set(heads)) == 4 and all(0 <= b < 8 and 0 <= h < 32 for b, h in heads)
