@@ -189,8 +189,11 @@ __device__ inline HeadRows head_rows(int bh, int BH, int group, int N, int D, co
 // partial row sum.  Writes P = 2^(s*c - m') as bf16 MFMA B-operand
 // fragments and returns alpha = 2^(m - m') for rescaling O.
 //   MASK: the tile crosses the causal diagonal or the end of the sequence;
-//   scores with key offset > lim_causal (causal) or >= lim_n are excluded.
-//   Unmasked tiles run no per-score compare or select at all.
+//   scores with key offset > lim_causal (causal) or >= lim_n are replaced
+//   by -inf before any arithmetic.  Unmasked tiles run no per-score compare
+//   or select at all.  c must be > 0 (a zero scale is raised to 1e-30 by
+//   the caller: every P of a row is then exactly 1 in fp32, as for scale 0,
+//   while -inf * c stays -inf for hidden keys).
 template <bool MASK, bool CAUSAL, class T>
 __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, int lim_n, float& m_run,
                                      float& l_part, vec8<T> (&pfrag)[4]) {
@@ -228,12 +231,10 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const float x0 = sv[u * 8 + e], x1 = sv[u * 8 + e + 1];
-      float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c, -m_use));
-      float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c, -m_use));
-      if (MASK) {  // keeps masked P exactly 0 also when scale = 0 (-inf * 0)
-        p0 = (x0 == -INFINITY) ? 0.f : p0;
-        p1 = (x1 == -INFINITY) ? 0.f : p1;
-      }
+      // c > 0 (the kernels raise a zero scale to 1e-30), so a hidden
+      // score gives 2^(-inf) = 0 with no select
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c, -m_use));
       const vec2<T> pr = cvt2<T>(p0, p1);
       // Row sum of exactly the bf16 probabilities the P.V product uses.
       lsum = dot2(pr, one, lsum);
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(kThreads * G * OS, (D >= 256 || G == 2 || OS == 2) 
   const int dh = OS == 1 ? 0 : tid >> 8;       // d range of O held by the wave
   const int col = lane & 31;   // query column of the transposed tiles
   const int half = lane >> 5;  // which 4-key group of each 8 (MFMA layout)
+  c = fmaxf(c, 1e-30f);        // tile_softmax needs c > 0 (scale 0: every P is 1)
 
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
@@ -534,6 +536,7 @@ __global__ __launch_bounds__(kThreads * G, G == 2 ? 1 : 2) void fwd_fp8_kernel(
   const int grp = G == 1 ? 0 : tid >> 8;       // key tiles of the wave
   const int col = lane & 31;
   const int half = lane >> 5;
+  c = fmaxf(c, 1e-30f);  // tile_softmax needs c > 0 (scale 0: every P is 1)
 
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);

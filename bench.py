@@ -429,6 +429,45 @@ def time_decode(fa, w, q, k, v, num_splits, steps, warmup):
             "kernels": "decode_split + decode_combine"}
 
 
+def time_default_legs(fa):
+    """The other measured workloads, in every default run (after the headline
+    leg, outside its timed region): causal bf16 forward on B1 H16 N2048 d64,
+    B1 H16 N32768 d128 (batch-1 long context) and B2 H16 N4096 d128, the
+    backward of the last, and split-K decode on B8 H32 N32768 d128.  Inputs
+    are the seeded workloads of the parity tests; each leg frees its tensors."""
+    import torch
+
+    import synthetic
+
+    legs = {}
+    for cid in (2, 4, 5):
+        ww = synthetic.WORKLOADS[cid]
+        qq, kk, vv = make_inputs(ww)
+        oo = torch.empty_like(qq)
+        ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
+        steps = 50 if cid == 2 else 20
+        _, msk, mn, mx, _ = time_launches(fa, qq, kk, vv, oo, ll, True, ww.scale, steps, 3)
+        f = attention_flops(ww.B, ww.H, ww.N, ww.d, True)
+        tf = f / (msk * 1e-3) / 1e12
+        legs[f"causal bf16 fwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"] = {
+            "ms": round(msk, 4), "min_ms": round(mn, 4), "max_ms": round(mx, 4), "TFLOP/s": round(tf, 2),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_call": f}
+        if cid == 5:
+            r = time_backward(fa, ww, qq, kk, vv, oo, ll, 20, 3)
+            r["frac_of_peak"] = round(r["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
+            legs[f"causal bf16 bwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"] = r
+        del qq, kk, vv, oo, ll
+        torch.cuda.empty_cache()
+    dw = synthetic.DECODE_WORKLOADS[6]
+    dq_, dk_, dv_ = decode_inputs(dw)
+    # 200 untimed calls: the first ~100 calls after the inputs are copied in
+    # run up to 10 % slower
+    legs[f"{dw.name} split-K"] = time_decode(fa, dw, dq_, dk_, dv_, 0, 50, 200)
+    del dq_, dk_, dv_
+    torch.cuda.empty_cache()
+    return legs
+
+
 def device_sysfs(torch):
     """sysfs directory of the GPU torch calls cuda:0 (from its PCI address),
     or None where it is not readable."""
@@ -763,10 +802,11 @@ def main():
             "power_cap_w": round(power_cap / 1e6, 1) if power_cap else None,
         },
     }
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    result["workloads"] = time_default_legs(fa)
     if args.extra:
         extra = {}
-        del q, k, v, o, lse
-        torch.cuda.empty_cache()
         for cid in (2, 4, 5):
             ww = synthetic.WORKLOADS[cid]
             qq, kk, vv = make_inputs(ww)

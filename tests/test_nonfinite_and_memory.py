@@ -2,19 +2,24 @@
 library allocates no device memory.
 
 Non-finite inputs.  The 16-bit forward kernels are built without NaN
-semantics (fmaxf may drop a NaN operand; the steady-tile overflow test
-"partial row sum > 2^16" is false for NaN), so a NaN score is neither
-caught nor hidden: 2^NaN = NaN enters P, the row sum and the P.V product.
-Hidden scores are replaced by -inf with an integer bit select before any
-arithmetic, so a NaN behind the causal mask never reaches a row that does
-not see it.  Consequences, checked below on the bf16 forward for the d = 128
-kernel and the generic d = 64 kernel:
+semantics: the row max (v_max_f32) drops a NaN operand, and the d = 128
+kernel's steady-tile overflow test "partial row sum > 2^16" is false for
+NaN.  A NaN score is therefore neither caught nor hidden: 2^NaN = NaN
+enters P, the row sum and the P.V product.  Hidden scores (behind the
+causal mask or past the end) are replaced by -inf with a select before any
+arithmetic, and 2^(-inf * c) = 0 for the kernels' c > 0, so a NaN score
+never reaches a row that does not see its key.  A NaN value row is
+different: P.V multiplies every key of a tile, and 0 * NaN = NaN, so it
+reaches every row whose wave multiplies the tile holding it, including
+rows that do not see it.  Checked below on the bf16 forward for the d = 128
+kernel and the generic d = 64 kernel (two wave groups on this grid):
   * NaN anywhere in query row i: O_i and L_i are NaN, every other row is
     bitwise what it is without the NaN;
   * NaN in key row j: every row that sees key j (causal: i >= j; otherwise
     all) has O and L NaN, the other rows are bitwise unchanged;
   * NaN in value row j: O of every row that sees key j is NaN; L of every
-    row, and O of the rows that do not see key j, are bitwise unchanged.
+    row is bitwise unchanged, and so is O of every row before the 64-key
+    tile holding row j (causal; such rows never multiply that tile).
 Other heads are never affected.
 
 Memory.  "PidokuInfra 10 -- FlashAttention", section 10 (hands-on
@@ -83,11 +88,13 @@ def test_nan_reaches_exactly_the_rows_that_see_it(fa, d, causal, where):
     assert np.isnan(o1[0, 0][hit]).all()
     if where == "v":
         assert same_bits(l1[0, 0], l0[0, 0])
+        # O rows that never multiply the value tile holding the NaN row
+        clean = rows < (row // 64) * 64 if causal else np.zeros(N, dtype=bool)
+        assert same_bits(o1[0, 0][clean], o0[0, 0][clean])
     else:
         assert np.isnan(l1[0, 0][hit]).all()
         assert same_bits(l1[0, 0][~hit], l0[0, 0][~hit])
-    # rows that do not see it
-    assert same_bits(o1[0, 0][~hit], o0[0, 0][~hit])
+        assert same_bits(o1[0, 0][~hit], o0[0, 0][~hit])
 
 
 def test_free_device_memory_unchanged_by_calls(fa):

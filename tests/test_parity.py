@@ -227,14 +227,15 @@ def test_other_scales(fa, dtype, scale):
                  scale_factor=max(1.0, abs(scale) * math.sqrt(d)))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("bf16", 64), ("bf16", 256), ("f16", 64),
+                                     ("f16", 128), ("f32", 64)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scale_zero_gives_prefix_means(fa, dtype, causal):
+def test_scale_zero_gives_prefix_means(fa, dtype, d, causal):
     """Closed form, no oracle: scale 0 makes O the mean of the visible V
     rows and L = log(#visible)."""
     import torch
 
-    n, d = 257, 128
+    n = 257
     st = {t: synthetic.full_storage(5000, t, 1, 2, n, d, dtype) for t in ("q", "k", "v")}
     q, k, v = (to_device(st[t], dtype) for t in ("q", "k", "v"))
     o, lse = fa.fwd(q, k, v, causal=causal, scale=0.0)
@@ -243,7 +244,7 @@ def test_scale_zero_gives_prefix_means(fa, dtype, causal):
     cnt = np.arange(1, n + 1) if causal else np.full(n, n)
     ref = np.cumsum(vv, axis=2) / cnt[None, None, :, None] if causal else np.repeat(
         vv.mean(axis=2, keepdims=True), n, axis=2)
-    tol_o = 2e-2 if dtype == "bf16" else 1e-5
+    tol_o = TOL[dtype][0]
     assert np.max(np.abs(o.float().cpu().numpy() - ref)) <= tol_o
     assert np.max(np.abs(lse.cpu().numpy() - np.log(cnt)[None, None, :])) <= 1e-5
 
