@@ -31,6 +31,9 @@ __all__ = [
     "bwd_tile_config",
     "decode",
     "fa_decode",
+    "fa_decode_static",
+    "decode_static",
+    "DECODE_STATIC_SCRATCH_BYTES",
     "decode_plan",
     "decode_workspace_bytes",
     "tile_config",
@@ -107,6 +110,8 @@ def _load() -> ctypes.CDLL:
     lib.fa_bwd_tile.restype = ci
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
     lib.fa_decode.restype = ci
+    lib.fa_decode_static.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci, vp]
+    lib.fa_decode_static.restype = ci
     lib.fa_decode_plan.argtypes = [ci, ci, ci, ci, ci, ci, ctypes.POINTER(ci), ctypes.POINTER(ci),
                                    ctypes.POINTER(sz)]
     lib.fa_decode_plan.restype = ci
@@ -467,6 +472,55 @@ def decode(q, k, v, scale: float | None = None, num_splits: int = 0, out=None, l
     _check(fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_ptr, out.data_ptr(), lse.data_ptr(),
                      workspace.data_ptr(), ws_bytes, B, H, Hkv, N, d, scale, num_splits,
                      dtypes[q.dtype], stream.cuda_stream))
+    return out, lse
+
+
+# FA_DECODE_STATIC_SCRATCH_BYTES of include/fa.h
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def fa_decode_static(q_ptr, k_ptr, v_ptr, seqlens_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, scale, num_splits, dtype,
+                     stream) -> int:
+    """Raw call of the C entry point with integer device addresses; returns
+    the fa_status_t code."""
+    return _LIB.fa_decode_static(q_ptr, k_ptr, v_ptr, seqlens_ptr, o_ptr, lse_ptr, int(B), int(H), int(Hkv), int(N),
+                                 int(d), float(scale), int(num_splits), int(dtype), stream)
+
+
+def decode_static(q, k, v, out, lse, scale: float | None = None, num_splits: int = 0, stream=None,
+                  cache_seqlens=None):
+    """decode() without a workspace: the library's static device scratch
+    holds the split partials, so the call allocates nothing (out and lse
+    are the caller's).  Calls that overlap in time on one device race on
+    that scratch.  Raises FaError (FA_ERR_SCRATCH) when the split partials
+    would exceed DECODE_STATIC_SCRATCH_BYTES."""
+    import torch
+
+    dtypes = {torch.bfloat16: DTYPE_BF16, torch.float16: DTYPE_F16}
+    if q.dtype not in dtypes:
+        raise TypeError(f"unsupported dtype {q.dtype} for decode; use torch.bfloat16 or torch.float16")
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [B, H, d] and k, v [B, Hkv, N, d]")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have the dtype of q")
+    _check_inputs(q.device, q=q, k=k, v=v)
+    B, H, d = q.shape
+    Bk, Hkv, N, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError("k, v must be [B, Hkv, N, d] with the B and d of q")
+    _check_out("out", out, q.shape, q.dtype, q.device)
+    _check_out("lse", lse, (B, H), torch.float32, q.device)
+    seq_ptr = None
+    if cache_seqlens is not None:
+        _check_out("cache_seqlens", cache_seqlens, (B,), torch.int32, q.device)
+        seq_ptr = cache_seqlens.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    _check(fa_decode_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), seq_ptr, out.data_ptr(), lse.data_ptr(), B, H,
+                            Hkv, N, d, scale, num_splits, dtypes[q.dtype], stream.cuda_stream))
     return out, lse
 
 

@@ -56,6 +56,7 @@ const char* fa_status_string(fa_status_t status) {
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP kernel launch failed";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or another output";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned or smaller than the size the call needs";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the problem needs more scratch than the static array of fa_decode_static holds (FA_DECODE_STATIC_SCRATCH_BYTES)";
   }
   return "unknown fa_status_t";
 }
@@ -403,9 +404,16 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
   return fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &ws) == FA_OK ? ws : 0;
 }
 
-fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o, float* lse,
-                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
-                      int num_splits, fa_dtype_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_decode and fa_decode_static: validation (no HIP call), then the launch
+// with the caller's workspace or, when static_scratch is set, the library's
+// static scratch array of the current device.
+fa_status_t decode_impl(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o,
+                        float* lse, void* workspace, size_t workspace_bytes, bool static_scratch, int B, int H,
+                        int Hkv, int N, int d, float scale, int num_splits, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   size_t need = 0;
   const fa_status_t st = fa_decode_plan(B, H, Hkv, N, d, num_splits, nullptr, nullptr, &need);
@@ -415,19 +423,27 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0 ||
       (((uintptr_t)lse | (uintptr_t)cache_seqlens) & 3u) != 0)
     return FA_ERR_ALIGN;
-  if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (static_scratch) {
+    if (need > FA_DECODE_STATIC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  } else if (!workspace || ((uintptr_t)workspace & 255u) != 0 || workspace_bytes < need) {
+    return FA_ERR_WORKSPACE;
+  }
   const size_t qb = (size_t)B * H * d * 2;
   const size_t kb = (size_t)B * Hkv * N * d * 2;
   const size_t lb = (size_t)B * H * sizeof(float);
   const void* ins[4] = {q, k, v, cache_seqlens};
   const size_t in_bytes[4] = {qb, kb, kb, cache_seqlens ? (size_t)B * sizeof(int) : 0};
   void* outs[3] = {o, lse, workspace};
-  const size_t out_bytes[3] = {qb, lb, need};
+  const size_t out_bytes[3] = {qb, lb, static_scratch ? 0 : need};
   for (int a = 0; a < 3; ++a) {
     for (int b = 0; b < 4; ++b)
       if (ranges_overlap(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_ALIAS;
     for (int b = a + 1; b < 3; ++b)
       if (ranges_overlap(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_ALIAS;
+  }
+  if (static_scratch) {
+    const hipError_t e = fa::decode_static_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e);
   }
 
   fa::DecodeParams p;
@@ -447,6 +463,24 @@ fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* ca
   p.num_splits = num_splits;
   const hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_decode_bf16(p, stream) : fa::launch_decode_f16(p, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d, float scale,
+                      int num_splits, fa_dtype_t dtype, hipStream_t stream) {
+  return decode_impl(q, k, v, cache_seqlens, o, lse, workspace, workspace_bytes, false, B, H, Hkv, N, d, scale,
+                     num_splits, dtype, stream);
+}
+
+fa_status_t fa_decode_static(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o,
+                             float* lse, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
+                             fa_dtype_t dtype, hipStream_t stream) {
+  return decode_impl(q, k, v, cache_seqlens, o, lse, nullptr, 0, true, B, H, Hkv, N, d, scale, num_splits, dtype,
+                     stream);
 }
 
 fa_status_t fa_mfma_ceiling(float* sink, int iters, int blocks, int store, hipStream_t stream) {

@@ -31,9 +31,13 @@
 // cross-lane max at all; the states of a workgroup are merged once at the
 // end.  A group of G query heads that share a key/value head is served by
 // one workgroup, so K and V are read once for all G.
+#include <atomic>
+#include <mutex>
+
 #include <math.h>
 #include <stdint.h>
 
+#include "fa.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -734,6 +738,40 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     case 256: return launch_d<T, 256>(p, plan, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// Scratch of fa_decode_static: the split partials (o~, m, l) of
+// decode_plan's workspace layout, for callers that cannot allocate.  One
+// copy per device, held by the loaded code object until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// is only a stand-in for the device symbol): its device address is looked
+// up once per device with hipGetSymbolAddress and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) { return launch_decode_t<__bf16>(p, stream); }

@@ -118,6 +118,9 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_f16(const BwdParams& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+// Device address, on the current device, of fa_decode_static's scratch
+// array (FA_DECODE_STATIC_SCRATCH_BYTES bytes); looked up once per device.
+hipError_t decode_static_scratch(void** ptr);
 hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream);
 
 // Backward workspace: -L/scale and -D, fp32 [BH][Npad] each; Npad = N

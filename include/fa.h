@@ -58,8 +58,12 @@ typedef enum {
   FA_ERR_SCALE = 6,                /* scale is NaN or infinite */
   FA_ERR_HIP = 7,                  /* the HIP launch reported an error */
   FA_ERR_ALIAS = 8,                /* an output overlaps an input or another output */
-  FA_ERR_WORKSPACE = 9             /* workspace missing, misaligned or too small */
+  FA_ERR_WORKSPACE = 9,            /* workspace missing, misaligned or too small */
+  FA_ERR_SCRATCH = 10              /* the problem needs more than the library's static scratch */
 } fa_status_t;
+
+/* Size of the static device scratch array behind fa_decode_static. */
+#define FA_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /*
  * fa_fwd -- attention forward for all B*H heads.
@@ -342,6 +346,31 @@ size_t fa_decode_workspace_bytes(int B, int H, int Hkv, int N, int d, int num_sp
 fa_status_t fa_decode(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o,
                       float* lse, void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N, int d,
                       float scale, int num_splits, fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_decode_static -- fa_decode without a workspace argument and without
+ * any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The split partials go to a static device array of
+ * FA_DECODE_STATIC_SCRATCH_BYTES (16 MiB) that the library holds on every
+ * device it runs on until the process ends; its device address is looked
+ * up once per device (hipGetSymbolAddress) on the first call there.
+ *   Arguments, layouts, checks and results as for fa_decode (the same
+ *   kernels and split plan: outputs are bitwise those of fa_decode with
+ *   the same num_splits), minus workspace / workspace_bytes.
+ *   A problem whose fa_decode_workspace_bytes(B, H, Hkv, N, d, num_splits)
+ *   exceeds FA_DECODE_STATIC_SCRATCH_BYTES returns FA_ERR_SCRATCH before
+ *   any HIP call (e.g. B * H * splits * (d + 2) * 4 bytes > 16 MiB).
+ * Every call on one device shares that device's array and leaves its
+ * partials in it; nothing in it needs to start at zero (every partial the
+ * merge reads is written by the same call first).  Calls that overlap in
+ * time on one device -- on different streams, or from different threads
+ * without ordering -- race on the array and give undefined results; calls
+ * on one stream are ordered and safe.
+ */
+fa_status_t fa_decode_static(const void* q, const void* k, const void* v, const int* cache_seqlens, void* o,
+                             float* lse, int B, int H, int Hkv, int N, int d, float scale, int num_splits,
+                             fa_dtype_t dtype, hipStream_t stream);
 
 /*
  * fa_last_hip_error -- the hipError_t behind the last FA_ERR_HIP an entry

@@ -506,3 +506,35 @@ def test_bwd_varlen_binding_rejects_host_outputs(fa):
     cu = torch.tensor([0, 8], dtype=torch.int32)
     with pytest.raises(ValueError):
         fa.bwd_varlen(q, q, q, q, lse, q, cu, 8, dq=torch.zeros(1, 8, 64, dtype=torch.bfloat16))
+
+
+def scall(fa, **over):
+    a = dict(DGOOD)
+    a.update(over)
+    return fa.fa_decode_static(a["q"], a["k"], a["v"], a["sl"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                               a["d"], a["scale"], a["splits"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(B=0), 2), (dict(Hkv=3), 2), (dict(dtype=0), 3), (dict(d=80), 4),
+    (dict(k=A + 0x1000008), 5), (dict(scale=float("inf")), 6), (dict(o=A + 0x1000000), 8),
+    # split partials of B64 H64 N32768 d256 over 8 splits: 64*64*8*(256+2)*4 bytes > 16 MiB
+    (dict(B=64, H=64, Hkv=64, N=32768, d=256, splits=8), 10),
+])
+def test_decode_static_validation_rejects_before_launch(fa, over, code):
+    assert scall(fa, **over) == code
+
+
+def test_decode_static_scratch_limit(fa):
+    """The static scratch size in the header and in the binding agree, and
+    a problem whose split partials just fit is not rejected by the size
+    check (it fails later, at the fake addresses' alias check)."""
+    text = open(os.path.join(HEADER_DIR, "fa.h")).read()
+    assert "#define FA_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert fa.DECODE_STATIC_SCRATCH_BYTES == 16 << 20
+    big = dict(B=64, H=64, Hkv=64, N=32768, d=256, splits=8)
+    assert fa.decode_workspace_bytes(64, 64, 64, 32768, 256, 8) > fa.DECODE_STATIC_SCRATCH_BYTES
+    assert fa.decode_workspace_bytes(64, 64, 64, 32768, 256, 2) <= fa.DECODE_STATIC_SCRATCH_BYTES
+    assert scall(fa, **big) == 10
+    assert scall(fa, **dict(big, splits=2, o=A + 0x1000000)) == 8
+    assert "FA_ERR_SCRATCH" in fa.status_string(10)
