@@ -985,8 +985,12 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   int wave_nt = nkt;
   if (CAUSAL) wave_nt = min(nkt, (qw + 31) / kBK + 1);
   if (qw >= N) wave_nt = 0;
+  // Tiles every row of this wave sees in full (the wave's own count: under
+  // the causal mask a wave's rows meet the diagonal at tile qw / kBK, so
+  // the waves of a workgroup leave the steady schedule at different tiles).
   int nfull = N / kBK;
-  if (CAUSAL) nfull = min(nfull, q0 / kBK);
+  if (CAUSAL) nfull = min(nfull, qw / kBK);
+  if (wave_nt == 0) nfull = 0;
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -1097,10 +1101,12 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       constexpr int F = decltype(fc)::value;
       constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
       asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(fr[F % kLead]) : "i"(last - F));
+      __builtin_amdgcn_s_setprio(2);
       if constexpr (F < 2)
         dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], f32x16{});
       else
         dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], dst[F % 2]);
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
       if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_any(Vh, dma_b, dma_t, F / 8, std::true_type{});
@@ -1137,7 +1143,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo[F % kLead]), "+v"(hi[F % kLead]) : "i"(2 * (last - F)));
       const vec8<T> vf =
           __builtin_bit_cast(vec8<T>, __builtin_shufflevector(lo[F % kLead], hi[F % kLead], 0, 1, 2, 3, 4, 5, 6, 7));
+      __builtin_amdgcn_s_setprio(2);
       oacc[b] = mfma32(vf, pfrag[u], oacc[b]);
+      __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
       if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
       if constexpr (DMA && F % 8 == 3) dma_any(Kh, dma_b, dma_t, F / 8, std::false_type{});
@@ -1211,7 +1219,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     l_part = l_part * alpha + (ps[0] + ps[1]);
     rescale(alpha);
   };
-  // Steady interval: tile j unmasked for every row, 1 <= j, j + 1 < nkt.
+  // Steady interval: tile j unmasked for every row of the wave, 1 <= j,
+  // j + 1 < nkt.
   // Returns true when tile j's probabilities overflowed the budget (P_j
   // then needs fast_redo before the next interval's P.V).
   // R = j mod 4 fixes every ring slot of the interval, and the scores of
