@@ -38,7 +38,7 @@ fa_status_t check_dtype_headdim(int d, fa_dtype_t dtype) {
 }
 
 // Head dims of the backward kernels.
-bool bwd_headdim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+bool bwd_headdim(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
 
 }  // namespace
 
@@ -252,9 +252,10 @@ fa_status_t fa_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   if (bh > INT_MAX) return FA_ERR_SHAPE;
   const int64_t elems = bh * N * d;
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
-  // The largest grid: one 256-thread workgroup per (query head, 128-row block).
+  // The largest grid: one 256-thread workgroup per (query head, 128-row
+  // block), two at d = 256 (one per half of the dK, dV columns).
   const int64_t nkb = ((int64_t)N + fa::bwd_block_k() - 1) / fa::bwd_block_k();
-  if (bh * nkb * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (bh * nkb * (d == 256 ? 2 : 1) * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
         (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || ((uintptr_t)lse & 3u) != 0)
@@ -339,7 +340,7 @@ fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const voi
   const int64_t elems = (int64_t)H * total * d;
   if (elems > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
   const int64_t nkb = ((int64_t)max_seqlen + fa::bwd_block_k() - 1) / fa::bwd_block_k();
-  if (bh * nkb * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
+  if (bh * nkb * (d == 256 ? 2 : 1) * 256 > kMaxWorkItems) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
         (uintptr_t)dk | (uintptr_t)dv) & 15u) != 0 || (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3u) != 0)

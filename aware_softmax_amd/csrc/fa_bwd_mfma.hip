@@ -27,7 +27,9 @@
 //             initial values of the dP and S accumulators below;
 //   bwd_dkdv  one workgroup per (head, 128-key block), 4 wave64s with 32
 //             keys each; 64-query tiles of Q and dO (plus L, D) streamed
-//             through triple-buffered LDS; dK, dV in registers;
+//             through triple-buffered LDS; dK, dV in registers (at d = 256
+//             two workgroups per key block, one per half of the columns of
+//             dK and dV, and double-buffered LDS);
 //   bwd_dq    one workgroup per (head, 128-query block), 4 wave64s with 32
 //             queries each; 32-key tiles of K and V streamed through
 //             triple-buffered LDS (48 KB); dQ in registers.  At 242 VGPRs
@@ -83,7 +85,7 @@ constexpr int kBKV = 128;     // bwd_dkdv: keys per workgroup (32 per wave)
 constexpr int kBQ = 64;       // bwd_dkdv: queries per streamed tile
 constexpr int kBQdq = 128;    // bwd_dq: queries per workgroup (32 per wave)
 constexpr int kBKdq = 32;     // bwd_dq: keys per streamed tile
-constexpr int kRing = 3;      // LDS buffers per streamed tensor
+constexpr int kRing = 3;      // LDS buffers per streamed tensor (bwd_dq; bwd_dkdv up to d = 128)
 constexpr int64_t kHeadSplitMaxWgs = 256;  // dK/dV grids up to one round on 256 CUs split the group's heads
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -134,8 +136,10 @@ constexpr int lds_row_elems() {
 //   * 32 lanes reading 4 chunks of 4 consecutive rows (transposing reads).
 template <int ROWB>
 __device__ __forceinline__ int swz_mask(int r) {
-  static_assert(ROWB == 256 || ROWB == 128, "rows of 64 or 128 bf16");
-  if constexpr (ROWB == 256)
+  static_assert(ROWB == 512 || ROWB == 256 || ROWB == 128, "rows of 64, 128 or 256 bf16");
+  // 512-byte rows: the 16 bank groups repeat every 16 chunks, so the
+  // 256-byte mask (4 bits) serves them as well.
+  if constexpr (ROWB >= 256)
     return ((r & 3) << 2) | ((r >> 2) & 3);
   else
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -261,22 +265,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ Og, 
 template <int D>
 struct DkdvLayout {
   static constexpr int ROWB = 2 * lds_row_elems<D>();
+  // Buffers per streamed tensor: three (DMA two tiles ahead), two at
+  // d = 256, whose 32 KiB tiles leave room for no third.
+  static constexpr int RING = D > 128 ? 2 : kRing;
   static constexpr int QTILE = kBQ * ROWB;    // one Q or dO tile
   static constexpr int STTILE = 2 * kBQ * 4;  // -L/scale[64], -D[64]
   static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + kRing * QTILE;
-  static constexpr int OFF_ST = OFF_DO + kRing * QTILE;
-  static constexpr int TOTAL = OFF_ST + kRing * STTILE;
+  static constexpr int OFF_DO = OFF_Q + RING * QTILE;
+  static constexpr int OFF_ST = OFF_DO + RING * QTILE;
+  static constexpr int TOTAL = OFF_ST + RING * STTILE;
   static_assert(TOTAL <= 160 * 1024, "fits the 160 KiB LDS");
 };
+
+// bwd_dkdv column halves: at d = 256 the dK and dV accumulators of 32 keys
+// (256 registers per lane) do not fit beside the K and V fragments, so
+// each (key block) is processed by two workgroups that rebuild the same S
+// and dP over the full d and accumulate dK and dV for one half of the
+// columns each (phase A is done twice: 1.5x the matrix work of one pass).
+template <int D>
+constexpr int dkdv_halves() {
+  return D > 128 ? 2 : 1;
+}
 
 // Per 64-query tile and wave (32 keys):
 //   A  S = Q K^T - L/scale and dP = dO V^T - D  (4 DT MFMAs; row fragments
 //      of the Q and dO tiles, several in flight);
 //   V  P = 2^(c S), dS = P dP, both packed to bf16 (VALU only);
-//   B  dV^T += dO^T P and dK^T += Q^T dS        (8 DB MFMAs, transposing reads).
+//   B  dV^T += dO^T P and dK^T += Q^T dS        (8 DBO MFMAs, transposing reads;
+//      DBO = the 32-column blocks of the workgroup's columns of dK and dV).
 // Iteration t runs A(t + 1) with V(t) riding on its MFMAs, then B(t); the
-// DMA of tile t + 2 is in flight meanwhile; one barrier per iteration.
+// DMA of the tile RING - 1 ahead is in flight meanwhile; one barrier per
+// iteration.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
@@ -285,11 +304,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
                      float scale, int group, VarLen vl, int hsplit, float* __restrict__ part) {
   using Ly = DkdvLayout<D>;
   constexpr int DT = D / 16;
-  constexpr int DB = D / 32;
+  constexpr int NH = dkdv_halves<D>();
+  constexpr int DBO = D / 32 / NH;  // 32-column blocks of dK, dV per workgroup
   constexpr int ROWB = Ly::ROWB;
-  constexpr int NA = 4 * DT;  // phase A MFMAs
-  constexpr int LA = 4;       // phase A fragments in flight
-  constexpr int NB = 8 * DB;  // phase B MFMAs
+  constexpr int RING = Ly::RING;
+  constexpr int PF = RING - 1;  // tiles in flight ahead of the one being read
+  constexpr int NA = 4 * DT;   // phase A MFMAs
+  constexpr int LA = 4;        // phase A fragments in flight
+  constexpr int NB = 8 * DBO;  // phase B MFMAs
   constexpr int LB = 4;       // phase B fragments in flight
   static_assert(NA % 8 == 0, "eight VALU groups ride on the phase A MFMAs");
   __shared__ __attribute__((aligned(1024))) char smem[Ly::TOTAL];
@@ -307,8 +329,13 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // into hsplit subsets of hc heads, one workgroup per (key/value head,
   // subset, key block), and each writes its partial dK, dV in fp32 to
   // `part` ([hsplit][BHkv][N][D] each) for bwd_reduce_kernel to sum.
-  int vbh, jb;
-  map_block(blockIdx.x, BHkv * hsplit * nkb, nkb, CAUSAL ? Order::HeavyFirst : Order::Plain, &vbh, &jb);
+  // With NH = 2 (d = 256) the column half dh is the fastest index of the
+  // head dimension, so both halves of a key block are neighbours in the
+  // schedule and read the same Q, dO tiles close in time.
+  int vbh2, jb;
+  map_block(blockIdx.x, BHkv * hsplit * NH * nkb, nkb, CAUSAL ? Order::HeavyFirst : Order::Plain, &vbh2, &jb);
+  const int vbh = vbh2 / NH;
+  const int dcol = (vbh2 - vbh * NH) * (D / NH);  // first dK, dV column of this workgroup
   const int bhk = vbh / hsplit;
   const int sub = vbh - bhk * hsplit;
   const int hc = group / hsplit;  // query heads of this workgroup: hs .. hs + hc - 1 of the group
@@ -361,7 +388,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
   const int span = nqt - it0;
   const int total = hc * span;
-  auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % kRing); };
+  auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % RING); };
   constexpr int kDmaPerWave = 1 + 2 * (Ly::QTILE / 1024 / kWaves);  // statistics, Q, dO
   auto dma_tile = [&](int v) {
     const int b = ring(v);
@@ -390,23 +417,23 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // Transposing reads: lane gets column 32b + col of rows 16u + 4 half +
   // {0..3} (lo) and 16u + 8 + 4 half + {0..3} (hi); the swizzle does not
   // depend on u, which enters as an immediate offset.
-  unsigned trq[DB][2];
+  unsigned trq[DBO][2];
   {
     const int tr_e = (lane & 15) >> 2, tr_t = lane & 3, tr_cg = (lane >> 4) & 1;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DBO; ++b)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi) {
         const int r = 4 * half + tr_e + 8 * hi;
-        const int chunk = 4 * b + 2 * tr_cg + (tr_t >> 1);
+        const int chunk = dcol / 8 + 4 * b + 2 * tr_cg + (tr_t >> 1);
         trq[b][hi] = (unsigned)(r * ROWB + ((chunk ^ swz_mask<ROWB>(r)) << 4) + (tr_t & 1) * 8);
       }
   }
   const unsigned sbase = lds_addr(smem);
 
-  f32x16 dkT[DB], dvT[DB];
+  f32x16 dkT[DBO], dvT[DBO];
 #pragma unroll
-  for (int b = 0; b < DB; ++b) {
+  for (int b = 0; b < DBO; ++b) {
     dkT[b] = f32x16{};
     dvT[b] = f32x16{};
   }
@@ -444,7 +471,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // riding on the MFMAs of step u (groups 0 and 1 run before step 0).
   auto iteration = [&](int v, int it, auto mask_c) {
     const int b = ring(v);
-    if (v + 2 < total) dma_tile(v + 2);
+    if (v + PF < total) dma_tile(v + PF);
     const unsigned aq = sbase + Ly::OFF_Q + b * Ly::QTILE;
     const unsigned ado = sbase + Ly::OFF_DO + b * Ly::QTILE;
     {
@@ -495,14 +522,14 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
     {
       s16x4 lo_[LB], hi_[LB];
       auto issue = [&](auto fc) {
-        constexpr int F = decltype(fc)::value, u = F / (2 * DB), bb = (F / 2) % DB, X = F % 2;
+        constexpr int F = decltype(fc)::value, u = F / (2 * DBO), bb = (F / 2) % DBO, X = F % 2;
         const unsigned a = X ? aq : ado;
         ds_tr64<u * 16 * ROWB>(lo_[F % LB], a + trq[bb][0]);
         ds_tr64<u * 16 * ROWB>(hi_[F % LB], a + trq[bb][1]);
       };
       static_for<LB>(issue);
       static_for<NB>([&](auto fc) {
-        constexpr int F = decltype(fc)::value, u = F / (2 * DB), bb = (F / 2) % DB, X = F % 2;
+        constexpr int F = decltype(fc)::value, u = F / (2 * DBO), bb = (F / 2) % DBO, X = F % 2;
         constexpr int last = (F + LB - 1 < NB - 1) ? F + LB - 1 : NB - 1;
         constexpr int qb = u / 2, h2 = u % 2;
         asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo_[F % LB]), "+v"(hi_[F % LB]) : "i"(2 * (last - F)));
@@ -518,14 +545,15 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         if constexpr (F + LB < NB) issue(ic<F + LB>{});
         // groups 2 (u + 1) and 2 (u + 1) + 1 after the first and second half
         // of step u's MFMAs
-        constexpr int per = 2 * DB, f = F % per;
+        constexpr int per = 2 * DBO, f = F % per;
         if constexpr (u < 3 && (f == per / 2 - 1 || f == per - 1))
           vgroup(ic<2 * (u + 1) + (f == per - 1 ? 1 : 0)>{}, mask_c, it);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    // tile v + 1 must be complete; the copies of tile v + 2 stay in flight
-    if (v + 2 < total)
+    // tile v + 1 must be complete; with three buffers the copies of tile
+    // v + 2 stay in flight
+    if (PF == 2 && v + 2 < total)
       dma_barrier<kDmaPerWave>();
     else
       dma_barrier<0>();
@@ -538,7 +566,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   it_e = max(it_e, it_s);
 
   dma_tile(0);
-  if (1 < total) {
+  if (PF == 2 && 1 < total) {
     dma_tile(1);
     dma_barrier<kDmaPerWave>();
   } else {
@@ -555,10 +583,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
   if (part && key < N) {  // fp32 partials of this head subset
     const size_t plane = (size_t)hsplit * BHkv * N * D;
-    float* pk = part + (((size_t)sub * BHkv + bhk) * N + key) * D + 4 * half;
+    float* pk = part + (((size_t)sub * BHkv + bhk) * N + key) * D + dcol + 4 * half;
     float* pv = pk + plane;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DBO; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x4 ok, ov;
@@ -571,10 +599,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         *(f32x4*)(pv + 32 * b + 8 * g) = ov;
       }
   } else if (key < N) {
-    T* dkrow = dKg + head + (size_t)key * D + 4 * half;
-    T* dvrow = dVg + head + (size_t)key * D + 4 * half;
+    T* dkrow = dKg + head + (size_t)key * D + dcol + 4 * half;
+    T* dvrow = dVg + head + (size_t)key * D + dcol + 4 * half;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+    for (int b = 0; b < DBO; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         vec4<T> ok, ov;
@@ -638,10 +666,15 @@ struct DqLayout {
 //   C  dQ^T += K^T dS^T                               (2 KB DB MFMAs, transposing reads).
 // Iteration j runs A(j + 1) with V(j) riding on its MFMAs, then C(j).
 // Three waves per SIMD at d = 32 (+8 % on B2 H16 N4096 d32 causal); at
-// d = 64 the same bound costs spills and 5 %.
+// d = 64 the same bound costs spills and 5 %.  One at d = 256, where the
+// Q and dO fragments and dQ take 256 registers per lane.
+template <int D>
+constexpr int dq_waves() {
+  return D <= 32 ? 3 : D <= 128 ? 2 : 1;
+}
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(D <= 32 ? 3 : 2, D <= 32 ? 3 : 2)))
+                          amdgpu_waves_per_eu(dq_waves<D>(), dq_waves<D>())))
 void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                    const T* __restrict__ dOg, const float* __restrict__ Lsg, const float* __restrict__ Dng,
                    T* __restrict__ dQg, int BH, int N, int Npad, int nqb, float c, float scale, int group,
@@ -894,7 +927,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     const int nkb = (p.N + kBKV - 1) / kBKV;
     const int bhkv = p.BH / p.group;
     const int hsplit = p.part ? p.hsplit : 1;
-    const dim3 grid((unsigned)(bhkv * hsplit * nkb)), block(kThreads);
+    const dim3 grid((unsigned)(bhkv * hsplit * dkdv_halves<D>() * nkb)), block(kThreads);
     if (p.causal)
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true>), grid, block, 0, stream, q, k, v, dout, ls, dn, (T*)p.dk,
                          (T*)p.dv, bhkv, p.N, npad, nkb, c, p.scale, p.group, vl, hsplit, p.part);
@@ -969,6 +1002,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     case 64: return launch_bwd<T, 64>(p, stream);
     case 96: return launch_bwd<T, 96>(p, stream);
     case 128: return launch_bwd<T, 128>(p, stream);
+    case 256: return launch_bwd<T, 256>(p, stream);
   }
   return hipErrorInvalidValue;
 }

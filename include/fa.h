@@ -222,8 +222,12 @@ size_t fa_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
  *                     owned by the caller; overwritten, contents undefined
  *                     afterwards.  It needs no initialisation.
  *   B, H, N, causal, scale   as for fa_fwd.
- *   d         head dimension: 32, 64, 96 or 128 (else
- *             FA_ERR_UNSUPPORTED_HEADDIM).
+ *   d         head dimension: 32, 64, 96, 128 or 256 (else
+ *             FA_ERR_UNSUPPORTED_HEADDIM).  At 256 the dK/dV pass runs
+ *             two workgroups per key block, one per half of the columns,
+ *             each rebuilding S and dP over the full d ("PidokuInfra 10 --
+ *             FlashAttention", section 5: the on-chip budget of a d = 256
+ *             tile).
  *   dtype     FA_DTYPE_BF16 or FA_DTYPE_F16 (P and dS are rounded to it for
  *             the MFMAs); FA_DTYPE_F32 returns FA_ERR_DTYPE.
  *   stream    HIP stream; three kernels are enqueued in order on it.
@@ -268,7 +272,7 @@ size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d);
  * [Hkv][total][d]; lse [H][total]; every sequence's gradients depend only
  * on its own rows.  workspace: at least fa_bwd_varlen_workspace_bytes(H,
  * total, d) bytes, 256-byte aligned.  dtype FA_DTYPE_BF16 or FA_DTYPE_F16;
- * d 32, 64, 96 or 128; the other arguments and the checks as for fa_bwd_gqa and
+ * d 32, 64, 96, 128 or 256; the other arguments and the checks as for fa_bwd_gqa and
  * fa_fwd_varlen (cu_seqlens clamped to [0, total] on the device).
  */
 fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -195,7 +195,8 @@ def test_bwd_workspace_bytes(fa):
     assert fa.bwd_workspace_bytes(1, 2, 65, 64) == 2 * 128 * 2 * 4
     assert fa.bwd_workspace_bytes(1, 1, 1, 128) == 64 * 2 * 4
     assert fa.bwd_workspace_bytes(1, 1, 64, 96) == fa.bwd_workspace_bytes(1, 1, 64, 32) == 64 * 2 * 4
-    for bad in ((0, 1, 64, 64), (1, 1, 0, 64), (1, 1, 64, 80), (1, 1, 64, 256), (1, -1, 64, 128)):
+    assert fa.bwd_workspace_bytes(1, 1, 64, 256) == 64 * 2 * 4
+    for bad in ((0, 1, 64, 64), (1, 1, 0, 64), (1, 1, 64, 80), (1, 1, 64, 512), (1, -1, 64, 128)):
         assert fa.bwd_workspace_bytes(*bad) == 0
     bk, bq = fa.bwd_tile_config(128)
     assert bk > 0 and bq > 0 and bk % 32 == 0
@@ -207,7 +208,7 @@ def test_bwd_workspace_bytes(fa):
     (dict(q=0), 1), (dict(lse=0), 1), (dict(do=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dv=0), 1),
     (dict(B=0), 2), (dict(N=-3), 2), (dict(B=1 << 20, H=1 << 12, N=1 << 20), 2),
     (dict(dtype=0), 3), (dict(dtype=5), 3),
-    (dict(d=80), 4), (dict(d=256), 4), (dict(d=48), 4),
+    (dict(d=80), 4), (dict(d=512), 4), (dict(d=48), 4),
     (dict(do=A + 0x5000008), 5), (dict(dk=A + 0x7000002), 5), (dict(lse=A + 0x4000001), 5),
     (dict(scale=float("nan")), 6), (dict(scale=float("-inf")), 6),
     (dict(dq=A), 8), (dict(dv=A + 0x7000100), 8), (dict(ws=A + 0x6000000), 8), (dict(dk=W + 0x100), 8),
@@ -380,7 +381,8 @@ def test_bwd_varlen_workspace_and_validation(fa):
     # two fp32 [H][ld] vectors, ld = total rounded up to 64, plus 64
     assert fa.bwd_varlen_workspace_bytes(4, 500, 128) == 4 * (512 + 64) * 2 * 4
     assert fa.bwd_varlen_workspace_bytes(4, 500, 96) == 4 * (512 + 64) * 2 * 4
-    assert fa.bwd_varlen_workspace_bytes(4, 500, 256) == 0
+    assert fa.bwd_varlen_workspace_bytes(4, 500, 256) == 4 * (512 + 64) * 2 * 4
+    assert fa.bwd_varlen_workspace_bytes(4, 500, 512) == 0
     W2 = A + 0x9000000
     args = dict(q=A, k=A + 0x1000000, v=A + 0x2000000, o=A + 0x3000000, lse=A + 0x4000000, do=A + 0x5000000,
                 cu=A + 0x6000000, dq=A + 0x6100000, dk=A + 0x7000000, dv=A + 0x8000000, ws=W2, ws_bytes=1 << 20,
@@ -392,7 +394,7 @@ def test_bwd_varlen_workspace_and_validation(fa):
         return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["cu"], a["dq"], a["dk"],
                                 a["dv"], a["ws"], a["ws_bytes"], a["B"], a["H"], a["Hkv"], a["total"], a["mx"],
                                 a["d"], a["causal"], a["scale"], a["dtype"], None)
-    for over, code in ((dict(cu=0), 1), (dict(mx=501), 2), (dict(Hkv=3), 2), (dict(dtype=0), 3), (dict(d=256), 4),
+    for over, code in ((dict(cu=0), 1), (dict(mx=501), 2), (dict(Hkv=3), 2), (dict(dtype=0), 3), (dict(d=512), 4),
                        (dict(cu=A + 0x6000001), 5), (dict(ws_bytes=100), 9), (dict(dq=A + 0x6000000 - 16), 8),
                        (dict(ws=A), 8)):
         assert call(**over) == code, over
@@ -441,7 +443,7 @@ def test_bwd_gqa_workspace_bytes(fa):
     assert fa.bwd_gqa_workspace_bytes(2, 16, 16, 4096, 128) == stats
     assert fa.bwd_gqa_workspace_bytes(1, 12, 4, 1000, 64) == fa.bwd_workspace_bytes(1, 12, 1000, 64)
     assert fa.bwd_gqa_workspace_bytes(8, 32, 8, 8192, 128) == fa.bwd_workspace_bytes(8, 32, 8192, 128)
-    for bad in ((0, 8, 2, 64, 64), (1, 8, 3, 64, 64), (1, 8, 2, 64, 256), (1, 8, 2, 0, 64)):
+    for bad in ((0, 8, 2, 64, 64), (1, 8, 3, 64, 64), (1, 8, 2, 64, 512), (1, 8, 2, 0, 64)):
         assert fa.bwd_gqa_workspace_bytes(*bad) == 0
 
 

@@ -149,22 +149,29 @@ def test_ragged_bwd(fa, n, d, causal):
 
 
 @pytest.mark.parametrize("n", [1, 7, 63, 65, 129, 333, 513])
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 96, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_ragged_bwd_head_dims(fa, n, d, causal):
     """d = 32 and 96: LDS rows padded to 64 / 128 elements, the MFMA loops
-    over d only."""
-    run_bwd(fa, 9000 + n * 4 + (d == 96) * 2 + causal, 1, 2, n, d, causal)
+    over d only.  d = 256: two dK/dV workgroups per key block (one per half
+    of the columns) and double-buffered LDS."""
+    cid = (20000 if d == 256 else 9000) + n * 4 + (d == 96) * 2 + causal
+    run_bwd(fa, cid, 1, 2, n, d, causal)
 
 
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 96, 256])
 def test_bwd_head_dims_long(fa, d):
     """B2 H4 N2048 causal: many query and key tiles per workgroup; 3 seeded
     heads."""
     run_bwd(fa, 9100 + d, 2, 4, 2048, d, True, heads=synthetic.sample_heads(9100 + d, 2, 4, 3))
 
 
-@pytest.mark.parametrize("d", [32, 96])
+def test_bwd_d256_sampled_heads(fa):
+    """B2 H8 N4096 d256 causal: 2 seeded heads, every row of dQ, dK, dV."""
+    run_bwd(fa, 9400, 2, 8, 4096, 256, True, heads=synthetic.sample_heads(9400, 2, 8, 2))
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
 def test_f16_bwd_head_dims(fa, d):
     run_bwd(fa, 9200 + d, 1, 2, 333, d, True, dtype="f16")
 
@@ -240,7 +247,8 @@ def test_outputs_untouched_outside_bounds(fa):
 
 
 @pytest.mark.parametrize("shape", [(2, 8, 2, 333, 128), (1, 12, 4, 1000, 64), (1, 6, 1, 257, 128),
-                                   (1, 8, 2, 2048, 128), (1, 6, 2, 300, 96), (1, 4, 1, 200, 32)])
+                                   (1, 8, 2, 2048, 128), (1, 6, 2, 300, 96), (1, 4, 1, 200, 32),
+                                   (1, 4, 2, 300, 256)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa_backward(fa, shape, causal):
     """fa_bwd_gqa: dK, dV of a key/value head sum over the query heads of
@@ -248,7 +256,7 @@ def test_gqa_backward(fa, shape, causal):
     import torch
 
     B, H, Hkv, N, d = shape
-    cid = 6950 + H * 8 + Hkv + (d == 128) + 3 * (d in (32, 96))
+    cid = 6950 + H * 8 + Hkv + (d == 128) + 3 * (d in (32, 96)) + 5 * (d == 256)
     st = {"q": synthetic.full_storage(cid, "q", B, H, N, d, "bf16"),
           "do": synthetic.full_storage(cid, "do", B, H, N, d, "bf16"),
           "k": synthetic.full_storage(cid, "k", B, Hkv, N, d, "bf16"),
@@ -337,7 +345,7 @@ def test_varlen_backward(fa, lengths, d, causal):
     varlen_bwd_case(fa, 8200 + len(lengths) * 8 + (d == 128) * 2 + causal, lengths, 4, 2, d, causal)
 
 
-@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("d", [32, 96, 256])
 def test_varlen_backward_head_dims(fa, d):
     varlen_bwd_case(fa, 8250 + d, [5, 0, 130, 64, 1, 257], 4, 2, d, True)
 
