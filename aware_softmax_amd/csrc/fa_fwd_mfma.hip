@@ -900,14 +900,38 @@ constexpr int kRingV = 4;  // V ring: as K (equal rings make the buffers of an i
 // K and V tiles sit unpadded in LDS (rows of D bf16) because the LDS-DMA
 // writes 1 KiB per wave instruction contiguously.  Bank conflicts of the
 // MFMA operand reads are removed by XOR-swizzling the 16-byte chunks of
-// each row:
-//   K: chunk c of row r is stored at c ^ (r mod CPR) -- the 16 lanes reading
+// each row.  d = 128 (256-byte rows, one row per bank line):
+//   K: chunk c of row r is stored at c ^ (r mod 16) -- the 16 lanes reading
 //      one logical chunk of 16 consecutive rows hit 16 distinct chunks;
 //   V: chunk c of row r is stored at c ^ 4(r mod 4) -- the LDS serves a
 //      transposing 8-byte read 32 lanes (256 bytes over its 64 banks) at a
 //      time, and those lanes touch 4 consecutive rows x 4 chunks, which land
 //      on 16 distinct chunks (a factor of 2 instead of 4 spreads them over
 //      only half the banks: a two-way conflict on every V read).
+// d = 64 (128-byte rows, two rows per bank line, so the bank quad of chunk
+// p of row r is 8 (r mod 2) + p):
+//   K: chunk c of row r is stored at c ^ ((r >> 1) mod 8) -- among 16
+//      consecutive rows the 8 of one parity get 8 distinct masks;
+//   V: chunk c of row r is stored at c ^ 4 ((r >> 1) mod 2) -- of 4
+//      consecutive rows x an aligned group of 4 chunks, rows r0 + 2 and
+//      r0 + 3 move the group to the other half of the row and the parities
+//      split each pair: 16 distinct quads.  The mask repeats every 4 rows,
+//      so the 8- and 16-row steps of the reads stay immediate offsets.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (D == 128)
+    return r & 15;
+  else
+    return (r >> 1) & 7;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (D == 128)
+    return 4 * (r & 3);
+  else
+    return 4 * ((r >> 1) & 1);
+}
+
 template <int D>
 struct Layout {
   static constexpr int CPR = D / 8;
@@ -919,6 +943,7 @@ struct Layout {
   static constexpr int INSTR_PER_TILE = kBK / ROWS_PER_INSTR;
   static constexpr int INSTR_PER_WAVE = INSTR_PER_TILE / kWaves;
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
+  static_assert(D == 64 || D == 128, "row swizzles exist for 128- and 256-byte rows");
 };
 
 template <class T, int D, bool CAUSAL, bool FULL>
@@ -933,7 +958,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   constexpr int NV = (kBK / 16) * DB;
   constexpr int NK = 2 * DT;
   constexpr int IPW = Ly::INSTR_PER_WAVE;
-  static_assert(NV == 16 && NK == 16, "32 MFMA slots per iteration");
+  // 32 softmax slots per interval over its NK + NV MFMAs: one slot per
+  // MFMA at d = 128, two at d = 64.
+  constexpr int SPM = 16 / NK;
+  static_assert(NV == NK && NK * SPM == 16, "32 softmax slots per interval");
+  static_assert(NK % IPW == 0 && NK / IPW >= 4, "DMA instructions spread over the MFMAs");
   __shared__ __attribute__((aligned(1024))) T smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
@@ -1011,8 +1040,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * Ly::ROWS_PER_INSTR + dma_row;
-    dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (row % CPR)) * 16));
-    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ (4 * (row & 3))) * 16));
+    dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ swz_k<D>(row)) * 16));
+    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ swz_v<D>(row)) * 16));
   }
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
@@ -1024,7 +1053,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       off = decltype(is_v)::value ? dv_lane[i] : dk_lane[i];
     } else {
       const int row = r0 + dma_row;
-      const int chunk = decltype(is_v)::value ? (dma_chunk ^ (4 * (row & 3))) : (dma_chunk ^ (row % CPR));
+      const int chunk = dma_chunk ^ (decltype(is_v)::value ? swz_v<D>(row) : swz_k<D>(row));
       off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
     }
     __builtin_amdgcn_global_load_lds((const void*)(src + off),
@@ -1049,14 +1078,14 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
   unsigned k_off[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * D + (((2 * t + half) ^ (col % CPR)) * 8)) * 2u;
+  for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * D + (((2 * t + half) ^ swz_k<D>(col)) * 8)) * 2u;
   const int tr_e = (lane & 15) >> 2;
   const int tr_t = lane & 3;
   const int tr_cg = (lane >> 4) & 1;
   unsigned v_off[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
-    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ (4 * tr_e)) * 8) +
+    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ swz_v<D>(half * 4 + tr_e)) * 8) +
                           (tr_t & 1) * 4) * 2u;
   const unsigned smem_base = lds_addr(smem);
   // Absolute LDS addresses of buffer 0 of each ring; the buffer, the
@@ -1108,8 +1137,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], dst[F % 2]);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
-      if constexpr (DMA && F % 8 == 3) dma_any(Vh, dma_b, dma_t, F / 8, std::true_type{});
+      if constexpr (SM) {
+        fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
+        if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
+      }
+      if constexpr (DMA && F % (NK / IPW) == 3) dma_any(Vh, dma_b, dma_t, F / (NK / IPW), std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1147,8 +1179,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       oacc[b] = mfma32(vf, pfrag[u], oacc[b]);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) fast_slot<T, S0 + F>(fs, sc, c, m_run);
-      if constexpr (DMA && F % 8 == 3) dma_any(Kh, dma_b, dma_t, F / 8, std::false_type{});
+      if constexpr (SM) {
+        fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
+        if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
+      }
+      if constexpr (DMA && F % (NV / IPW) == 3) dma_any(Kh, dma_b, dma_t, F / (NV / IPW), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1340,16 +1375,18 @@ constexpr int kSplitMaxBlocks = 1024;
 
 template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  constexpr bool kDuo = D == 128;
-  const int bq = kDuo ? duo::kBQ : kBQ;
-  const int nqb = (p.N + bq - 1) / bq;
+  constexpr bool kCanDuo = D == 128 || D == 64;
   constexpr bool kCanSplit = D <= 96;
-  const bool split = kCanSplit && (int64_t)p.BH * nqb <= kSplitMaxBlocks;
+  const bool split = kCanSplit && (int64_t)p.BH * ((p.N + kBQ - 1) / kBQ) <= kSplitMaxBlocks;
+  // d = 64 runs the duo kernel on grids too large for the two-group split
+  const bool duo_k = D == 128 || (kCanDuo && !split);
+  const int bq = duo_k ? duo::kBQ : kBQ;
+  const int nqb = (p.N + bq - 1) / bq;
   const float c_signed = p.scale * 1.44269504088896340736f;
   const int negate = p.scale < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
   constexpr int kOS = D == 256 ? 2 : 1;  // d = 256: two waves per query block, each half of O
-  dim3 grid(p.BH * nqb), block(kDuo ? duo::kThreads : split ? 2 * kThreads : kOS * kThreads);
+  dim3 grid(p.BH * nqb), block(duo_k ? duo::kThreads : split ? 2 * kThreads : kOS * kThreads);
   const T* q = (const T*)p.q;
   const T* k = (const T*)p.k;
   const T* v = (const T*)p.v;
@@ -1363,13 +1400,20 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const void* fn;
   // FULL (no row clamping in the copies) needs every sequence to be a whole
   // number of key tiles: known only for fixed length.
-  if constexpr (kDuo)
+  if constexpr (D == 128) {
     fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
                                : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
-  else if constexpr (kCanSplit)
+  } else if constexpr (kCanDuo) {
+    if (duo_k)
+      fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
+                                 : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
+    else
+      fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2>;
+  } else if constexpr (kCanSplit) {
     fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
-  else
+  } else {
     fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1, kOS>;
+  }
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
