@@ -31,12 +31,14 @@
 //     HBM;
 //   * exp is the hardware exp2 with scale*log2(e) folded into one FMA.
 // Two kernels:
-//   * d = 64: 4 waves, 128 query rows per workgroup, K/V tiles staged
-//     through registers into padded, double-buffered LDS rows;
-//   * d = 128 ("duo"): 8 waves (two per SIMD), 256 query rows, K/V tiles
-//     copied HBM -> LDS by LDS-DMA into XOR-swizzled rings, every MFMA
-//     followed by a slot of softmax VALU work; steady tiles skip the row
-//     max (fixed reference max with an overflow check, see below).
+//   * d = 32, 96, 256: 4 waves, 128 query rows per workgroup, K/V tiles
+//     staged through registers into padded, double-buffered LDS rows;
+//   * d = 128 and 64 ("duo"): 8 waves (two per SIMD), 256 query rows (128
+//     with two wave groups over the key tiles on small grids, d = 64), K/V
+//     tiles copied HBM -> LDS by LDS-DMA into XOR-swizzled rings, every
+//     MFMA followed by one (d = 128) or two (d = 64) slots of softmax VALU
+//     work; steady tiles skip the row max (fixed reference max with an
+//     overflow check, see below).
 #include <math.h>
 #include <stdlib.h>
 
@@ -892,7 +894,13 @@ __device__ constexpr int kb_slot(T) {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBQ = 256;
+constexpr int kBQ = 256;  // query rows per workgroup with one wave group (G = 1)
+// G = 2 (small grids, d = 64): the two groups of 4 waves share 128 query
+// rows and take alternate key tiles, merging (m, l, O) at the end.
+template <int G>
+constexpr int block_q() {
+  return kBQ / G;
+}
 constexpr int kLead = 3;
 constexpr int kRingK = 4;  // K ring: tile being read, one landing, one being written, one spare
 constexpr int kRingV = 4;  // V ring: as K (equal rings make the buffers of an interval depend on j mod 4 only)
@@ -932,26 +940,31 @@ __device__ __forceinline__ int swz_v(int r) {
     return 4 * ((r >> 1) & 1);
 }
 
-template <int D>
+// A ring slot holds one key tile per wave group (G tiles of kBK rows, the
+// keys of one interval, contiguous in HBM and copied as one G kBK-row tile).
+template <int D, int G>
 struct Layout {
   static constexpr int CPR = D / 8;
-  static constexpr int TILE = kBK * D;
+  static constexpr int TILE = kBK * D;  // one group's tile
+  static constexpr int SLOT = G * TILE;
   static constexpr int K0 = 0;
-  static constexpr int V0 = kRingK * TILE;
-  static constexpr int TOTAL = (kRingK + kRingV) * TILE;
+  static constexpr int V0 = kRingK * SLOT;
+  static constexpr int TOTAL = (kRingK + kRingV) * SLOT;
   static constexpr int ROWS_PER_INSTR = 64 / CPR;
-  static constexpr int INSTR_PER_TILE = kBK / ROWS_PER_INSTR;
+  static constexpr int INSTR_PER_TILE = G * kBK / ROWS_PER_INSTR;  // per slot
   static constexpr int INSTR_PER_WAVE = INSTR_PER_TILE / kWaves;
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
   static_assert(D == 64 || D == 128, "row swizzles exist for 128- and 256-byte rows");
+  static_assert(TOTAL * 2 <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
-template <class T, int D, bool CAUSAL, bool FULL>
+template <class T, int D, bool CAUSAL, bool FULL, int G = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group, const int* __restrict__ cu_seqlens, int H, int total) {
-  using Ly = Layout<D>;
+  using Ly = Layout<D, G>;
+  constexpr int BQ = block_q<G>();
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
   constexpr int CPR = Ly::CPR;
@@ -973,7 +986,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
-  const int q0 = qb * kBQ;
+  const int q0 = qb * BQ;
   HeadRows hr = head_rows(bh, BH, group, N, D, cu_seqlens, H, total);
   if (cu_seqlens) {
     N = hr.n;
@@ -987,10 +1000,13 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
   // -inf * c stays -inf for hidden keys.
   c = fmaxf(c, 1e-30f);
-  // Waves w and w + 4 share a SIMD; give them rows 64(w%4) + 32(w/4) so the
-  // two waves of a SIMD meet the causal diagonal at the same tile (their
-  // numbers of visible tiles differ by at most one).
-  const int qw = q0 + (wave & 3) * 64 + (wave >> 2) * 32;
+  // Waves w and w + 4 share a SIMD.  G = 1: they get rows 64(w%4) + 32(w/4),
+  // so the two waves of a SIMD meet the causal diagonal at the same tile
+  // (their numbers of visible tiles differ by at most one).  G = 2: they
+  // get the same rows 32(w%4), wave w the even key tiles (group 0), wave
+  // w + 4 the odd ones (group 1).
+  const int grp = G == 2 ? (wave >> 2) : 0;
+  const int qw = G == 2 ? q0 + (wave & 3) * 32 : q0 + (wave & 3) * 64 + (wave >> 2) * 32;
   const int qi = qw + col;
   vec8<T> qf[DT];
   if (qi < N) {
@@ -1009,10 +1025,17 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
   }
 
-  int nkt = (N + kBK - 1) / kBK;
-  if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / kBK + 1);
-  int wave_nt = nkt;
-  if (CAUSAL) wave_nt = min(nkt, (qw + 31) / kBK + 1);
+  // Key tiles of kBK rows (global index t); the workgroup runs nkt
+  // intervals, interval j holding tiles G j .. G j + G - 1, and a wave
+  // handles tile G j + grp of interval j: below, wave_nt and nfull count
+  // the wave's own tiles (its local index j).
+  int nkt_all = (N + kBK - 1) / kBK;
+  if (CAUSAL) nkt_all = min(nkt_all, (q0 + BQ - 1) / kBK + 1);
+  const int nkt = (nkt_all + G - 1) / G;
+  // the number of the wave's tiles among tiles 0 .. x - 1
+  auto local = [&](int x) { return G == 1 ? x : max(0, (x - grp + 1) / 2); };
+  int wave_nt = nkt_all;
+  if (CAUSAL) wave_nt = min(nkt_all, (qw + 31) / kBK + 1);
   if (qw >= N) wave_nt = 0;
   // Tiles every row of this wave sees in full (the wave's own count: under
   // the causal mask a wave's rows meet the diagonal at tile qw / kBK, so
@@ -1020,6 +1043,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   int nfull = N / kBK;
   if (CAUSAL) nfull = min(nfull, qw / kBK);
   if (wave_nt == 0) nfull = 0;
+  wave_nt = local(wave_nt);
+  nfull = min(local(nfull), wave_nt - 1);
 
   f32x16 oacc[DB];
 #pragma unroll
@@ -1045,7 +1070,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   }
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
-    const int kt0 = t * kBK;
+    const int kt0 = t * G * kBK;
     const char* src = (const char*)(Xh + (size_t)kt0 * D);
     const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
     unsigned off;
@@ -1066,12 +1091,12 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     if constexpr (std::is_integral_v<decltype(buf)>) {
       dma_one(Xh, buf, t, i, is_v);
     } else {
-      constexpr int eoff = (decltype(is_v)::value ? Ly::V0 : Ly::K0) + kb_slot(buf) * Ly::TILE;
+      constexpr int eoff = (decltype(is_v)::value ? Ly::V0 : Ly::K0) + kb_slot(buf) * Ly::SLOT;
       dma_one(Xh, eoff, t, i, is_v);
     }
   };
-  auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::TILE; };
-  auto vbuf = [](int t) { return Ly::V0 + (t % kRingV) * Ly::TILE; };
+  auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::SLOT; };
+  auto vbuf = [](int t) { return Ly::V0 + (t % kRingV) * Ly::SLOT; };
   auto iteration_barrier = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(2 * IPW) : "memory");
   };
@@ -1087,7 +1112,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   for (int b = 0; b < DB; ++b)
     v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ swz_v<D>(half * 4 + tr_e)) * 8) +
                           (tr_t & 1) * 4) * 2u;
-  const unsigned smem_base = lds_addr(smem);
+  // (plus the byte offset of the wave's tile within a slot)
+  const unsigned smem_base = lds_addr(smem) + (unsigned)(grp * Ly::TILE * 2);
   // Absolute LDS addresses of buffer 0 of each ring; the buffer, the
   // 32-key half and the 16-key step then enter as instruction immediates.
   unsigned k_abs[DT], v_abs[DB];
@@ -1121,7 +1147,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
       if constexpr (CT)
-        read_k<kb_slot(kb) * Ly::TILE * 2 + (F % 2) * 32 * D * 2>(fr[F % kLead], k_abs[F / 2]);
+        read_k<kb_slot(kb) * Ly::SLOT * 2 + (F % 2) * 32 * D * 2>(fr[F % kLead], k_abs[F / 2]);
       else
         read_k<(F % 2) * 32 * D * 2>(fr[F % kLead], base + k_abs[F / 2]);
     };
@@ -1161,7 +1187,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       constexpr int F = decltype(fc)::value;
       constexpr int u = F / DB, b = F % DB;
       if constexpr (CT) {
-        constexpr int o = kb_slot(vb) * Ly::TILE * 2;
+        constexpr int o = kb_slot(vb) * Ly::SLOT * 2;
         read_v<o + u * 16 * D * 2, o + (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], v_abs[b]);
       } else {
         read_v<u * 16 * D * 2, (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], base + v_abs[b]);
@@ -1208,7 +1234,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   using On = std::true_type;
   using Off = std::false_type;
   auto masked_softmax = [&](int j) {
-    const int kt0 = j * kBK;
+    const int kt0 = (G * j + grp) * kBK;
     int lim = N - kt0 - half * 4;
     if (CAUSAL) lim = min(lim, qi - kt0 - half * 4 + 1);
     const float m_before = m_run;
@@ -1339,6 +1365,35 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   for (; j < nkt; ++j) general(j);
   if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (G == 2) {
+    // Merge the two groups' (m, l, O~) of the same rows through LDS (the
+    // rings are free once every wave has passed this barrier: its last
+    // reads are done and its copies have landed).  Both sides are exact
+    // for any reference m: O~ and l are rescaled by 2^(m_g - m_max).
+    constexpr int NX = DB * 16 + 2;
+    float* xs = (float*)smem + (wave & 3) * NX * 64 + lane;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xs[(b * 16 + e) * 64] = oacc[b][e];
+      xs[DB * 16 * 64] = m_run;
+      xs[(DB * 16 + 1) * 64] = l_part;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xs[DB * 16 * 64];
+    const float m_new = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[b][e] = oacc[b][e] * a0 + xs[(b * 16 + e) * 64] * a1;
+    l_part = l_part * a0 + xs[(DB * 16 + 1) * 64] * a1;
+    m_run = m_new;
+  }
 
   const float l_tot = swap_halves(l_part, false);
   if (qi < N) {
@@ -1359,18 +1414,21 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
 }  // namespace duo
 
-// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 (FULL when
-// the sequence is a whole number of key tiles: no row clamping in the
-// copies), the 4-wave kernel for d = 32, 64, 96 and 256 (at d <= 96 the
-// 2d/16 + 2d/16 MFMAs per tile leave too few slots to hide the softmax of a
-// 64-key tile; at d = 256 two waves per SIMD do not fit the registers).
-// Grids of at most this many workgroups run the d <= 96 kernel with two
-// wave groups over the keys (G = 2): with few workgroups per CU there is no
+// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 and 64
+// (FULL when the sequence is a whole number of copied tiles: no row
+// clamping in the copies; two softmax slots per MFMA at d = 64), the
+// 4-wave kernel for d = 32, 96 and 256 (at d = 256 two waves per SIMD do
+// not fit the registers).
+// Grids of at most this many workgroups of 128 rows run with two wave
+// groups over the keys of each row block (G = 2; the duo kernel at d = 64,
+// the 4-wave one at d = 32 and 96): with few workgroups per CU there is no
 // later workgroup to balance the causal row blocks, and the run takes as
-// long as the longest block's chain of key tiles.  Measured (causal bf16,
-// same box): +22 % at B1 H16 N2048 d64 (256 workgroups), +47 % at B1 H16
-// N4096 d64, +6 % at B2 H16 N4096 d64 (1024), -5 % at B4 H16 N2048 d64
-// (1024), -12 % at B2 H32 N8192 d64 (4096).
+// long as the longest block's chain of key tiles.  Measured with the 4-wave
+// kernel (causal bf16, same box): +22 % at B1 H16 N2048 d64 (256
+// workgroups), +47 % at B1 H16 N4096 d64, +6 % at B2 H16 N4096 d64 (1024),
+// -5 % at B4 H16 N2048 d64 (1024), -12 % at B2 H32 N8192 d64 (4096).  The
+// duo kernel with two groups, against the 4-wave one with two: B1 H16
+// N2048 d64 300 -> 412 TFLOP/s, B2 H16 N4096 d64 593 -> 768.
 constexpr int kSplitMaxBlocks = 1024;
 
 template <class T, int D, bool CAUSAL>
@@ -1378,9 +1436,11 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr bool kCanDuo = D == 128 || D == 64;
   constexpr bool kCanSplit = D <= 96;
   const bool split = kCanSplit && (int64_t)p.BH * ((p.N + kBQ - 1) / kBQ) <= kSplitMaxBlocks;
-  // d = 64 runs the duo kernel on grids too large for the two-group split
-  const bool duo_k = D == 128 || (kCanDuo && !split);
-  const int bq = duo_k ? duo::kBQ : kBQ;
+  // d = 64 runs the duo kernel on every grid: one wave group per 256 rows
+  // on large grids, two groups over the key tiles of 128 rows on small ones
+  const bool duo_k = kCanDuo;
+  const int duo_g = D == 64 && split ? 2 : 1;
+  const int bq = duo_k ? (duo_g == 2 ? duo::block_q<2>() : duo::block_q<1>()) : kBQ;
   const int nqb = (p.N + bq - 1) / bq;
   const float c_signed = p.scale * 1.44269504088896340736f;
   const int negate = p.scale < 0.f ? 1 : 0;
@@ -1399,16 +1459,17 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
   const void* fn;
   // FULL (no row clamping in the copies) needs every sequence to be a whole
-  // number of key tiles: known only for fixed length.
+  // number of copied tiles (G key tiles): known only for fixed length.
   if constexpr (D == 128) {
     fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
                                : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
   } else if constexpr (kCanDuo) {
-    if (duo_k)
+    if (duo_g == 2)
+      fn = !cu && p.N % (2 * kBK) == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true, 2>
+                                       : (const void*)duo::fwd_kernel<T, D, CAUSAL, false, 2>;
+    else
       fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
                                  : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
-    else
-      fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2>;
   } else if constexpr (kCanSplit) {
     fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
   } else {
@@ -1464,7 +1525,7 @@ hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
 // Waves per workgroup as launched on large grids (d <= 96 runs 8 waves, in
 // two key groups, only on grids of at most kSplitMaxBlocks workgroups).
 TileConfig mfma_tile(int d) {
-  if (d == 128) return TileConfig{duo::kBQ, kBK, duo::kWaves};
+  if (d == 128 || d == 64) return TileConfig{duo::kBQ, kBK, duo::kWaves};
   if (d == 256) return TileConfig{kBQ, kBK, 2 * kWaves};  // two waves per 32 query rows
   return TileConfig{kBQ, kBK, kWaves};
 }

@@ -165,8 +165,9 @@ const char* fa_status_string(fa_status_t status);
 /*
  * fa_fwd_tile -- the tile configuration fa_fwd uses for (d, dtype):
  * query rows per workgroup, keys per streamed tile and wavefronts per
- * workgroup (as launched on large grids: at d <= 96 a grid of at most 1024
- * workgroups runs twice as many waves, two groups splitting the keys).
+ * workgroup, as launched on large grids.  On small grids (at most 1024
+ * workgroups of 128 rows) d <= 96 runs two wave groups splitting the keys
+ * of each 128-row block: 8 waves at d = 32, 64 and 96.
  * Host-only; makes no HIP call.  Returns FA_OK or
  * FA_ERR_NULL / FA_ERR_DTYPE / FA_ERR_UNSUPPORTED_HEADDIM.
  */
