@@ -507,7 +507,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
   const int tr_e = (lane & 15) >> 2;
   const int tr_t = lane & 3;
   const int tr_cg = (lane >> 4) & 1;
-  const vec2<T> one = vec2<T>{(T)1.0f, (T)1.0f};
 
   if (nst > 0) {
     gload(0);
@@ -548,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
           const float p0 = x0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x0 - m_use);
           const float p1 = x1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x1 - m_use);
           const vec2<T> pr = __builtin_convertvector((f32x2){p0, p1}, vec2<T>);
-          lsum = dot2(T{}, __builtin_bit_cast(unsigned, pr), __builtin_bit_cast(unsigned, one), lsum);
+          lsum += p0 + p1;  // fp32 adds: a v_dot2 would wait for the matrix pipe
           w[e >> 1] = __builtin_bit_cast(unsigned, pr);
         }
         pf[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});

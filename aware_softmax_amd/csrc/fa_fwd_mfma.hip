@@ -65,28 +65,21 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// The two 16-bit element types: MFMA, the fp32 pair -> element pair
-// conversion (round to nearest even) and the dot product of a pair with an
-// fp32 accumulate.
+// The two 16-bit element types: MFMA and the fp32 pair -> element pair
+// conversion (round to nearest even).  Row sums of P are fp32 adds, not
+// v_dot2 of the packed pair with (1, 1): on gfx950 a v_dot2 waits for the
+// SIMD's matrix pipe, so beside the other wave's MFMAs it runs several
+// times slower than the two adds it replaces (measured: a softmax
+// instruction mix ran 1.8x faster beside an MFMA stream with adds).
 __device__ __forceinline__ f32x16 mfma32(const vec8<__bf16>& a, const vec8<__bf16>& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma32(const vec8<_Float16>& a, const vec8<_Float16>& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float dot2(vec2<__bf16> a, vec2<__bf16> b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
-}
-__device__ __forceinline__ float dot2(vec2<_Float16> a, vec2<_Float16> b, float c) {
-  return __builtin_amdgcn_fdot2(a, b, c, false);
-}
 template <class T>
 __device__ __forceinline__ vec2<T> cvt2(float a, float b) {
   return __builtin_convertvector((f32x2){a, b}, vec2<T>);
-}
-template <class T>
-__device__ __forceinline__ vec2<T> one2() {
-  return vec2<T>{(T)1.0f, (T)1.0f};
 }
 
 constexpr int kBQ = 128;  // query rows per workgroup
@@ -226,7 +219,6 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
   m_run = m_new;
   float lsum = l_part * alpha;
-  const vec2<T> one = one2<T>();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     unsigned w[4];
@@ -238,8 +230,7 @@ __device__ inline float tile_softmax(float (&sv)[32], float c, int lim_causal, i
       const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, c, -m_use));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, c, -m_use));
       const vec2<T> pr = cvt2<T>(p0, p1);
-      // Row sum of exactly the bf16 probabilities the P.V product uses.
-      lsum = dot2(pr, one, lsum);
+      lsum += p0 + p1;
       w[e >> 1] = __builtin_bit_cast(unsigned, pr);
     }
     pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
@@ -779,12 +770,12 @@ template <class T, int K>
 __device__ __forceinline__ void fast_slot(FastSoftmax& st, const f32x16 (&s)[2], float c, float m) {
   auto sv = [&](int i) { return s[i >> 4][i & 15]; };
   constexpr int r = K / 2;
-  const vec2<T> one = one2<T>();
   if constexpr (K % 2 == 0) {
     if constexpr (r >= 1) {
       constexpr int q = r - 1;
       const vec2<T> pr = cvt2<T>(st.p[0], st.p[1]);
-      st.ps[q & 3] = dot2(pr, one, q < 4 ? 0.f : st.ps[q & 3]);
+      const float pp = st.p[0] + st.p[1];
+      st.ps[q & 3] = q < 4 ? pp : st.ps[q & 3] + pp;
       st.w[q] = __builtin_bit_cast(unsigned, pr);
       asm volatile("" ::"v"(st.w[q]), "v"(st.ps[q & 3]));
     }
@@ -801,9 +792,8 @@ __device__ __forceinline__ void fast_slot(FastSoftmax& st, const f32x16 (&s)[2],
 // Packs pair 15 and returns the lane's partial row sum of the tile.
 template <class T>
 __device__ __forceinline__ float fast_finish(FastSoftmax& st, vec8<T> (&pfrag)[4]) {
-  const vec2<T> one = one2<T>();
   const vec2<T> pr = cvt2<T>(st.p[0], st.p[1]);
-  st.ps[3] = dot2(pr, one, st.ps[3]);
+  st.ps[3] += st.p[0] + st.p[1];
   st.w[15] = __builtin_bit_cast(unsigned, pr);
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -839,7 +829,6 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
   if (raise) m_run = m_tile;
   const float m_use = m_run == -INFINITY ? 0.f : m_run;
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
-  const vec2<T> one = one2<T>();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     unsigned w[4];
@@ -849,7 +838,7 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
       const float p0 = __builtin_amdgcn_exp2f(fmaf(s[i >> 4][i & 15], c, -m_use));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m_use));
       const vec2<T> pr = cvt2<T>(p0, p1);
-      ps[e >> 1] = dot2(pr, one, ps[e >> 1]);
+      ps[e >> 1] += p0 + p1;
       w[e >> 1] = __builtin_bit_cast(unsigned, pr);
     }
     pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
@@ -1262,8 +1251,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float ps[2] = {0.f, 0.f};
-    const vec2<T> one = one2<T>();
-#pragma unroll
+  #pragma unroll
     for (int u = 0; u < 4; ++u) {
       unsigned w[4];
 #pragma unroll
@@ -1272,7 +1260,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i >> 4][i & 15], c, -m_run));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[(i + 1) >> 4][(i + 1) & 15], c, -m_run));
         const vec2<T> pr = cvt2<T>(p0, p1);
-        ps[e >> 2] = dot2(pr, one, ps[e >> 2]);
+        ps[e >> 2] += p0 + p1;
         w[e >> 1] = __builtin_bit_cast(unsigned, pr);
       }
       pfrag[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});

@@ -44,8 +44,9 @@ def values(storage, dtype):
 
 
 def run_case(fa, config_id, B, H, N, d, dtype, causal, scale=None, heads=None, rows=None,
-             tensors=None):
-    """Runs fa.fwd and returns (max |dO|, max |dL|) against the oracle."""
+             tensors=None, stats=False):
+    """Runs fa.fwd and returns (max |dO|, max |dL|) against the oracle; with
+    stats, also max |O_ref| and max |v| over the checked heads."""
     import torch
 
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -56,6 +57,7 @@ def run_case(fa, config_id, B, H, N, d, dtype, causal, scale=None, heads=None, r
     torch.cuda.synchronize()
     heads = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
     err_o = err_l = 0.0
+    o_max = v_max = 0.0
     for b, h in heads:
         ob = o[b, h].float().cpu().numpy().astype(np.float64)
         lb = lse[b, h].cpu().numpy().astype(np.float64)
@@ -64,7 +66,9 @@ def run_case(fa, config_id, B, H, N, d, dtype, causal, scale=None, heads=None, r
         sel = slice(None) if rows is None else rows
         err_o = max(err_o, float(np.max(np.abs(ob[sel] - ref_o))))
         err_l = max(err_l, float(np.max(np.abs(lb[sel] - ref_l))))
-    return err_o, err_l
+        o_max = max(o_max, float(np.max(np.abs(ref_o))))
+        v_max = max(v_max, float(np.max(np.abs(values(tensors["v"][b, h], dtype)))))
+    return (err_o, err_l, o_max, v_max) if stats else (err_o, err_l)
 
 
 def assert_close(errs, dtype, scale_factor=1.0):
@@ -78,6 +82,24 @@ def assert_close(errs, dtype, scale_factor=1.0):
         to, tl = to * scale_factor, tl * scale_factor
     assert errs[0] <= to, f"max |O - oracle| = {errs[0]:.3e} > {to}"
     assert errs[1] <= tl, f"max |L - oracle| = {errs[1]:.3e} > {tl}"
+
+
+UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def assert_close_sharp(res, dtype):
+    """For adversarial score distributions (a few keys carry almost all of
+    a row's weight, so |O| approaches max |v|): the kernels round P to the
+    element type for the P.V product while l sums the unrounded fp32 P, so
+    O carries a relative perturbation of at most u (unit roundoff) of the
+    weights, |dO| <= u max|v|, plus the rounding of O itself, u |O|.  The
+    bound is max(tolerance, u (max|v| + max|O_ref|) + 1e-3); on the
+    workloads' random scores the fixed tolerance is the binding one."""
+    err_o, err_l, o_max, v_max = res
+    to, tl = TOL[dtype]
+    bound_o = max(to, UNIT_ROUNDOFF[dtype] * (v_max + o_max) + 1e-3)
+    assert err_o <= bound_o, f"max |O - oracle| = {err_o:.3e} > {bound_o:.3e}"
+    assert err_l <= tl, f"max |L - oracle| = {err_l:.3e} > {tl}"
 
 
 # ------------------------------------------------------------ the five workloads
@@ -307,8 +329,8 @@ def test_large_scores_d128(fa, causal, scale):
     (scale * sqrt(d) ~ 23: later tiles exceed it by dozens of log2 units),
     so the d = 128 kernel must raise its reference max mid-row many times."""
     d = 128
-    assert_close(run_case(fa, 4100 + int(scale * 10) + causal, 1, 2, 1000, d, "bf16", causal, scale=scale),
-                 "bf16")
+    assert_close_sharp(run_case(fa, 4100 + int(scale * 10) + causal, 1, 2, 1000, d, "bf16", causal, scale=scale,
+                                stats=True), "bf16")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -320,7 +342,7 @@ def test_key_magnitude_ramp_d128(fa, causal):
     st = {t: synthetic.full_storage(4200 + causal, t, 1, 2, n, d, "bf16") for t in ("q", "k", "v")}
     kv = synthetic.bf16_bits_to_f32(st["k"]) * (1.0 + np.arange(n, dtype=np.float32) / 16.0)[None, None, :, None]
     st["k"] = synthetic.bf16_round_bits(kv)
-    assert_close(run_case(fa, 0, 1, 2, n, d, "bf16", causal, tensors=st), "bf16")
+    assert_close_sharp(run_case(fa, 0, 1, 2, n, d, "bf16", causal, tensors=st, stats=True), "bf16")
 
 
 # d = 64 on grids above the two-group split limit (1024 workgroups of 128
@@ -335,7 +357,8 @@ def test_large_scores_d64_large_grid(fa, causal, scale):
     tile's row max, so the reference max is raised mid-row; 3 seeded heads."""
     cid = 4300 + int(scale * 10) + causal
     heads = synthetic.sample_heads(cid, 2, 72, 3)
-    assert_close(run_case(fa, cid, 2, 72, 1024, 64, "bf16", causal, scale=scale, heads=heads), "bf16")
+    assert_close_sharp(run_case(fa, cid, 2, 72, 1024, 64, "bf16", causal, scale=scale, heads=heads, stats=True),
+                       "bf16")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -347,7 +370,7 @@ def test_key_magnitude_ramp_d64_large_grid(fa, causal):
     kv = synthetic.bf16_bits_to_f32(st["k"]) * (1.0 + np.arange(n, dtype=np.float32) / 16.0)[None, None, :, None]
     st["k"] = synthetic.bf16_round_bits(kv)
     heads = synthetic.sample_heads(4400 + causal, B, H, 3)
-    assert_close(run_case(fa, 0, B, H, n, d, "bf16", causal, tensors=st, heads=heads), "bf16")
+    assert_close_sharp(run_case(fa, 0, B, H, n, d, "bf16", causal, tensors=st, heads=heads, stats=True), "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -435,7 +458,8 @@ def test_f16_forward_throughput_shape_sampled(fa):
 def test_f16_large_scores(fa, scale):
     """Scores of |scale| * q.k up to ~30: probabilities above the fp16 range
     must send the tile through the exact update (the overflow check)."""
-    assert_close(run_case(fa, 1910 + int(scale * 10), 1, 2, 1000, 128, "f16", True, scale=scale), "f16")
+    assert_close_sharp(run_case(fa, 1910 + int(scale * 10), 1, 2, 1000, 128, "f16", True, scale=scale, stats=True),
+                       "f16")
 
 
 # ------------------------------------------------------------ variable length
