@@ -182,6 +182,25 @@ __device__ __forceinline__ f32x16 mfma(const vec8<__bf16>& a, const vec8<__bf16>
 __device__ __forceinline__ f32x16 mfma(const vec8<_Float16>& a, const vec8<_Float16>& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+// dK^T / dV^T accumulation with the accumulator pinned to AGPRs (C and D
+// of the MFMA in the accumulation register file).  Left to itself the
+// compiler keeps part of the scores there as well and shuttles them with
+// v_accvgpr_mov (48 per tile at d = 128); pinned, dK and dV take 128 AGPRs,
+// everything else fits the VGPRs, and the backward is 8-10 % faster (B2 H16
+// N4096 d128 causal, same box).  The asm is opaque to the compiler's hazard
+// checks, so it carries its own: two wait states first (the B operand may
+// just have been written by VALU), and mfma_drain before the accumulators
+// are read.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const vec8<__bf16>& a, const vec8<__bf16>& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const vec8<_Float16>& a, const vec8<_Float16>& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulating MFMA and any other access of
+// its accumulator.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // Waits until all but this wave's last KEEP vector memory operations (the
 // LDS-DMA copies of the tile after next, issued this iteration) and all its
 // LDS operations are complete, then the workgroup barrier.  Vector memory
@@ -536,11 +555,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         if constexpr (X == 0) {
           const vec8<T> pf = __builtin_bit_cast(
               vec8<T>, (u32x4){pw[qb][4 * h2], pw[qb][4 * h2 + 1], pw[qb][4 * h2 + 2], pw[qb][4 * h2 + 3]});
-          dvT[bb] = mfma(join<T>(lo_[F % LB], hi_[F % LB]), pf, dvT[bb]);
+          mfma_acc(dvT[bb], join<T>(lo_[F % LB], hi_[F % LB]), pf);
         } else {
           const vec8<T> dsf = __builtin_bit_cast(
               vec8<T>, (u32x4){dw[qb][4 * h2], dw[qb][4 * h2 + 1], dw[qb][4 * h2 + 2], dw[qb][4 * h2 + 3]});
-          dkT[bb] = mfma(join<T>(lo_[F % LB], hi_[F % LB]), dsf, dkT[bb]);
+          mfma_acc(dkT[bb], join<T>(lo_[F % LB], hi_[F % LB]), dsf);
         }
         if constexpr (F + LB < NB) issue(ic<F + LB>{});
         // groups 2 (u + 1) and 2 (u + 1) + 1 after the first and second half
@@ -580,6 +599,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
     for (; it < nqt; ++it, ++v) iteration(v, it, std::true_type{});
   }
 
+  mfma_drain();
   // ---- dK = scale * (dK^T)^T, dV: lane writes key `key`, d = 32 b + 8 g + 4 half + {0..3}.
   if (part && key < N) {  // fp32 partials of this head subset
     const size_t plane = (size_t)hsplit * BHkv * N * D;

@@ -547,7 +547,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(
           const float p0 = x0 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x0 - m_use);
           const float p1 = x1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x1 - m_use);
           const vec2<T> pr = __builtin_convertvector((f32x2){p0, p1}, vec2<T>);
-          lsum += p0 + p1;  // fp32 adds: a v_dot2 would wait for the matrix pipe
+          // the converted values in fp32 (a v_dot2 would wait for the matrix pipe)
+          lsum += (float)pr[0] + (float)pr[1];
           w[e >> 1] = __builtin_bit_cast(unsigned, pr);
         }
         pf[u] = __builtin_bit_cast(vec8<T>, (u32x4){w[0], w[1], w[2], w[3]});
