@@ -51,9 +51,10 @@
 //     row-fragment reads (ds_read_b128) and the transposing reads are free
 //     of bank conflicts, and are filled by LDS-DMA (global_load_lds) two
 //     tiles ahead;
-//   * each tile is software-pipelined: the MFMAs that compute the next
-//     tile's scores run while the current tile's P and dS are exponentiated
-//     and packed on the VALU, then the current tile's gradient MFMAs run.
+//   * the exponentials and packing of a tile ride on its MFMAs: in
+//     bwd_dkdv those of the first 32-query block on the MFMAs that compute
+//     the second block's scores, the second block's on the first gradient
+//     MFMAs; in bwd_dq on the gradient MFMAs.
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
@@ -309,11 +310,13 @@ constexpr int dkdv_halves() {
 // Per 64-query tile and wave (32 keys):
 //   A  S = Q K^T - L/scale and dP = dO V^T - D  (4 DT MFMAs; row fragments
 //      of the Q and dO tiles, several in flight);
-//   V  P = 2^(c S), dS = P dP, both packed to bf16 (VALU only);
+//   V  P = 2^(c S), dS = P dP, both packed to bf16 (VALU only), in eight
+//      groups of 4 rows: those of query block 0 ride on the second half of
+//      A (block 1's MFMAs), those of block 1 on the first two steps of B;
 //   B  dV^T += dO^T P and dK^T += Q^T dS        (8 DBO MFMAs, transposing reads;
 //      DBO = the 32-column blocks of the workgroup's columns of dK and dV).
-// Iteration t runs A(t + 1) with V(t) riding on its MFMAs, then B(t); the
-// DMA of the tile RING - 1 ahead is in flight meanwhile; one barrier per
+// Iteration t runs A(t) and B(t) with V(t) spread over both; the DMA of
+// the tile RING - 1 ahead is in flight meanwhile; one barrier per
 // iteration.
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
@@ -533,11 +536,13 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         else
           dP[qb] = mfma(fa[F % LA], vf[t], dP[qb]);
         if constexpr (F + LA < NA) issue(ic<F + LA>{});
+        // groups 0-3 (query block 0, complete after the first half) ride on
+        // the second half's MFMAs, one after each quarter of it
+        constexpr int Q4 = DT / 2;
+        if constexpr (F >= 2 * DT && (F - 2 * DT) % Q4 == Q4 - 1) vgroup(ic<(F - 2 * DT) / Q4>{}, mask_c, it);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
-    vgroup(ic<0>{}, mask_c, it);
-    vgroup(ic<1>{}, mask_c, it);
     {
       s16x4 lo_[LB], hi_[LB];
       auto issue = [&](auto fc) {
@@ -562,11 +567,11 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
           mfma_acc(dkT[bb], join<T>(lo_[F % LB], hi_[F % LB]), dsf);
         }
         if constexpr (F + LB < NB) issue(ic<F + LB>{});
-        // groups 2 (u + 1) and 2 (u + 1) + 1 after the first and second half
-        // of step u's MFMAs
+        // groups 4 + 2u and 5 + 2u (query block 1, used from step 2 on)
+        // after the first and second half of step u < 2's MFMAs
         constexpr int per = 2 * DBO, f = F % per;
-        if constexpr (u < 3 && (f == per / 2 - 1 || f == per - 1))
-          vgroup(ic<2 * (u + 1) + (f == per - 1 ? 1 : 0)>{}, mask_c, it);
+        if constexpr (u < 2 && (f == per / 2 - 1 || f == per - 1))
+          vgroup(ic<4 + 2 * u + (f == per - 1 ? 1 : 0)>{}, mask_c, it);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
