@@ -888,6 +888,17 @@ __device__ inline float softmax_masked_inplace(f32x16 (&s)[2], float c, int lim,
 // only.
 namespace duo {
 
+// LDS-DMA through a buffer descriptor: the tile's base address sits in
+// scalar registers and each lane adds only its constant byte offset (no
+// 64-bit address arithmetic per copy on the VALU); rows past the end of
+// the sequence fall outside the descriptor's range and read as zeros.
+// Word 3 selects the plain 32-bit data format of gfx9-family descriptors.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned lds_u32;
+constexpr int kBufferWord3 = 0x00020000;
+__device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 template <class T>
 __device__ constexpr int kb_slot(T) {
   return T::value;
@@ -959,7 +970,7 @@ struct Layout {
   static_assert(TOTAL * 2 <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
-template <class T, int D, bool CAUSAL, bool FULL, int G = 1>
+template <class T, int D, bool CAUSAL, int G = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
@@ -1060,8 +1071,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
   const int dma_row = lane / CPR;
   const int dma_chunk = lane % CPR;
-  // Source byte offsets of the lane within a tile, for FULL launches (N a
-  // multiple of the tile: no row is ever clamped).
+  // Source byte offsets of the lane within a copied tile (the descriptor's
+  // range cuts rows past the end of the sequence).
   unsigned dk_lane[IPW], dv_lane[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
@@ -1072,18 +1083,12 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
     const int kt0 = t * G * kBK;
-    const char* src = (const char*)(Xh + (size_t)kt0 * D);
+    const int rows = min(N - kt0, G * kBK);
+    const uint64_t base = (uint64_t)(uintptr_t)(Xh + (size_t)kt0 * D);
+    const i32x4 rs = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32), rows * D * 2, kBufferWord3};
     const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
-    unsigned off;
-    if constexpr (FULL) {
-      off = decltype(is_v)::value ? dv_lane[i] : dk_lane[i];
-    } else {
-      const int row = r0 + dma_row;
-      const int chunk = dma_chunk ^ (decltype(is_v)::value ? swz_v<D>(row) : swz_k<D>(row));
-      off = (unsigned)(min(row, N - 1 - kt0) * (D * 2) + chunk * 16);
-    }
-    __builtin_amdgcn_global_load_lds((const void*)(src + off),
-                                     (__attribute__((address_space(3))) void*)(smem + buf + r0 * D), 16, 0, 0);
+    raw_buffer_load_lds(rs, (lds_u32*)(smem + buf + r0 * D), 16, (int)(decltype(is_v)::value ? dv_lane[i] : dk_lane[i]),
+                        0, 0, 0);
   };
   // DMA of tile t into a ring slot given as an element offset (general
   // path) or as integral_constant<int, slot> of the K (is_v false) or V
@@ -1415,8 +1420,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 }  // namespace duo
 
 // Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 and 64
-// (FULL when the sequence is a whole number of copied tiles: no row
-// clamping in the copies; two softmax slots per MFMA at d = 64), the
+// (two softmax slots per MFMA at d = 64), the
 // 4-wave kernel for d = 32, 96 and 256 (at d = 256 two waves per SIMD do
 // not fit the registers).
 // Grids of at most this many workgroups of 128 rows run with two wave
@@ -1458,18 +1462,10 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   int H = p.H, total = p.total;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
   const void* fn;
-  // FULL (no row clamping in the copies) needs every sequence to be a whole
-  // number of copied tiles (G key tiles): known only for fixed length.
   if constexpr (D == 128) {
-    fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
-                               : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
+    fn = (const void*)duo::fwd_kernel<T, D, CAUSAL>;
   } else if constexpr (kCanDuo) {
-    if (duo_g == 2)
-      fn = !cu && p.N % (2 * kBK) == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true, 2>
-                                       : (const void*)duo::fwd_kernel<T, D, CAUSAL, false, 2>;
-    else
-      fn = !cu && p.N % kBK == 0 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, true>
-                                 : (const void*)duo::fwd_kernel<T, D, CAUSAL, false>;
+    fn = duo_g == 2 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 2> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
   } else if constexpr (kCanSplit) {
     fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
   } else {
