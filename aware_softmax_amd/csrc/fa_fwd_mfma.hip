@@ -970,13 +970,26 @@ struct Layout {
   static_assert(TOTAL * 2 <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
-template <class T, int D, bool CAUSAL, int G = 1>
+// PERSIST: a grid of W workgroups per XCD (one per CU) walks the XCD's
+// items -- its heads one after the other, each head's query blocks heaviest
+// first -- dealt to the W workgroups in snake order (W items forward, the
+// next W backward), so the XCD's CUs stream the K and V of one or two heads
+// at a time (shared in its L2) and every workgroup's total pairs heavy
+// blocks with light ones.  The copies
+// that, on an item's last intervals, would re-read its last tile fetch the
+// next item's first K and V tiles instead (each item is a whole number of
+// ring periods), and the next Q block is loaded while the item's last P.V
+// and its stores run: no workgroup launch and no cold prologue per item.
+// Only for fixed length with N a multiple of the 256-row block and every
+// XCD holding whole heads.
+template <class T, int D, bool CAUSAL, int G = 1, bool PERSIST = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group, const int* __restrict__ cu_seqlens, int H, int total) {
   using Ly = Layout<D, G>;
   constexpr int BQ = block_q<G>();
+  static_assert(!PERSIST || G == 1, "persistent launches run one wave group");
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
   constexpr int CPR = Ly::CPR;
@@ -996,18 +1009,25 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  int bh, qb;
-  map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
-  const int q0 = qb * BQ;
-  HeadRows hr = head_rows(bh, BH, group, N, D, cu_seqlens, H, total);
-  if (cu_seqlens) {
-    N = hr.n;
-    if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
-  }
-  const size_t head = hr.q;
-  const T* Qh = Qg + head;
-  const T* Kh = Kg + hr.kv;
-  const T* Vh = Vg + hr.kv;
+  // The k-th item (head, query block) of this workgroup.
+  auto item = [&](int k, int* bh, int* qb) -> bool {
+    if constexpr (!PERSIST) {
+      if (k > 0) return false;
+      map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, bh, qb);
+      return true;
+    } else {
+      const int per = BH * nqb / kNumXcd;  // items of this XCD
+      const int W = (int)gridDim.x / kNumXcd;
+      const int xcd = (int)blockIdx.x % kNumXcd, wg = (int)blockIdx.x / kNumXcd;
+      const int p = k * W + ((k & 1) ? W - 1 - wg : wg);
+      if (p >= per) return false;
+      const int hd = p / nqb;          // head of this XCD
+      const int rank = p - hd * nqb;   // 0 = heaviest
+      *bh = xcd * (per / nqb) + hd;
+      *qb = CAUSAL ? nqb - 1 - rank : rank;
+      return true;
+    }
+  };
 
   // A zero scale becomes 1e-30: every P stays exactly 1 in fp32 while
   // -inf * c stays -inf for hidden keys.
@@ -1018,17 +1038,41 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   // get the same rows 32(w%4), wave w the even key tiles (group 0), wave
   // w + 4 the odd ones (group 1).
   const int grp = G == 2 ? (wave >> 2) : 0;
-  const int qw = G == 2 ? q0 + (wave & 3) * 32 : q0 + (wave & 3) * 64 + (wave >> 2) * 32;
-  const int qi = qw + col;
+  const int q_rel = G == 2 ? (wave & 3) * 32 : (wave & 3) * 64 + (wave >> 2) * 32;
   vec8<T> qf[DT];
-  if (qi < N) {
-    const vec8<T>* src = (const vec8<T>*)(Qh + (size_t)qi * D + half * 8);
+  auto load_q = [&](const T* Qh, int qi, int n) {
+    if (qi < n) {
+      const vec8<T>* src = (const vec8<T>*)(Qh + (size_t)qi * D + half * 8);
 #pragma unroll
-    for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
-  } else {
+      for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
+    } else {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) qf[t] = vec8<T>{};
+      for (int t = 0; t < DT; ++t) qf[t] = vec8<T>{};
+    }
+  };
+
+  int bh, qb;
+  bool have = item(0, &bh, &qb);
+  for (int k_item = 0; have; ++k_item) {
+  int nbh = 0, nqbi = 0;
+  const bool more = PERSIST && item(k_item + 1, &nbh, &nqbi);
+  const int q0 = qb * BQ;
+  HeadRows hr = head_rows(bh, BH, group, N, D, cu_seqlens, H, total);
+  if (cu_seqlens) {
+    N = hr.n;
+    if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
   }
+  const size_t head = hr.q;
+  const T* Qh = Qg + head;
+  const T* Kh = Kg + hr.kv;
+  const T* Vh = Vg + hr.kv;
+  // the next item's K and V heads (persistent launches)
+  const HeadRows hn = head_rows(nbh, BH, group, N, D, cu_seqlens, H, total);
+  const T* Kn = Kg + hn.kv;
+  const T* Vn = Vg + hn.kv;
+  const int qw = q0 + q_rel;
+  const int qi = qw + col;
+  if (k_item == 0) load_q(Qh, qi, N);  // later items' Q blocks come with the previous item
   if (negate) {  // scale < 0: use -Q and |scale| (negation is exact)
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
@@ -1081,7 +1125,12 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ swz_v<D>(row)) * 16));
   }
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
-    t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
+    if (PERSIST && more && t >= nkt) {  // the next item's tile t - nkt (same ring slot: nkt is a multiple of 4)
+      Xh = decltype(is_v)::value ? Vn : Kn;
+      t -= nkt;
+    } else {
+      t = min(t, nkt - 1);  // tiles past the last one re-read it (never used)
+    }
     const int kt0 = t * G * kBK;
     const int rows = min(N - kt0, G * kBK);
     const uint64_t base = (uint64_t)(uintptr_t)(Xh + (size_t)kt0 * D);
@@ -1321,14 +1370,16 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     iteration_barrier();
   };
 
+  if (k_item == 0) {  // later items' first tiles were copied during the previous item
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    dma_one(Kh, kbuf(0), 0, i, Off{});
-    dma_one(Kh, kbuf(1), 1, i, Off{});
-    dma_one(Kh, kbuf(2), 2, i, Off{});
-    dma_one(Vh, vbuf(0), 0, i, On{});
+    for (int i = 0; i < IPW; ++i) {
+      dma_one(Kh, kbuf(0), 0, i, Off{});
+      dma_one(Kh, kbuf(1), 1, i, Off{});
+      dma_one(Kh, kbuf(2), 2, i, Off{});
+      dma_one(Vh, vbuf(0), 0, i, On{});
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   const int jend = min(nfull, nkt - 1);
   if (wave_nt > 0) qk(kbuf(0), Off{}, Off{}, 0, 0, S_lo{}, sacc, sacc);
   general(0);
@@ -1368,8 +1419,10 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     }
   }
   for (; j < nkt; ++j) general(j);
+  // every Q.K of the item is done: load the next item's Q block
+  if (more) load_q(Qg + hn.q, nqbi * BQ + q_rel + col, N);
   if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (G == 2) {
     // Merge the two groups' (m, l, O~) of the same rows through LDS (the
     // rings are free once every wave has passed this barrier: its last
@@ -1415,6 +1468,10 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       }
     if (half == 0) Lg[hr.l + qi] = (m_run + log2f(l_tot)) * 0.69314718055994530942f;
   }
+  bh = nbh;
+  qb = nqbi;
+  have = more;
+  }
 }
 
 }  // namespace duo
@@ -1435,6 +1492,19 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 // N2048 d64 300 -> 412 TFLOP/s, B2 H16 N4096 d64 593 -> 768.
 constexpr int kSplitMaxBlocks = 1024;
 
+// Compute units of the current device (cached per device; 0 if unknown).
+inline int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   constexpr bool kCanDuo = D == 128 || D == 64;
@@ -1451,6 +1521,13 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const float c = negate ? -c_signed : c_signed;
   constexpr int kOS = D == 256 ? 2 : 1;  // d = 256: two waves per query block, each half of O
   dim3 grid(p.BH * nqb), block(duo_k ? duo::kThreads : split ? 2 * kThreads : kOS * kThreads);
+  // Persistent duo launch: fixed length, whole 256-row blocks, every XCD
+  // holding whole heads; one workgroup per CU.
+  const int64_t items = (int64_t)p.BH * nqb;
+  const int cus = device_cus();
+  const bool persist = duo_k && duo_g == 1 && !p.cu_seqlens && p.N % duo::kBQ == 0 && items % kNumXcd == 0 &&
+                       (items / kNumXcd) % nqb == 0 && cus >= kNumXcd;
+  if (persist) grid = dim3((unsigned)(kNumXcd * std::min<int64_t>(cus / kNumXcd, items / kNumXcd)));
   const T* q = (const T*)p.q;
   const T* k = (const T*)p.k;
   const T* v = (const T*)p.v;
@@ -1462,10 +1539,11 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   int H = p.H, total = p.total;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
   const void* fn;
-  if constexpr (D == 128) {
-    fn = (const void*)duo::fwd_kernel<T, D, CAUSAL>;
-  } else if constexpr (kCanDuo) {
-    fn = duo_g == 2 ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 2> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
+  if constexpr (kCanDuo) {
+    fn = persist ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 1, true> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
+    if constexpr (D == 64) {
+      if (duo_g == 2) fn = (const void*)duo::fwd_kernel<T, D, CAUSAL, 2>;
+    }
   } else if constexpr (kCanSplit) {
     fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
   } else {

@@ -383,6 +383,32 @@ def test_d64_throughput_shape_sampled(fa, dtype):
                           heads=synthetic.sample_heads(cid, 8, 32, 4)), dtype)
 
 
+# Persistent launches: fixed length, N a multiple of 256 and every XCD
+# holding whole heads (B * H * N / 256 a multiple of 8 with the per-XCD
+# share a multiple of N / 256) run one workgroup per CU over a snake-ordered
+# item list, each item's first K/V tiles copied during the previous one.
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [-0.3, 0.2])
+def test_persistent_scales_d128(fa, causal, scale):
+    """B2 H8 N1024 d128 (64 items, 8 per XCD): negated Q on every item of a
+    workgroup (the negation applies to the Q block loaded by the previous
+    item); 4 seeded heads."""
+    cid = 4600 + int(scale * 10) + causal
+    heads = synthetic.sample_heads(cid, 2, 8, 4)
+    assert_close(run_case(fa, cid, 2, 8, 1024, 128, "bf16", causal, scale=scale, heads=heads), "bf16")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_persistent_d64(fa, causal):
+    """B4 H72 N512 d64 (576 items of 256 rows; above the two-group limit, so
+    the persistent one-group launch); 4 seeded heads, every row."""
+    cid = 4700 + causal
+    heads = synthetic.sample_heads(cid, 4, 72, 4)
+    assert_close(run_case(fa, cid, 4, 72, 512, 64, "bf16", causal, heads=heads), "bf16")
+
+
 # ------------------------------------------------------------ grouped key/value heads
 
 
