@@ -1,6 +1,6 @@
 """Throughput of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-legs] [--extra]
 
 A step is one fa_fwd over the whole causal bf16 workload B=8, H=32,
 N=8192, d=128 (scale 1/sqrt(d)), inputs resident in HBM before timing.
@@ -465,7 +465,8 @@ def time_decode(fa, w, q, k, v, num_splits, steps, warmup):
 def time_default_legs(fa):
     """The other measured workloads, in every default run (after the headline
     leg, outside its timed region): causal bf16 forward on B1 H16 N2048 d64,
-    B1 H16 N32768 d128 (batch-1 long context) and B2 H16 N4096 d128, the
+    B8 H32 N8192 d64, B1 H16 N32768 d128 (batch-1 long context) and B2 H16
+    N4096 d128, the
     backward of the last and of B2 H8 N4096 d256, and split-K decode on B8
     H32 N32768 d128.  Inputs are the seeded workloads of the parity tests
     (the d256 one drawn the same way); each leg frees its tensors."""
@@ -478,8 +479,9 @@ def time_default_legs(fa):
     legs = {}
     w256 = dataclasses.replace(synthetic.WORKLOADS[5], config_id=9400, name="causal bf16 backward B2 H8 N4096 d256",
                                H=8, d=256)
-    for cid in (2, 4, 5, 256):
-        ww = w256 if cid == 256 else synthetic.WORKLOADS[cid]
+    w64 = dataclasses.replace(synthetic.WORKLOADS[3], config_id=4500, name="causal bf16 B8 H32 N8192 d64", d=64)
+    for cid in (2, 64, 4, 5, 256):
+        ww = {256: w256, 64: w64}.get(cid) or synthetic.WORKLOADS[cid]
         qq, kk, vv = make_inputs(ww)
         oo = torch.empty_like(qq)
         ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
@@ -724,6 +726,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the other workloads' legs (profiling runs: some legs launch the headline kernel)")
     ap.add_argument("--extra", action="store_true", help="also time the other workloads and non-causal")
     ap.add_argument("--profile-run", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
@@ -854,7 +858,8 @@ def main():
     }
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    result["workloads"] = time_default_legs(fa)
+    if not args.no_legs:
+        result["workloads"] = time_default_legs(fa)
     if args.extra:
         extra = {}
         for cid in (2, 4, 5):
