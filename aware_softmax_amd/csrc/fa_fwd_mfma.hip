@@ -1222,7 +1222,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
         if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
       }
-      if constexpr (DMA && F % (NK / IPW) == 3) dma_any(Vh, dma_b, dma_t, F / (NK / IPW), std::true_type{});
+      if constexpr (DMA && F % (NK / IPW) == (NK / IPW) - 1) dma_any(Vh, dma_b, dma_t, F / (NK / IPW), std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -1264,7 +1264,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
         if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
       }
-      if constexpr (DMA && F % (NV / IPW) == 3) dma_any(Kh, dma_b, dma_t, F / (NV / IPW), std::false_type{});
+      if constexpr (DMA && F % (NV / IPW) == (NV / IPW) - 1) dma_any(Kh, dma_b, dma_t, F / (NV / IPW), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
   };
