@@ -211,28 +211,53 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(KEEP) : "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned lds_u32;
+// Word 3 of a gfx9-family buffer descriptor: the plain 32-bit data format.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
-// Copies rows [r0, r0 + kRows) of a row-major [N][D] 16-bit matrix into a
-// swizzled LDS tile (rows past N - 1 are clamped; their values are never
-// used unmasked).  One wave instruction writes 1 KiB of LDS contiguously
-// (lane l at byte 16 l); the swizzle is applied by choosing which logical
-// chunk each lane fetches.  Wave w issues instructions [w IPW, (w + 1) IPW).
-template <int D, int kRows, class T>
-__device__ __forceinline__ void dma_rows(const T* X, int r0, int N, char* tile, int wave, int lane) {
-  constexpr int ROWB = 2 * lds_row_elems<D>(), CPR = ROWB / 16, RPI = 1024 / ROWB;
-  constexpr int IPW = kRows * ROWB / 1024 / kWaves;
-  static_assert(kRows * ROWB % (1024 * kWaves) == 0, "DMA splits evenly over waves");
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int inst = wave * IPW + i;
-    const int row = inst * RPI + lane / CPR;
-    const int slot = (lane % CPR) ^ swz_mask<ROWB>(row);  // logical chunk of this LDS slot
-    const int chunk = slot < D / 8 ? slot : slot - D / 8;   // pad slots: a copy of a real chunk
-    const size_t off = (size_t)min(r0 + row, N - 1) * D + chunk * 8;
-    __builtin_amdgcn_global_load_lds((const void*)(X + off), (lds_void*)(tile + inst * 1024), 16, 0, 0);
-  }
+// Buffer descriptor of the `bytes` bytes at p, kept in scalar registers
+// (every argument is uniform over the wave; readfirstlane says so).
+__device__ __forceinline__ i32x4 buffer_desc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return {__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)),
+          __builtin_amdgcn_readfirstlane(bytes), kBufferWord3};
 }
+
+// LDS-DMA of rows [r0, r0 + kRows) of a row-major [N][D] 16-bit matrix into
+// a swizzled LDS tile.  One wave instruction writes 1 KiB of LDS
+// contiguously (lane l at byte 16 l); the swizzle is applied by choosing
+// which logical chunk each lane fetches.  The tile's first row is the base
+// of a buffer descriptor and each lane adds a constant byte offset, so a
+// copy costs no vector ALU work; rows past N - 1 fall outside the
+// descriptor's range and read as zeros (they are masked wherever they
+// enter).  Wave w issues instructions [w IPW, (w + 1) IPW).
+template <int D, int kRows>
+struct RowTileDma {
+  static constexpr int ROWB = 2 * lds_row_elems<D>(), CPR = ROWB / 16, RPI = 1024 / ROWB;
+  static constexpr int IPW = kRows * ROWB / 1024 / kWaves;
+  static_assert(kRows * ROWB % (1024 * kWaves) == 0, "DMA splits evenly over waves");
+  unsigned off[IPW];  // byte offset of this lane's chunk from the tile's first row
+  __device__ RowTileDma(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = (wave * IPW + i) * RPI + lane / CPR;
+      const int slot = (lane % CPR) ^ swz_mask<ROWB>(row);  // logical chunk of this LDS slot
+      const int chunk = slot < D / 8 ? slot : slot - D / 8;   // pad slots: a copy of a real chunk
+      off[i] = (unsigned)(row * D * 2 + chunk * 16);
+    }
+  }
+  template <class T>
+  __device__ i32x4 desc(const T* X, int r0, int N) const {
+    return buffer_desc(X + (size_t)r0 * D, min(max(N - r0, 0), kRows) * D * 2);
+  }
+  // instruction i of this wave
+  __device__ void copy(const i32x4& rs, char* tile, int wave, int i) const {
+    raw_buffer_load_lds(rs, (lds_u32*)(tile + (wave * IPW + i) * 1024), 16, (int)off[i], 0, 0, 0);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // bwd_pre: one row per LPR lanes (CPL 16-byte chunks of dO and O each; LPR
@@ -411,20 +436,38 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   const int span = nqt - it0;
   const int total = hc * span;
   auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % RING); };
-  constexpr int kDmaPerWave = 1 + 2 * (Ly::QTILE / 1024 / kWaves);  // statistics, Q, dO
-  auto dma_tile = [&](int v) {
-    const int b = ring(v);
+  using QDma = RowTileDma<D, kBQ>;
+  const QDma qdma(wave, lane);
+  constexpr int kDmaPerWave = 1 + 2 * QDma::IPW;  // statistics, Q, dO
+  static_assert(kDmaPerWave <= NA, "the copies of a tile ride on phase A's MFMAs");
+  // Descriptors of tile v: its 64 statistics (-L/scale for waves 0 and 2,
+  // -D for waves 1 and 3: the duplicate copy writes the same bytes and keeps
+  // the number of DMA instructions per wave uniform for the waits), Q, dO.
+  struct TileDesc {
+    i32x4 st, q, dO;
+  };
+  auto tile_desc = [&](int v) {
     const int rr = __builtin_amdgcn_readfirstlane(v / span);
     const int r = hs + rr;
     const int it = it0 + v - rr * span;
     const size_t qhead = q_off(r);
-    // the tile's 64 statistics: -L/scale by waves 0 and 2, -D by waves 1
-    // and 3 (the duplicate copy writes the same bytes; it keeps the number
-    // of DMA instructions per wave uniform for the waits)
-    __builtin_amdgcn_global_load_lds((const void*)((wave & 1 ? Dng : Lsg) + st_off(r) + it * kBQ + lane),
-                                     (lds_void*)(smem + Ly::OFF_ST + b * Ly::STTILE + (wave & 1) * 4 * kBQ), 4, 0, 0);
-    dma_rows<D, kBQ>(Qg + qhead, it * kBQ, N, smem + Ly::OFF_Q + b * Ly::QTILE, wave, lane);
-    dma_rows<D, kBQ>(dOg + qhead, it * kBQ, N, smem + Ly::OFF_DO + b * Ly::QTILE, wave, lane);
+    return TileDesc{buffer_desc((wave & 1 ? Dng : Lsg) + st_off(r) + it * kBQ, kBQ * 4),
+                    qdma.desc(Qg + qhead, it * kBQ, N), qdma.desc(dOg + qhead, it * kBQ, N)};
+  };
+  // DMA instruction k of this wave for a tile with descriptors t into ring buffer b
+  auto dma_op = [&](const TileDesc& t, int b, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k == 0)
+      raw_buffer_load_lds(t.st, (lds_u32*)(smem + Ly::OFF_ST + b * Ly::STTILE + (wave & 1) * 4 * kBQ), 4, lane * 4,
+                          0, 0, 0);
+    else if constexpr (k <= QDma::IPW)
+      qdma.copy(t.q, smem + Ly::OFF_Q + b * Ly::QTILE, wave, k - 1);
+    else
+      qdma.copy(t.dO, smem + Ly::OFF_DO + b * Ly::QTILE, wave, k - 1 - QDma::IPW);
+  };
+  auto dma_tile = [&](int v) {
+    const TileDesc t = tile_desc(v);
+    static_for<kDmaPerWave>([&](auto kc) { dma_op(t, ring(v), kc); });
   };
 
   // Lane-constant LDS byte offsets within a tile.
@@ -493,7 +536,13 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   // riding on the MFMAs of step u (groups 0 and 1 run before step 0).
   auto iteration = [&](int v, int it, auto mask_c) {
     const int b = ring(v);
-    if (v + PF < total) dma_tile(v + PF);
+    // The copies of tile v + PF ride on phase A's MFMAs, one every
+    // kDmaStride.  Past the last tile they repeat it into the buffer of tile
+    // v - 1 (already consumed, never read again): no branch in the MFMA
+    // stream, and the waits below count the same instructions.
+    const TileDesc nt = tile_desc(min(v + PF, total - 1));
+    const int nb = ring(v + PF);
+    constexpr int kDmaStride = PF == 1 ? 1 : NA / kDmaPerWave;  // one tile ahead: copy early
     const unsigned aq = sbase + Ly::OFF_Q + b * Ly::QTILE;
     const unsigned ado = sbase + Ly::OFF_DO + b * Ly::QTILE;
     {
@@ -536,6 +585,8 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
         else
           dP[qb] = mfma(fa[F % LA], vf[t], dP[qb]);
         if constexpr (F + LA < NA) issue(ic<F + LA>{});
+        if constexpr (F % kDmaStride == 0 && F / kDmaStride < kDmaPerWave)
+          dma_op(nt, nb, ic<F / kDmaStride>{});
         // groups 0-3 (query block 0, complete after the first half) ride on
         // the second half's MFMAs, one after each quarter of it
         constexpr int Q4 = DT / 2;
@@ -767,12 +818,19 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   int nkt = (N + kBKdq - 1) / kBKdq;
   if (CAUSAL) nkt = min(nkt, (q0 + kBQdq - 1) / kBKdq + 1);
   auto ring = [&](int j) { return __builtin_amdgcn_readfirstlane(j % kRing); };
-  constexpr int kDmaPerWave = 2 * (Ly::KTILE / 1024 / kWaves);  // K, V
-  auto dma_tile = [&](int j) {
-    const int b = ring(j);
-    dma_rows<D, kBKdq>(Kh, j * kBKdq, N, smem + Ly::OFF_K + b * Ly::KTILE, wave, lane);
-    dma_rows<D, kBKdq>(Vh, j * kBKdq, N, smem + Ly::OFF_V + b * Ly::KTILE, wave, lane);
+  using KDma = RowTileDma<D, kBKdq>;
+  const KDma kdma(wave, lane);
+  constexpr int kDmaPerWave = 2 * KDma::IPW;  // K, V
+  static_assert(kDmaPerWave <= NA, "the copies of a tile ride on phase A's MFMAs");
+  // DMA instruction k of this wave for key tile j into ring buffer b
+  auto dma_op = [&](int j, int b, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (k < KDma::IPW)
+      kdma.copy(kdma.desc(Kh, j * kBKdq, N), smem + Ly::OFF_K + b * Ly::KTILE, wave, k);
+    else
+      kdma.copy(kdma.desc(Vh, j * kBKdq, N), smem + Ly::OFF_V + b * Ly::KTILE, wave, k - KDma::IPW);
   };
+  auto dma_tile = [&](int j) { static_for<kDmaPerWave>([&](auto kc) { dma_op(j, ring(j), kc); }); };
 
   unsigned rf_lane[KB];  // K / V row fragments: row 32 kb + col, chunk 2t + half
 #pragma unroll
@@ -825,7 +883,12 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
 
   auto iteration = [&](int j, auto mask_c) {
     const int b = ring(j);
-    if (j + 2 < nkt) dma_tile(j + 2);
+    // The copies of tile j + 2 ride on phase A's MFMAs, one every
+    // kDmaStride; past the last tile they repeat it into the buffer of tile
+    // j - 1 (consumed, never read again).
+    const int jn = min(j + 2, nkt - 1);
+    const int nb = ring(j + 2);
+    constexpr int kDmaStride = NA / kDmaPerWave;
     const unsigned ak = sbase + Ly::OFF_K + b * Ly::KTILE;
     const unsigned av = sbase + Ly::OFF_V + b * Ly::KTILE;
     {
@@ -851,6 +914,8 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
         else
           dP[kb] = mfma(fa[F % LA], dof[t], dP[kb]);
         if constexpr (F + LA < NA) issue(ic<F + LA>{});
+        if constexpr (F % kDmaStride == 0 && F / kDmaStride < kDmaPerWave)
+          dma_op(jn, nb, ic<F / kDmaStride>{});
         __builtin_amdgcn_sched_barrier(0);
       });
     }
