@@ -454,7 +454,8 @@ def test_library_imports_no_allocator(fa):
     frees or clears device or host memory through the HIP runtime -- it does
     not even import those routines.  The imported HIP symbols are limited to
     kernel registration and launch, error reporting and the address lookup
-    of a static device array."""
+    of a static device array, plus the compute-unit count query that sizes a
+    persistent grid."""
     out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     hip = sorted({line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()})
@@ -468,7 +469,8 @@ def test_library_imports_no_allocator(fa):
             assert bad not in low, f"libfa.so imports {name}"
     allowed = {"__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
                "__hipRegisterFunction", "__hipUnregisterFatBinary", "__hipRegisterVar", "hipGetErrorString",
-               "hipGetLastError", "hipLaunchKernel", "hipGetSymbolAddress", "hipGetDevice"}
+               "hipGetLastError", "hipLaunchKernel", "hipGetSymbolAddress", "hipGetDevice",
+               "hipDeviceGetAttribute"}
     assert set(hip) <= allowed, f"unexpected HIP imports: {sorted(set(hip) - allowed)}"
 
 
