@@ -124,6 +124,26 @@ def make_inputs(w, threads=16):
     return out
 
 
+def prewarm(fn, ms=200.0):
+    """Calls fn() back to back until about `ms` of GPU time has passed
+    (untimed).  After an idle spell the first tens of milliseconds of
+    launches run 3-6 % slower than the steady state (clock and memory
+    system ramping up); every timed region below starts after such a
+    stretch of the same launches."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    done, n = 0.0, 1
+    while done < ms and n < 100000:
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        done += a.elapsed_time(b)
+        n = min(2 * n, 1000)
+
+
 def time_launches(fa, q, k, v, o, lse, causal, scale, steps, warmup):
     import torch
 
@@ -200,6 +220,7 @@ def time_backward(fa, w, q, k, v, o, lse, steps, warmup):
     def step():
         fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
+    prewarm(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -240,6 +261,7 @@ def time_gqa(fa, steps=10, warmup=2):
         label = f"causal bf16 B{B} H{H} Hkv{Hkv} N{N} d{d}"
 
         def timed(fn):
+            prewarm(fn)
             for _ in range(warmup):
                 fn()
             torch.cuda.synchronize()
@@ -277,6 +299,7 @@ def time_f16(fa, steps=10, warmup=2):
     dev = torch.device("cuda:0")
 
     def timed(fn):
+        prewarm(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -341,6 +364,7 @@ def time_fp8(fa, steps=10, warmup=3):
         def step():
             fa.fwd_fp8(q, k, v, ds, ds, ds, causal=True, scale=w.scale, out=o, lse=lse)
 
+        prewarm(step)
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
@@ -385,6 +409,7 @@ def time_varlen(fa, steps=10, warmup=2):
     f = sum(attention_flops(1, H, int(n), d, True) for n in lens)
 
     def timed(fn):
+        prewarm(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -487,6 +512,7 @@ def time_default_legs(fa):
         ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
         steps = 50 if cid == 2 else 20
         if cid != 256:
+            prewarm(lambda: fa.fwd(qq, kk, vv, causal=True, scale=ww.scale, out=oo, lse=ll))
             _, msk, mn, mx, _ = time_launches(fa, qq, kk, vv, oo, ll, True, ww.scale, steps, 3)
             f = attention_flops(ww.B, ww.H, ww.N, ww.d, True)
             leg = {"ms": round(msk, 4), "min_ms": round(mn, 4), "max_ms": round(mx, 4)}
@@ -800,6 +826,13 @@ def main():
         print(f"profile-run: 1 GiB copy + {args.steps} fa_fwd launches done", flush=True)
         return
 
+    # the device's clock under the forward, sampled over 1 s of back-to-back
+    # launches; it also brings the device to its steady state before the
+    # timed steps (see prewarm)
+    path = device_sysfs(torch)
+    clock = sustained_clock(fa, torch, path, q, k, v, o, lse, w.scale)
+    if path is None:
+        prewarm(lambda: fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse), 1000.0)
     ms_step, ms_kernel, ms_min, ms_max, wall = time_launches(
         fa, q, k, v, o, lse, True, w.scale, args.steps, args.warmup)
     flops = attention_flops(w.B, w.H, w.N, w.d, True)
@@ -808,9 +841,7 @@ def main():
     per_launch = time_launches.last_per_launch
     bq, bk, waves = fa.tile_config(w.d, fa.DTYPE_BF16)
     traffic = read_traffic()
-    path = device_sysfs(torch)
     props = torch.cuda.get_device_properties(0)
-    clock = sustained_clock(fa, torch, path, q, k, v, o, lse, w.scale)
     ceiling = mfma_ceiling(fa, torch, path)
     cold_ms = cold_cache(fa, torch, q, k, v, o, lse, w.scale)
     power_cap = read_hwmon(path, "power1_cap") if path else None
@@ -867,6 +898,7 @@ def main():
             qq, kk, vv = make_inputs(ww)
             oo = torch.empty_like(qq)
             ll = torch.empty((ww.B, ww.H, ww.N), dtype=torch.float32, device=qq.device)
+            prewarm(lambda: fa.fwd(qq, kk, vv, causal=True, scale=ww.scale, out=oo, lse=ll))
             ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, True, ww.scale, 20, 3)
             f = attention_flops(ww.B, ww.H, ww.N, ww.d, True)
             label = f"causal bf16 fwd B{ww.B} H{ww.H} N{ww.N} d{ww.d}"
@@ -887,6 +919,7 @@ def main():
         qq, kk, vv = make_inputs(w)
         oo = torch.empty_like(qq)
         ll = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=qq.device)
+        prewarm(lambda: fa.fwd(qq, kk, vv, causal=False, scale=w.scale, out=oo, lse=ll))
         ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, False, w.scale, 10, 2)
         f = attention_flops(w.B, w.H, w.N, w.d, False)
         extra["non-causal bf16 B8 H32 N8192 d128"] = {
@@ -900,6 +933,7 @@ def main():
             qq, kk, vv = make_inputs(hw)
             oo = torch.empty_like(qq)
             ll = torch.empty((hw.B, hw.H, hw.N), dtype=torch.float32, device=qq.device)
+            prewarm(lambda: fa.fwd(qq, kk, vv, causal=True, scale=hw.scale, out=oo, lse=ll))
             ms, msk, _, _, _ = time_launches(fa, qq, kk, vv, oo, ll, True, hw.scale, 10, 2)
             f = attention_flops(hw.B, hw.H, hw.N, hw.d, True)
             extra[f"causal bf16 fwd B8 H32 N8192 d{d}"] = {"ms": round(msk, 4),
