@@ -896,6 +896,9 @@ namespace duo {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned lds_u32;
 constexpr int kBufferWord3 = 0x00020000;
+// A lane source offset beyond every descriptor's range: the copy writes
+// zeros to LDS and reads nothing.
+constexpr unsigned kPadOffset = 0x40000000u;
 __device__ void raw_buffer_load_lds(i32x4 rsrc, lds_u32* lds, int size, int voffset, int soffset, int offset,
                                     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
@@ -982,12 +985,22 @@ struct Layout {
 // and its stores run: no workgroup launch and no cold prologue per item.
 // Only for fixed length with N a multiple of the 256-row block and every
 // XCD holding whole heads.
+// LDS row length of head dim D: d = 96 keeps the 256-byte rows (and
+// swizzles) of d = 128; its last four 16-byte chunks of each K and V row
+// are never read, and their copies are given an out-of-range source, so
+// they fetch nothing.
+template <int D>
+constexpr int lds_dim() {
+  return D == 96 ? 128 : D;
+}
+
 template <class T, int D, bool CAUSAL, int G = 1, bool PERSIST = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
                 T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
     int group, const int* __restrict__ cu_seqlens, int H, int total) {
-  using Ly = Layout<D, G>;
+  constexpr int LD = lds_dim<D>();
+  using Ly = Layout<LD, G>;
   constexpr int BQ = block_q<G>();
   static_assert(!PERSIST || G == 1, "persistent launches run one wave group");
   constexpr int DT = D / 16;
@@ -996,10 +1009,10 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   constexpr int NV = (kBK / 16) * DB;
   constexpr int NK = 2 * DT;
   constexpr int IPW = Ly::INSTR_PER_WAVE;
-  // 32 softmax slots per interval over its NK + NV MFMAs: one slot per
-  // MFMA at d = 128, two at d = 64.
-  constexpr int SPM = 16 / NK;
-  static_assert(NV == NK && NK * SPM == 16, "32 softmax slots per interval");
+  // 32 softmax slots per interval over its NK + NV MFMAs, 16 per product:
+  // MFMA F of a product carries slots 16F/NK .. 16(F+1)/NK - 1 (one per
+  // MFMA at d = 128, two at d = 64, one or two at d = 96).
+  static_assert(NV == NK && NK <= 16, "32 softmax slots per interval");
   static_assert(NK % IPW == 0 && NK / IPW >= 4, "DMA instructions spread over the MFMAs");
   __shared__ __attribute__((aligned(1024))) T smem[Ly::TOTAL];
 
@@ -1121,8 +1134,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * Ly::ROWS_PER_INSTR + dma_row;
-    dk_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ swz_k<D>(row)) * 16));
-    dv_lane[i] = (unsigned)(row * (D * 2) + ((dma_chunk ^ swz_v<D>(row)) * 16));
+    const int ck = dma_chunk ^ swz_k<LD>(row), cv = dma_chunk ^ swz_v<LD>(row);
+    dk_lane[i] = ck < D / 8 ? (unsigned)(row * (D * 2) + ck * 16) : kPadOffset;
+    dv_lane[i] = cv < D / 8 ? (unsigned)(row * (D * 2) + cv * 16) : kPadOffset;
   }
   auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
     if (PERSIST && more && t >= nkt) {  // the next item's tile t - nkt (same ring slot: nkt is a multiple of 4)
@@ -1136,7 +1150,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const uint64_t base = (uint64_t)(uintptr_t)(Xh + (size_t)kt0 * D);
     const i32x4 rs = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32), rows * D * 2, kBufferWord3};
     const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
-    raw_buffer_load_lds(rs, (lds_u32*)(smem + buf + r0 * D), 16, (int)(decltype(is_v)::value ? dv_lane[i] : dk_lane[i]),
+    raw_buffer_load_lds(rs, (lds_u32*)(smem + buf + r0 * LD), 16, (int)(decltype(is_v)::value ? dv_lane[i] : dk_lane[i]),
                         0, 0, 0);
   };
   // DMA of tile t into a ring slot given as an element offset (general
@@ -1158,14 +1172,14 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
   unsigned k_off[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * D + (((2 * t + half) ^ swz_k<D>(col)) * 8)) * 2u;
+  for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * LD + (((2 * t + half) ^ swz_k<LD>(col)) * 8)) * 2u;
   const int tr_e = (lane & 15) >> 2;
   const int tr_t = lane & 3;
   const int tr_cg = (lane >> 4) & 1;
   unsigned v_off[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b)
-    v_off[b] = (unsigned)((half * 4 + tr_e) * D + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ swz_v<D>(half * 4 + tr_e)) * 8) +
+    v_off[b] = (unsigned)((half * 4 + tr_e) * LD + (((4 * b + 2 * tr_cg + (tr_t >> 1)) ^ swz_v<LD>(half * 4 + tr_e)) * 8) +
                           (tr_t & 1) * 4) * 2u;
   // (plus the byte offset of the wave's tile within a slot)
   const unsigned smem_base = lds_addr(smem) + (unsigned)(grp * Ly::TILE * 2);
@@ -1202,9 +1216,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
       if constexpr (CT)
-        read_k<kb_slot(kb) * Ly::SLOT * 2 + (F % 2) * 32 * D * 2>(fr[F % kLead], k_abs[F / 2]);
+        read_k<kb_slot(kb) * Ly::SLOT * 2 + (F % 2) * 32 * LD * 2>(fr[F % kLead], k_abs[F / 2]);
       else
-        read_k<(F % 2) * 32 * D * 2>(fr[F % kLead], base + k_abs[F / 2]);
+        read_k<(F % 2) * 32 * LD * 2>(fr[F % kLead], base + k_abs[F / 2]);
     };
     static_for<kLead>(issue);
     static_for<NK>([&](auto fc) {
@@ -1218,10 +1232,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
         dst[F % 2] = mfma32(fr[F % kLead], qf[F / 2], dst[F % 2]);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) {
-        fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
-        if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
-      }
+      if constexpr (SM)
+        static_for<16 * (F + 1) / NK - 16 * F / NK>(
+            [&](auto sc_i) { fast_slot<T, S0 + 16 * F / NK + decltype(sc_i)::value>(fs, sc, c, m_run); });
       if constexpr (DMA && F % (NK / IPW) == (NK / IPW) - 1) dma_any(Vh, dma_b, dma_t, F / (NK / IPW), std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1243,9 +1256,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       constexpr int u = F / DB, b = F % DB;
       if constexpr (CT) {
         constexpr int o = kb_slot(vb) * Ly::SLOT * 2;
-        read_v<o + u * 16 * D * 2, o + (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], v_abs[b]);
+        read_v<o + u * 16 * LD * 2, o + (u * 16 + 8) * LD * 2>(lo[F % kLead], hi[F % kLead], v_abs[b]);
       } else {
-        read_v<u * 16 * D * 2, (u * 16 + 8) * D * 2>(lo[F % kLead], hi[F % kLead], base + v_abs[b]);
+        read_v<u * 16 * LD * 2, (u * 16 + 8) * LD * 2>(lo[F % kLead], hi[F % kLead], base + v_abs[b]);
       }
     };
     static_for<kLead>(issue);
@@ -1260,10 +1273,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       oacc[b] = mfma32(vf, pfrag[u], oacc[b]);
       __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
-      if constexpr (SM) {
-        fast_slot<T, S0 + SPM * F>(fs, sc, c, m_run);
-        if constexpr (SPM == 2) fast_slot<T, S0 + SPM * F + 1>(fs, sc, c, m_run);
-      }
+      if constexpr (SM)
+        static_for<16 * (F + 1) / NK - 16 * F / NK>(
+            [&](auto sc_i) { fast_slot<T, S0 + 16 * F / NK + decltype(sc_i)::value>(fs, sc, c, m_run); });
       if constexpr (DMA && F % (NV / IPW) == (NV / IPW) - 1) dma_any(Kh, dma_b, dma_t, F / (NV / IPW), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1476,10 +1488,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
 }  // namespace duo
 
-// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128 and 64
-// (two softmax slots per MFMA at d = 64), the
-// 4-wave kernel for d = 32, 96 and 256 (at d = 256 two waves per SIMD do
-// not fit the registers).
+// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128, 96 and
+// 64 (two softmax slots per MFMA at d = 64, one or two at d = 96), the
+// 4-wave kernel for d = 32 and 256 (at d = 256 two waves per SIMD do not
+// fit the registers) and for d = 96 on grids of fewer 256-row blocks than
+// CUs.
 // Grids of at most this many workgroups of 128 rows run with two wave
 // groups over the keys of each row block (G = 2; the duo kernel at d = 64,
 // the 4-wave one at d = 32 and 96): with few workgroups per CU there is no
@@ -1507,12 +1520,18 @@ inline int device_cus() {
 
 template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  constexpr bool kCanDuo = D == 128 || D == 64;
+  constexpr bool kCanDuo = D == 128 || D == 64 || D == 96;
   constexpr bool kCanSplit = D <= 96;
   const bool split = kCanSplit && (int64_t)p.BH * ((p.N + kBQ - 1) / kBQ) <= kSplitMaxBlocks;
   // d = 64 runs the duo kernel on every grid: one wave group per 256 rows
-  // on large grids, two groups over the key tiles of 128 rows on small ones
-  const bool duo_k = kCanDuo;
+  // on large grids, two groups over the key tiles of 128 rows on small ones.
+  // d = 96 (whose two groups' rings would not fit the LDS) runs one group
+  // of 256 rows unless that leaves CUs without a workgroup; then the 4-wave
+  // kernel's two-group form.  Causal bf16, same box: B2 H16 N4096 710 ->
+  // 1039 TFLOP/s, B1 H16 N4096 679 -> 707, but B1 H16 N2048 (128 blocks
+  // of 256 rows) 356 -> 334.
+  const bool duo_k =
+      kCanDuo && !(D == 96 && split && (int64_t)p.BH * ((p.N + duo::kBQ - 1) / duo::kBQ) < device_cus());
   const int duo_g = D == 64 && split ? 2 : 1;
   const int bq = duo_k ? (duo_g == 2 ? duo::block_q<2>() : duo::block_q<1>()) : kBQ;
   const int nqb = (p.N + bq - 1) / bq;
@@ -1539,7 +1558,12 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   int H = p.H, total = p.total;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
   const void* fn;
-  if constexpr (kCanDuo) {
+  if constexpr (D == 96) {
+    if (duo_k)
+      fn = persist ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 1, true> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
+    else
+      fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2>;
+  } else if constexpr (kCanDuo) {
     fn = persist ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 1, true> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
     if constexpr (D == 64) {
       if (duo_g == 2) fn = (const void*)duo::fwd_kernel<T, D, CAUSAL, 2>;
@@ -1599,7 +1623,7 @@ hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
 // Waves per workgroup as launched on large grids (d <= 96 runs 8 waves, in
 // two key groups, only on grids of at most kSplitMaxBlocks workgroups).
 TileConfig mfma_tile(int d) {
-  if (d == 128 || d == 64) return TileConfig{duo::kBQ, kBK, duo::kWaves};
+  if (d == 128 || d == 96 || d == 64) return TileConfig{duo::kBQ, kBK, duo::kWaves};
   if (d == 256) return TileConfig{kBQ, kBK, 2 * kWaves};  // two waves per 32 query rows
   return TileConfig{kBQ, kBK, kWaves};
 }
