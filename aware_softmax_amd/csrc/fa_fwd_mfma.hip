@@ -986,12 +986,12 @@ struct Layout {
 // Only for fixed length with N a multiple of the 256-row block and every
 // XCD holding whole heads.
 // LDS row length of head dim D: d = 96 keeps the 256-byte rows (and
-// swizzles) of d = 128; its last four 16-byte chunks of each K and V row
-// are never read, and their copies are given an out-of-range source, so
-// they fetch nothing.
+// swizzles) of d = 128, d = 32 the 128-byte rows of d = 64; the last
+// 16-byte chunks of each K and V row (four of them) are never read, and
+// their copies are given an out-of-range source, so they fetch nothing.
 template <int D>
 constexpr int lds_dim() {
-  return D == 96 ? 128 : D;
+  return D == 96 ? 128 : D == 32 ? 64 : D;
 }
 
 template <class T, int D, bool CAUSAL, int G = 1, bool PERSIST = false>
@@ -1011,9 +1011,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   constexpr int IPW = Ly::INSTR_PER_WAVE;
   // 32 softmax slots per interval over its NK + NV MFMAs, 16 per product:
   // MFMA F of a product carries slots 16F/NK .. 16(F+1)/NK - 1 (one per
-  // MFMA at d = 128, two at d = 64, one or two at d = 96).
+  // MFMA at d = 128, two at d = 64, one or two at d = 96, four at d = 32).
   static_assert(NV == NK && NK <= 16, "32 softmax slots per interval");
-  static_assert(NK % IPW == 0 && NK / IPW >= 4, "DMA instructions spread over the MFMAs");
+  static_assert(NK % IPW == 0 && NK / IPW >= 2, "DMA instructions spread over the MFMAs");
   __shared__ __attribute__((aligned(1024))) T smem[Ly::TOTAL];
 
   const int tid = threadIdx.x;
@@ -1488,21 +1488,22 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
 }  // namespace duo
 
-// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128, 96 and
-// 64 (two softmax slots per MFMA at d = 64, one or two at d = 96), the
-// 4-wave kernel for d = 32 and 256 (at d = 256 two waves per SIMD do not
-// fit the registers) and for d = 96 on grids of fewer 256-row blocks than
-// CUs.
+// Kernel per head dim: the two-waves-per-SIMD kernel for d = 128, 96, 64
+// and 32 (one softmax slot per MFMA at d = 128, one or two at d = 96, two
+// at d = 64, four at d = 32), the 4-wave kernel for d = 256 (two waves per
+// SIMD do not fit the registers) and for d = 96 on grids of fewer 256-row
+// blocks than CUs.
 // Grids of at most this many workgroups of 128 rows run with two wave
-// groups over the keys of each row block (G = 2; the duo kernel at d = 64,
-// the 4-wave one at d = 32 and 96): with few workgroups per CU there is no
+// groups over the keys of each row block (G = 2; the duo kernel at d = 64
+// and 32, the 4-wave one at d = 96): with few workgroups per CU there is no
 // later workgroup to balance the causal row blocks, and the run takes as
 // long as the longest block's chain of key tiles.  Measured with the 4-wave
 // kernel (causal bf16, same box): +22 % at B1 H16 N2048 d64 (256
 // workgroups), +47 % at B1 H16 N4096 d64, +6 % at B2 H16 N4096 d64 (1024),
 // -5 % at B4 H16 N2048 d64 (1024), -12 % at B2 H32 N8192 d64 (4096).  The
 // duo kernel with two groups, against the 4-wave one with two: B1 H16
-// N2048 d64 300 -> 412 TFLOP/s, B2 H16 N4096 d64 593 -> 768.
+// N2048 d64 300 -> 412 TFLOP/s, B2 H16 N4096 d64 593 -> 768; d32 B1 H16
+// N2048 190 -> 246, B2 H16 N4096 500 -> 505.
 constexpr int kSplitMaxBlocks = 1024;
 
 // Compute units of the current device (cached per device; 0 if unknown).
@@ -1520,11 +1521,12 @@ inline int device_cus() {
 
 template <class T, int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  constexpr bool kCanDuo = D == 128 || D == 64 || D == 96;
+  constexpr bool kCanDuo = D == 128 || D == 96 || D == 64 || D == 32;
   constexpr bool kCanSplit = D <= 96;
   const bool split = kCanSplit && (int64_t)p.BH * ((p.N + kBQ - 1) / kBQ) <= kSplitMaxBlocks;
-  // d = 64 runs the duo kernel on every grid: one wave group per 256 rows
-  // on large grids, two groups over the key tiles of 128 rows on small ones.
+  // d = 64 and 32 run the duo kernel on every grid: one wave group per 256
+  // rows on large grids, two groups over the key tiles of 128 rows on small
+  // ones.
   // d = 96 (whose two groups' rings would not fit the LDS) runs one group
   // of 256 rows unless that leaves CUs without a workgroup; then the 4-wave
   // kernel's two-group form.  Causal bf16, same box: B2 H16 N4096 710 ->
@@ -1532,7 +1534,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   // of 256 rows) 356 -> 334.
   const bool duo_k =
       kCanDuo && !(D == 96 && split && (int64_t)p.BH * ((p.N + duo::kBQ - 1) / duo::kBQ) < device_cus());
-  const int duo_g = D == 64 && split ? 2 : 1;
+  const int duo_g = (D == 64 || D == 32) && split ? 2 : 1;
   const int bq = duo_k ? (duo_g == 2 ? duo::block_q<2>() : duo::block_q<1>()) : kBQ;
   const int nqb = (p.N + bq - 1) / bq;
   const float c_signed = p.scale * 1.44269504088896340736f;
@@ -1565,12 +1567,10 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
       fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2>;
   } else if constexpr (kCanDuo) {
     fn = persist ? (const void*)duo::fwd_kernel<T, D, CAUSAL, 1, true> : (const void*)duo::fwd_kernel<T, D, CAUSAL>;
-    if constexpr (D == 64) {
+    if constexpr (D == 64 || D == 32) {
       if (duo_g == 2) fn = (const void*)duo::fwd_kernel<T, D, CAUSAL, 2>;
     }
-  } else if constexpr (kCanSplit) {
-    fn = split ? (const void*)fwd_mfma_kernel<T, D, CAUSAL, 2> : (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1>;
-  } else {
+  } else {  // d = 256
     fn = (const void*)fwd_mfma_kernel<T, D, CAUSAL, 1, kOS>;
   }
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
@@ -1623,7 +1623,7 @@ hipError_t launch_fwd_fp8(const FwdParams& p, hipStream_t stream) {
 // Waves per workgroup as launched on large grids (d <= 96 runs 8 waves, in
 // two key groups, only on grids of at most kSplitMaxBlocks workgroups).
 TileConfig mfma_tile(int d) {
-  if (d == 128 || d == 96 || d == 64) return TileConfig{duo::kBQ, kBK, duo::kWaves};
+  if (d == 128 || d == 96 || d == 64 || d == 32) return TileConfig{duo::kBQ, kBK, duo::kWaves};
   if (d == 256) return TileConfig{kBQ, kBK, 2 * kWaves};  // two waves per 32 query rows
   return TileConfig{kBQ, kBK, kWaves};
 }

@@ -64,12 +64,13 @@ def same_bits(a, b):
     return np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("where", ["q", "k", "v"])
 def test_nan_reaches_exactly_the_rows_that_see_it(fa, d, causal, where):
     # d = 96 on a grid above the two-group limit (2048 blocks of 128 rows),
-    # so that its two-waves-per-SIMD kernel (LDS rows padded to 128) runs
+    # so that its two-waves-per-SIMD kernel (LDS rows padded to 128) runs;
+    # the others on a small grid (two wave groups for d = 32 and 64)
     B, H, N = (8, 32, 1000) if d == 96 else (1, 2, 1000)
     row = 300  # inside the second 256-row block, not on a tile edge
     st = {t: synthetic.full_storage(7700 + d + causal, t, B, H, N, d, "bf16") for t in ("q", "k", "v")}

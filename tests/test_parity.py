@@ -233,18 +233,19 @@ def test_large_grid_single_group(fa, d, causal):
     assert_close(run_case(fa, cid, 8, 32, 1000, d, "bf16", causal, heads=heads), "bf16")
 
 
+@pytest.mark.parametrize("d", [32, 96])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_d96_large_grid_persistent(fa, dtype, causal):
-    """B4 H16 N4096 d96: 2048 blocks of 128 rows, above the two-group
-    limit, so d = 96 runs the two-waves-per-SIMD kernel, persistent (N a
-    multiple of its 256-row block), with 96-element rows in HBM and
-    128-element rows in LDS; 4 seeded heads, sampled rows plus every
+def test_padded_lds_rows_large_grid_persistent(fa, d, dtype, causal):
+    """B4 H16 N4096 at d = 32 and 96: 2048 blocks of 128 rows, above the
+    two-group limit, so the two-waves-per-SIMD kernel runs persistent (N a
+    multiple of its 256-row block) with LDS rows of 64 and 128 elements
+    (rows of 32 and 96 in HBM); 4 seeded heads, sampled rows plus every
     block edge."""
-    cid = 1760 + (dtype == "f16") * 2 + causal
+    cid = 1760 + (dtype == "f16") * 2 + causal + (d == 32) * 4
     rows = synthetic.sample_rows(cid, 4096, 384)
     heads = synthetic.sample_heads(cid, 4, 16, 4)
-    assert_close(run_case(fa, cid, 4, 16, 4096, 96, dtype, causal, heads=heads, rows=rows), dtype)
+    assert_close(run_case(fa, cid, 4, 16, 4096, d, dtype, causal, heads=heads, rows=rows), dtype)
 
 
 @pytest.mark.parametrize("n", [1, 5, 64, 100, 257])
@@ -539,11 +540,13 @@ def test_varlen_head_dims(fa, d):
     assert_close(varlen_case(fa, 1980 + d, [77, 300, 0, 129], 2, 2, d, "bf16", True), "bf16")
 
 
-def test_varlen_d96_large_grid(fa):
-    """Packed lengths 2048, 1000, 17, 513 at H24 Hkv8 d96 causal: 1536
-    blocks of 128 rows, above the two-group limit, so d = 96 runs the
-    two-waves-per-SIMD kernel over packed rows (grouped heads too)."""
-    assert_close(varlen_case(fa, 1985, [2048, 1000, 17, 513], 24, 8, 96, "bf16", True), "bf16")
+@pytest.mark.parametrize("d", [32, 96])
+def test_varlen_padded_lds_rows_large_grid(fa, d):
+    """Packed lengths 2048, 1000, 17, 513 at H24 Hkv8 causal, d = 32 and
+    96: 1536 blocks of 128 rows, above the two-group limit, so the
+    two-waves-per-SIMD kernel runs one group over packed rows (grouped
+    heads too)."""
+    assert_close(varlen_case(fa, 1985 + d, [2048, 1000, 17, 513], 24, 8, d, "bf16", True), "bf16")
 
 
 def test_varlen_f16(fa):
