@@ -360,28 +360,32 @@ def test_key_magnitude_ramp_d128(fa, causal):
     assert_close_sharp(run_case(fa, 0, 1, 2, n, d, "bf16", causal, tensors=st, stats=True), "bf16")
 
 
-# d = 64 on grids above the two-group split limit (1024 workgroups of 128
-# rows) runs the two-waves-per-SIMD kernel with its reference-max steady
-# loop; these cases force it with 144 heads.
+# d = 32, 64 and 96 on grids above the two-group split limit (1024
+# workgroups of 128 rows) run the two-waves-per-SIMD kernel's one-group
+# form with its reference-max steady loop; these cases force it with 144
+# heads.
 
 
+@pytest.mark.parametrize("d", [32, 64, 96])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("scale", [2.0, -1.5])
-def test_large_scores_d64_large_grid(fa, causal, scale):
-    """B2 H72 N1024 d64 (1152 workgroups): scores far beyond the first
-    tile's row max, so the reference max is raised mid-row; 3 seeded heads."""
-    cid = 4300 + int(scale * 10) + causal
+def test_large_scores_large_grid(fa, d, causal, scale):
+    """B2 H72 N1024 (1152 workgroups): scores far beyond the first tile's
+    row max, so the reference max is raised mid-row; 3 seeded heads."""
+    cid = 4300 + int(scale * 10) + causal + (d != 64) * 3 * d
     heads = synthetic.sample_heads(cid, 2, 72, 3)
-    assert_close_sharp(run_case(fa, cid, 2, 72, 1024, 64, "bf16", causal, scale=scale, heads=heads, stats=True),
+    assert_close_sharp(run_case(fa, cid, 2, 72, 1024, d, "bf16", causal, scale=scale, heads=heads, stats=True),
                        "bf16")
 
 
+@pytest.mark.parametrize("d", [32, 64, 96])
 @pytest.mark.parametrize("causal", [False, True])
-def test_key_magnitude_ramp_d64_large_grid(fa, causal):
-    """B2 H72 N1024 d64 with key j scaled by 1 + j/16 (every tile exceeds
-    all earlier ones); 3 seeded heads."""
-    B, H, n, d = 2, 72, 1024, 64
-    st = {t: synthetic.full_storage(4400 + causal, t, B, H, n, d, "bf16") for t in ("q", "k", "v")}
+def test_key_magnitude_ramp_large_grid(fa, d, causal):
+    """B2 H72 N1024 with key j scaled by 1 + j/16 (every tile exceeds all
+    earlier ones); 3 seeded heads."""
+    B, H, n = 2, 72, 1024
+    cid = 4400 + causal + (d != 64) * 3 * d
+    st = {t: synthetic.full_storage(cid, t, B, H, n, d, "bf16") for t in ("q", "k", "v")}
     kv = synthetic.bf16_bits_to_f32(st["k"]) * (1.0 + np.arange(n, dtype=np.float32) / 16.0)[None, None, :, None]
     st["k"] = synthetic.bf16_round_bits(kv)
     heads = synthetic.sample_heads(4400 + causal, B, H, 3)
