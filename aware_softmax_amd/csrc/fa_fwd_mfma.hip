@@ -957,19 +957,28 @@ __device__ __forceinline__ int swz_v(int r) {
 
 // A ring slot holds one key tile per wave group (G tiles of kBK rows, the
 // keys of one interval, contiguous in HBM and copied as one G kBK-row tile).
-template <int D, int G>
+// F8 (e4m3 inputs, d = 128): the K slots hold the tile's bytes (128-byte
+// rows: the d = 64 geometry and swizzle); V is copied as bytes into a
+// staging ring (128-byte rows, unswizzled) and widened to bf16 into the V
+// ring (the d = 128 geometry) by the whole workgroup in the interval
+// before its P.V.  Sizes in elements of the 16-bit type.
+template <int D, int G, bool F8 = false>
 struct Layout {
-  static constexpr int CPR = D / 8;
+  static constexpr int CPR = F8 ? D / 16 : D / 8;  // 16-byte chunks of a copied row
   static constexpr int TILE = kBK * D;  // one group's tile
   static constexpr int SLOT = G * TILE;
+  static constexpr int KSLOT = F8 ? SLOT / 2 : SLOT;
+  static constexpr int STSLOT = F8 ? SLOT / 2 : 0;
   static constexpr int K0 = 0;
-  static constexpr int V0 = kRingK * SLOT;
-  static constexpr int TOTAL = (kRingK + kRingV) * SLOT;
+  static constexpr int V0 = kRingK * KSLOT;
+  static constexpr int ST0 = V0 + kRingV * SLOT;
+  static constexpr int TOTAL = ST0 + kRingV * STSLOT;
   static constexpr int ROWS_PER_INSTR = 64 / CPR;
   static constexpr int INSTR_PER_TILE = G * kBK / ROWS_PER_INSTR;  // per slot
   static constexpr int INSTR_PER_WAVE = INSTR_PER_TILE / kWaves;
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
   static_assert(D == 64 || D == 128, "row swizzles exist for 128- and 256-byte rows");
+  static_assert(!F8 || (D == 128 && G == 1), "e4m3 inputs: d = 128, one wave group");
   static_assert(TOTAL * 2 <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
@@ -994,25 +1003,37 @@ constexpr int lds_dim() {
   return D == 96 ? 128 : D == 32 ? 64 : D;
 }
 
-template <class T, int D, bool CAUSAL, int G = 1, bool PERSIST = false>
+// F8: q, k, v hold e4m3 bytes (In = uint8_t), T = bf16 is the type of P,
+// of the widened V and of O; o_scale (the V factor) multiplies O.
+template <class T, int D, bool CAUSAL, int G = 1, bool PERSIST = false, bool F8 = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
-void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __restrict__ Vg,
-                T* __restrict__ Og, float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate,
-    int group, const int* __restrict__ cu_seqlens, int H, int total) {
+void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
+                const std::conditional_t<F8, uint8_t, T>* __restrict__ Kg,
+                const std::conditional_t<F8, uint8_t, T>* __restrict__ Vg, T* __restrict__ Og,
+                float* __restrict__ Lg, int BH, int N, int nqb, float c, int negate, int group,
+                const int* __restrict__ cu_seqlens, int H, int total, float o_scale) {
+  using In = std::conditional_t<F8, uint8_t, T>;
   constexpr int LD = lds_dim<D>();
-  using Ly = Layout<LD, G>;
+  using Ly = Layout<LD, G, F8>;
+  // Copied rows: bytes per row in HBM, and the row length (in elements of
+  // T) of the K tile in LDS, whose swizzle it takes.
+  constexpr int HROWB = F8 ? D : D * 2;
+  constexpr int KLD = F8 ? D / 2 : LD;
   constexpr int BQ = block_q<G>();
   static_assert(!PERSIST || G == 1, "persistent launches run one wave group");
   constexpr int DT = D / 16;
   constexpr int DB = D / 32;
   constexpr int CPR = Ly::CPR;
   constexpr int NV = (kBK / 16) * DB;
-  constexpr int NK = 2 * DT;
+  // Q.K MFMAs per interval: 16-wide d steps, or 64-wide with e4m3 inputs
+  constexpr int NK = F8 ? 2 * (D / 64) : 2 * DT;
   constexpr int IPW = Ly::INSTR_PER_WAVE;
   // 32 softmax slots per interval over its NK + NV MFMAs, 16 per product:
-  // MFMA F of a product carries slots 16F/NK .. 16(F+1)/NK - 1 (one per
-  // MFMA at d = 128, two at d = 64, one or two at d = 96, four at d = 32).
-  static_assert(NV == NK && NK <= 16, "32 softmax slots per interval");
+  // MFMA F of a product of NM MFMAs carries slots 16F/NM .. 16(F+1)/NM - 1
+  // (one per MFMA at d = 128, two at d = 64, one or two at d = 96, four at
+  // d = 32; with e4m3 inputs one per P.V and four per Q.K MFMA, each of
+  // which takes twice the time of a 16-bit one).
+  static_assert(NV <= 16 && NK <= 16, "32 softmax slots per interval");
   static_assert(NK % IPW == 0 && NK / IPW >= 2, "DMA instructions spread over the MFMAs");
   __shared__ __attribute__((aligned(1024))) T smem[Ly::TOTAL];
 
@@ -1052,9 +1073,24 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   // w + 4 the odd ones (group 1).
   const int grp = G == 2 ? (wave >> 2) : 0;
   const int q_rel = G == 2 ? (wave & 3) * 32 : (wave & 3) * 64 + (wave >> 2) * 32;
-  vec8<T> qf[DT];
-  auto load_q = [&](const T* Qh, int qi, int n) {
-    if (qi < n) {
+  vec8<T> qf[F8 ? 1 : DT];
+  // e4m3: lane (query, half) holds bytes 64 t + 32 half .. + 31 of its row
+  // (and K fragments the same bytes of a key row).
+  i32x8 qf8[F8 ? D / 64 : 1];
+  auto load_q = [&](const In* Qh, int qi, int n) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < D / 64; ++t) {
+        if (qi < n) {
+          const u32x4* src = (const u32x4*)(Qh + (size_t)qi * D + 64 * t + 32 * half);
+          const u32x4 lo = src[0], hi = src[1];
+          qf8[t] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2],
+                         (int)hi[3]};
+        } else {
+          qf8[t] = i32x8{};
+        }
+      }
+    } else if (qi < n) {
       const vec8<T>* src = (const vec8<T>*)(Qh + (size_t)qi * D + half * 8);
 #pragma unroll
       for (int t = 0; t < DT; ++t) qf[t] = src[2 * t];
@@ -1076,21 +1112,26 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     if (q0 >= N) return;  // past the end of this sequence (the whole workgroup)
   }
   const size_t head = hr.q;
-  const T* Qh = Qg + head;
-  const T* Kh = Kg + hr.kv;
-  const T* Vh = Vg + hr.kv;
+  const In* Qh = Qg + head;
+  const In* Kh = Kg + hr.kv;
+  const In* Vh = Vg + hr.kv;
   // the next item's K and V heads (persistent launches)
   const HeadRows hn = head_rows(nbh, BH, group, N, D, cu_seqlens, H, total);
-  const T* Kn = Kg + hn.kv;
-  const T* Vn = Vg + hn.kv;
+  const In* Kn = Kg + hn.kv;
+  const In* Vn = Vg + hn.kv;
   const int qw = q0 + q_rel;
   const int qi = qw + col;
   if (k_item == 0) load_q(Qh, qi, N);  // later items' Q blocks come with the previous item
   if (negate) {  // scale < 0: use -Q and |scale| (negation is exact)
+    if constexpr (F8) {
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      u32x4 u = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
-      qf[t] = __builtin_bit_cast(vec8<T>, u);
+      for (int t = 0; t < D / 64; ++t) qf8[t] ^= (int)0x80808080u;
+    } else {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        u32x4 u = __builtin_bit_cast(u32x4, qf[t]) ^ 0x80008000u;
+        qf[t] = __builtin_bit_cast(vec8<T>, u);
+      }
     }
   }
 
@@ -1134,11 +1175,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int row = (wave * IPW + i) * Ly::ROWS_PER_INSTR + dma_row;
-    const int ck = dma_chunk ^ swz_k<LD>(row), cv = dma_chunk ^ swz_v<LD>(row);
-    dk_lane[i] = ck < D / 8 ? (unsigned)(row * (D * 2) + ck * 16) : kPadOffset;
-    dv_lane[i] = cv < D / 8 ? (unsigned)(row * (D * 2) + cv * 16) : kPadOffset;
+    const int ck = dma_chunk ^ swz_k<KLD>(row), cv = F8 ? dma_chunk : dma_chunk ^ swz_v<LD>(row);
+    dk_lane[i] = ck < HROWB / 16 ? (unsigned)(row * HROWB + ck * 16) : kPadOffset;
+    dv_lane[i] = cv < HROWB / 16 ? (unsigned)(row * HROWB + cv * 16) : kPadOffset;
   }
-  auto dma_one = [&](const T* Xh, int buf, int t, int i, auto is_v) {
+  auto dma_one = [&](const In* Xh, int buf, int t, int i, auto is_v) {
     if (PERSIST && more && t >= nkt) {  // the next item's tile t - nkt (same ring slot: nkt is a multiple of 4)
       Xh = decltype(is_v)::value ? Vn : Kn;
       t -= nkt;
@@ -1148,31 +1189,47 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     const int kt0 = t * G * kBK;
     const int rows = min(N - kt0, G * kBK);
     const uint64_t base = (uint64_t)(uintptr_t)(Xh + (size_t)kt0 * D);
-    const i32x4 rs = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32), rows * D * 2, kBufferWord3};
+    const i32x4 rs = {(int)(uint32_t)base, (int)(uint32_t)(base >> 32), rows * HROWB, kBufferWord3};
     const int r0 = (wave * IPW + i) * Ly::ROWS_PER_INSTR;
-    raw_buffer_load_lds(rs, (lds_u32*)(smem + buf + r0 * LD), 16, (int)(decltype(is_v)::value ? dv_lane[i] : dk_lane[i]),
+    raw_buffer_load_lds(rs, (lds_u32*)(smem + buf + r0 * KLD), 16, (int)(decltype(is_v)::value ? dv_lane[i] : dk_lane[i]),
                         0, 0, 0);
   };
   // DMA of tile t into a ring slot given as an element offset (general
   // path) or as integral_constant<int, slot> of the K (is_v false) or V
   // ring.
-  auto dma_any = [&](const T* Xh, auto buf, int t, int i, auto is_v) {
+  auto dma_any = [&](const In* Xh, auto buf, int t, int i, auto is_v) {
     if constexpr (std::is_integral_v<decltype(buf)>) {
       dma_one(Xh, buf, t, i, is_v);
     } else {
-      constexpr int eoff = (decltype(is_v)::value ? Ly::V0 : Ly::K0) + kb_slot(buf) * Ly::SLOT;
+      constexpr int eoff = decltype(is_v)::value ? (F8 ? Ly::ST0 + kb_slot(buf) * Ly::STSLOT
+                                                       : Ly::V0 + kb_slot(buf) * Ly::SLOT)
+                                                 : Ly::K0 + kb_slot(buf) * Ly::KSLOT;
       dma_one(Xh, eoff, t, i, is_v);
     }
   };
-  auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::SLOT; };
+  auto kbuf = [](int t) { return Ly::K0 + (t % kRingK) * Ly::KSLOT; };
   auto vbuf = [](int t) { return Ly::V0 + (t % kRingV) * Ly::SLOT; };
+  // copy target of V tile t: the V ring, or the staging ring (F8)
+  auto vdst = [](int t) { return F8 ? Ly::ST0 + (t % kRingV) * Ly::STSLOT : Ly::V0 + (t % kRingV) * Ly::SLOT; };
+  // V tiles are copied kVLead intervals ahead (one more with the widening
+  // step in between).
+  constexpr int kVLead = F8 ? 2 : 1;
   auto iteration_barrier = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(2 * IPW) : "memory");
   };
 
-  unsigned k_off[DT];
+  // K fragment reads of row col: 16-bit, chunk 2t + half (16-wide d step
+  // t) at k_off[t]; e4m3, chunks 4t + 2 half and 4t + 2 half + 1 of the
+  // 128-byte row (64-wide d step t) at k_off[2t] and k_off[2t + 1].
+  constexpr int NKA = F8 ? 2 * (D / 64) : DT;
+  unsigned k_off[NKA];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) k_off[t] = (unsigned)(col * LD + (((2 * t + half) ^ swz_k<LD>(col)) * 8)) * 2u;
+  for (int t = 0; t < NKA; ++t) {
+    if constexpr (F8)
+      k_off[t] = (unsigned)(col * KLD * 2 + (((4 * (t >> 1) + 2 * half + (t & 1)) ^ swz_k<KLD>(col)) * 16));
+    else
+      k_off[t] = (unsigned)(col * LD + (((2 * t + half) ^ swz_k<LD>(col)) * 8)) * 2u;
+  }
   const int tr_e = (lane & 15) >> 2;
   const int tr_t = lane & 3;
   const int tr_cg = (lane >> 4) & 1;
@@ -1185,9 +1242,9 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   const unsigned smem_base = lds_addr(smem) + (unsigned)(grp * Ly::TILE * 2);
   // Absolute LDS addresses of buffer 0 of each ring; the buffer, the
   // 32-key half and the 16-key step then enter as instruction immediates.
-  unsigned k_abs[DT], v_abs[DB];
+  unsigned k_abs[NKA], v_abs[DB];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) k_abs[t] = smem_base + Ly::K0 * 2 + k_off[t];
+  for (int t = 0; t < NKA; ++t) k_abs[t] = smem_base + Ly::K0 * 2 + k_off[t];
 #pragma unroll
   for (int b = 0; b < DB; ++b) v_abs[b] = smem_base + Ly::V0 * 2 + v_off[b];
   auto buf_rel = [&](int elem_off) {
@@ -1212,11 +1269,49 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     constexpr bool CT = !std::is_integral_v<decltype(kb)>;
     unsigned base = 0;  // byte offset of the slot from slot 0
     if constexpr (!CT) base = buf_rel(kb - Ly::K0);
+    if constexpr (F8) {
+      // MFMA F: key half F % 2, 64-wide d step F / 2; two 16-byte reads
+      vec8<T> fl[kLead], fh[kLead];
+      auto issue = [&](auto fc) {
+        constexpr int F = decltype(fc)::value;
+        constexpr int o = (F % 2) * 32 * KLD * 2;
+        if constexpr (CT) {
+          constexpr int os = kb_slot(kb) * Ly::KSLOT * 2 + o;
+          read_k<os>(fl[F % kLead], k_abs[2 * (F / 2)]);
+          read_k<os>(fh[F % kLead], k_abs[2 * (F / 2) + 1]);
+        } else {
+          read_k<o>(fl[F % kLead], base + k_abs[2 * (F / 2)]);
+          read_k<o>(fh[F % kLead], base + k_abs[2 * (F / 2) + 1]);
+        }
+      };
+      static_for<kLead>(issue);
+      static_for<NK>([&](auto fc) {
+        constexpr int F = decltype(fc)::value;
+        constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(fl[F % kLead]), "+v"(fh[F % kLead]) : "i"(2 * (last - F)));
+        const u32x4 lo = __builtin_bit_cast(u32x4, fl[F % kLead]), hi = __builtin_bit_cast(u32x4, fh[F % kLead]);
+        const i32x8 kf{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        __builtin_amdgcn_s_setprio(2);
+        if constexpr (F < 2)
+          dst[F % 2] = mfma_f8(kf, qf8[F / 2], f32x16{});
+        else
+          dst[F % 2] = mfma_f8(kf, qf8[F / 2], dst[F % 2]);
+        __builtin_amdgcn_s_setprio(0);
+        if constexpr (F + kLead < NK) issue(std::integral_constant<int, F + kLead>{});
+        if constexpr (SM)
+          static_for<16 * (F + 1) / NK - 16 * F / NK>(
+              [&](auto sc_i) { fast_slot<T, S0 + 16 * F / NK + decltype(sc_i)::value>(fs, sc, c, m_run); });
+        if constexpr (DMA && F % (NK / IPW) == (NK / IPW) - 1)
+          dma_any(Vh, dma_b, dma_t, F / (NK / IPW), std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return;
+    }
     vec8<T> fr[kLead];
     auto issue = [&](auto fc) {
       constexpr int F = decltype(fc)::value;
       if constexpr (CT)
-        read_k<kb_slot(kb) * Ly::SLOT * 2 + (F % 2) * 32 * LD * 2>(fr[F % kLead], k_abs[F / 2]);
+        read_k<kb_slot(kb) * Ly::KSLOT * 2 + (F % 2) * 32 * LD * 2>(fr[F % kLead], k_abs[F / 2]);
       else
         read_k<(F % 2) * 32 * LD * 2>(fr[F % kLead], base + k_abs[F / 2]);
     };
@@ -1240,13 +1335,39 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     });
   };
 
+  // Widening of V tile t (F8): each thread takes 16 bytes, row tid / 8,
+  // d = 16 (tid % 8) .. + 15, from staging slot t % 4 and writes them as
+  // two 16-byte bf16 chunks into V slot t % 4 (exact: every e4m3 value is
+  // a bf16 value).  Read and write are split so that the read's latency
+  // can ride on MFMAs.
+  char* const sm = (char*)smem;
+  const int w_row = tid >> 3, w_c = tid & 7;
+  const unsigned w_src = Ly::ST0 * 2 + tid * 16;
+  const unsigned w_dst0 = Ly::V0 * 2 + w_row * LD * 2 + (((2 * w_c) ^ swz_v<LD>(w_row)) * 16);
+  const unsigned w_dst1 = Ly::V0 * 2 + w_row * LD * 2 + (((2 * w_c + 1) ^ swz_v<LD>(w_row)) * 16);
+  u32x4 w_in{};
+  auto widen_read = [&](int slot) { w_in = *(const u32x4*)(sm + w_src + slot * (Ly::STSLOT * 2)); };
+  auto widen_write = [&](int slot) {
+    unsigned w[8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      w[2 * x] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w_in[x], 1.f, false));
+      w[2 * x + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w_in[x], 1.f, true));
+    }
+    *(u32x4*)(sm + w_dst0 + slot * (Ly::SLOT * 2)) = u32x4{w[0], w[1], w[2], w[3]};
+    *(u32x4*)(sm + w_dst1 + slot * (Ly::SLOT * 2)) = u32x4{w[4], w[5], w[6], w[7]};
+  };
+
   // O^T += V^T P^T from V buffer vb.  With SM, slots S0..S0+15 of the fast
   // update of the scores sc ride along; with DMA, the K DMA of tile dma_t
-  // into buffer dma_b.
-  auto pv = [&](auto vb, auto with_sm, auto with_dma, int dma_t, auto dma_b, auto slot0, const f32x16(&sc)[2]) {
+  // into buffer dma_b; with widen = integral_constant<int, slot> (F8), the
+  // widening of the V tile of that ring slot.
+  auto pv = [&](auto vb, auto with_sm, auto with_dma, int dma_t, auto dma_b, auto slot0, const f32x16(&sc)[2],
+                auto widen) {
     constexpr bool SM = decltype(with_sm)::value;
     constexpr bool DMA = decltype(with_dma)::value;
     constexpr int S0 = decltype(slot0)::value;
+    constexpr bool WIDEN = !std::is_same_v<decltype(widen), std::false_type>;
     constexpr bool CT = !std::is_integral_v<decltype(vb)>;
     unsigned base = 0;
     if constexpr (!CT) base = buf_rel(vb - Ly::V0);
@@ -1274,8 +1395,10 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       __builtin_amdgcn_s_setprio(0);
       if constexpr (F + kLead < NV) issue(std::integral_constant<int, F + kLead>{});
       if constexpr (SM)
-        static_for<16 * (F + 1) / NK - 16 * F / NK>(
-            [&](auto sc_i) { fast_slot<T, S0 + 16 * F / NK + decltype(sc_i)::value>(fs, sc, c, m_run); });
+        static_for<16 * (F + 1) / NV - 16 * F / NV>(
+            [&](auto sc_i) { fast_slot<T, S0 + 16 * F / NV + decltype(sc_i)::value>(fs, sc, c, m_run); });
+      if constexpr (WIDEN && F == 1) widen_read(decltype(widen)::value);
+      if constexpr (WIDEN && F == NV / 2) widen_write(decltype(widen)::value);
       if constexpr (DMA && F % (NV / IPW) == (NV / IPW) - 1) dma_any(Kh, dma_b, dma_t, F / (NV / IPW), std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -1357,10 +1480,11 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
     constexpr int R = decltype(r_c)::value;
     f32x16(&cur)[2] = (R & 1) ? sb : sacc;
     f32x16(&nxt)[2] = (R & 1) ? sacc : sb;
+    using Widen = std::conditional_t<F8, std::integral_constant<int, R>, std::false_type>;
     pv(std::integral_constant<int, (R + 3) % 4>{}, On{}, On{}, j + 3, std::integral_constant<int, (R + 3) % 4>{},
-       S_lo{}, cur);
-    qk(std::integral_constant<int, (R + 1) % 4>{}, On{}, On{}, j + 1, std::integral_constant<int, (R + 1) % 4>{},
-       S_hi{}, cur, nxt);
+       S_lo{}, cur, Widen{});
+    qk(std::integral_constant<int, (R + 1) % 4>{}, On{}, On{}, j + kVLead,
+       std::integral_constant<int, (R + kVLead) % 4>{}, S_hi{}, cur, nxt);
     const bool ovf = fast_check();
     iteration_barrier();
     return ovf;
@@ -1370,13 +1494,17 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       dma_one(Kh, kbuf(j + 3), j + 3, i, Off{});
-      dma_one(Vh, vbuf(j + 1), j + 1, i, On{});
+      dma_one(Vh, vdst(j + kVLead), j + kVLead, i, On{});
     }
   };
   // Any interval (first, masked or last tiles; per-wave tile counts).
   auto general = [&](int j) {
     dma_all(j);
-    if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+    if constexpr (F8) {
+      widen_read(j % kRingV);
+      widen_write(j % kRingV);
+    }
+    if (j >= 1 && j - 1 < wave_nt) pv(vbuf(j - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc, Off{});
     if (j < wave_nt) masked_softmax(j);
     if (j + 1 < wave_nt) qk(kbuf(j + 1), Off{}, Off{}, 0, 0, S_lo{}, sacc, sacc);
     iteration_barrier();
@@ -1388,7 +1516,8 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
       dma_one(Kh, kbuf(0), 0, i, Off{});
       dma_one(Kh, kbuf(1), 1, i, Off{});
       dma_one(Kh, kbuf(2), 2, i, Off{});
-      dma_one(Vh, vbuf(0), 0, i, On{});
+      dma_one(Vh, vdst(0), 0, i, On{});
+      if constexpr (F8) dma_one(Vh, vdst(1), 1, i, On{});
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   }
@@ -1433,7 +1562,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
   for (; j < nkt; ++j) general(j);
   // every Q.K of the item is done: load the next item's Q block
   if (more) load_q(Qg + hn.q, nqbi * BQ + q_rel + col, N);
-  if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc);
+  if (nkt - 1 < wave_nt) pv(vbuf(nkt - 1), Off{}, Off{}, 0, 0, S_lo{}, sacc, Off{});
   if (!more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (G == 2) {
     // Merge the two groups' (m, l, O~) of the same rows through LDS (the
@@ -1467,7 +1596,7 @@ void fwd_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* __r
 
   const float l_tot = swap_halves(l_part, false);
   if (qi < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = F8 ? o_scale / l_tot : 1.f / l_tot;
     T* orow = Og + head + (size_t)qi * D + half * 4;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
@@ -1558,7 +1687,9 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   int group = p.group;
   const int* cu = p.cu_seqlens;
   int H = p.H, total = p.total;
-  void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate, &group, &cu, &H, &total};
+  float o_scale = 1.f;
+  void* args[] = {&q,     &k,          &v,     &o,     &lse, &bh, &n, (void*)&nqb, (void*)&c, (void*)&negate,
+                  &group, &cu,         &H,     &total, &o_scale};
   const void* fn;
   if constexpr (D == 96) {
     if (duo_k)
@@ -1597,6 +1728,32 @@ hipError_t launch_f8(const FwdParams& p, hipStream_t stream) {
   const float c_signed = p.scale * p.q_descale * p.k_descale * 1.44269504088896340736f;
   const int negate = c_signed < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
+  if constexpr (D == 128) {
+    // The two-waves-per-SIMD kernel (e4m3 Q.K, V widened in LDS) unless
+    // its 256-row blocks would leave CUs idle; persistent as in launch().
+    const int nqb2 = (p.N + duo::kBQ - 1) / duo::kBQ;
+    const int64_t items = (int64_t)p.BH * nqb2;
+    const int cus = device_cus();
+    if (!(split && items < cus)) {
+      const bool persist = p.N % duo::kBQ == 0 && items % kNumXcd == 0 && (items / kNumXcd) % nqb2 == 0 &&
+                           cus >= kNumXcd;
+      dim3 grid(p.BH * nqb2), block(duo::kThreads);
+      if (persist) grid = dim3((unsigned)(kNumXcd * std::min<int64_t>(cus / kNumXcd, items / kNumXcd)));
+      const uint8_t* q = (const uint8_t*)p.q;
+      const uint8_t* k = (const uint8_t*)p.k;
+      const uint8_t* v = (const uint8_t*)p.v;
+      __bf16* o = (__bf16*)p.o;
+      float* lse = p.lse;
+      int bh = p.BH, n = p.N, group = p.group, H = p.H, total = p.total;
+      const int* cu = nullptr;
+      float o_scale = p.v_descale;
+      void* args[] = {&q,     &k,  &v, &o,     &lse,     &bh, &n, (void*)&nqb2, (void*)&c, (void*)&negate,
+                      &group, &cu, &H, &total, &o_scale};
+      const void* fn = persist ? (const void*)duo::fwd_kernel<__bf16, D, CAUSAL, 1, true, true>
+                               : (const void*)duo::fwd_kernel<__bf16, D, CAUSAL, 1, false, true>;
+      return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    }
+  }
   dim3 grid(p.BH * nqb), block(split ? 2 * kThreads : kThreads);
   const uint8_t* q = (const uint8_t*)p.q;
   const uint8_t* k = (const uint8_t*)p.k;
