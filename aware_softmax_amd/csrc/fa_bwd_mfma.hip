@@ -435,7 +435,12 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   const int it0 = CAUSAL ? kb0 / kBQ : 0;
   const int span = nqt - it0;
   const int total = hc * span;
-  auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane(v % RING); };
+  // Tile v goes to ring buffer (v + ring_off) mod RING, the offset chosen
+  // so that the first head's first unmasked tile lands in buffer 0 (the
+  // unrolled loop below starts there).
+  const int it_s0 = CAUSAL ? min(it0 + 2, nqt) : 0;
+  const int ring_off = (RING - (it_s0 - it0) % RING) % RING;
+  auto ring = [&](int v) { return __builtin_amdgcn_readfirstlane((v + ring_off) % RING); };
   using QDma = RowTileDma<D, kBQ>;
   const QDma qdma(wave, lane);
   constexpr int kDmaPerWave = 1 + 2 * QDma::IPW;  // statistics, Q, dO
@@ -495,6 +500,27 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
       }
   }
   const unsigned sbase = lds_addr(smem);
+  // Absolute LDS addresses in ring buffer 0 (Q and dO): the row fragments
+  // of 16-wide d step t, the transposing reads, the statistics.  The ring
+  // buffer (when known at compile time), the query block and the 16-query
+  // step then enter as instruction immediates.  At d = 256 (no registers
+  // to spare) the addresses are formed per read and the ring buffer stays
+  // a run-time value.
+  constexpr bool kAbs = D <= 128;
+  unsigned rq[kAbs ? DT : 1], rdo[kAbs ? DT : 1], tq[DBO][2], tdo[DBO][2];
+#pragma unroll
+  for (int t = 0; t < (kAbs ? DT : 0); ++t) {
+    rq[t] = sbase + Ly::OFF_Q + (rf_lane[0] ^ (unsigned)(t << 5));
+    rdo[t] = sbase + Ly::OFF_DO + (rf_lane[0] ^ (unsigned)(t << 5));
+  }
+#pragma unroll
+  for (int b = 0; b < DBO; ++b)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      tq[b][hi] = sbase + Ly::OFF_Q + trq[b][hi];
+      tdo[b][hi] = sbase + Ly::OFF_DO + trq[b][hi];
+    }
+  const unsigned ast0 = sbase + Ly::OFF_ST + 16 * half;
 
   f32x16 dkT[DBO], dvT[DBO];
 #pragma unroll
@@ -534,33 +560,52 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
 
   // One tile: phase A, then phase B with the VALU groups of step u + 1
   // riding on the MFMAs of step u (groups 0 and 1 run before step 0).
-  auto iteration = [&](int v, int it, auto mask_c) {
-    const int b = ring(v);
+  // bc: the ring buffer of tile v, as an int or as integral_constant (then
+  // every buffer offset is an instruction immediate).
+  auto iteration = [&](int v, int it, auto mask_c, auto bc) {
+    constexpr bool CT = !std::is_integral_v<decltype(bc)>;
+    int b;
+    if constexpr (CT)
+      b = decltype(bc)::value;
+    else
+      b = bc;
     // The copies of tile v + PF ride on phase A's MFMAs, one every
     // kDmaStride.  Past the last tile they repeat it into the buffer of tile
     // v - 1 (already consumed, never read again): no branch in the MFMA
     // stream, and the waits below count the same instructions.
     const TileDesc nt = tile_desc(min(v + PF, total - 1));
-    const int nb = ring(v + PF);
+    const int nb = CT ? (b + PF) % RING : ring(v + PF);
     constexpr int kDmaStride = PF == 1 ? 1 : NA / kDmaPerWave;  // one tile ahead: copy early
-    const unsigned aq = sbase + Ly::OFF_Q + b * Ly::QTILE;
-    const unsigned ado = sbase + Ly::OFF_DO + b * Ly::QTILE;
+    // buffer offsets: immediates (BQ, BS) or run-time additions (bq, bs)
+    constexpr int BQ = [] {
+      if constexpr (CT) return decltype(bc)::value * Ly::QTILE;
+      else return 0;
+    }();
+    constexpr int BS = [] {
+      if constexpr (CT) return decltype(bc)::value * Ly::STTILE;
+      else return 0;
+    }();
+    const unsigned bq = CT ? 0u : (unsigned)(b * Ly::QTILE);
     {
-      const unsigned ast = sbase + Ly::OFF_ST + b * Ly::STTILE + 16 * half;
+      const unsigned ast = ast0 + (CT ? 0u : (unsigned)(b * Ly::STTILE));
       // initial accumulators: register 4 g + e of query block qb holds query
       // 32 qb + 8 g + 4 half + e
       f32x4 init[2][2][4];  // [S or dP][qb][g]
       static_for<8>([&](auto kc) {
         constexpr int k = decltype(kc)::value, qb = k / 4, g = k % 4;
-        ds_b128f<(32 * qb + 8 * g) * 4>(init[0][qb][g], ast);
-        ds_b128f<(kBQ + 32 * qb + 8 * g) * 4>(init[1][qb][g], ast);
+        ds_b128f<BS + (32 * qb + 8 * g) * 4>(init[0][qb][g], ast);
+        ds_b128f<BS + (kBQ + 32 * qb + 8 * g) * 4>(init[1][qb][g], ast);
       });
       vec8<T> fa[LA];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, qb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
-        ds_b128<0>(fa[F % LA], (X ? ado : aq) + (rf_lane[qb] ^ (unsigned)(t << 5)));
+        if constexpr (kAbs)
+          ds_b128<BQ + qb * 32 * ROWB>(fa[F % LA], (X ? rdo[t] : rq[t]) + bq);
+        else
+          ds_b128<0>(fa[F % LA], sbase + (X ? Ly::OFF_DO : Ly::OFF_Q) + (unsigned)(b * Ly::QTILE) +
+                                     (rf_lane[qb] ^ (unsigned)(t << 5)));
       };
-      static_for<LA>(issue);
+      static_for<(LA < NA ? LA : NA)>(issue);
       asm volatile("s_waitcnt lgkmcnt(%16)"
                    : "+v"(init[0][0][0]), "+v"(init[0][0][1]), "+v"(init[0][0][2]), "+v"(init[0][0][3]),
                      "+v"(init[0][1][0]), "+v"(init[0][1][1]), "+v"(init[0][1][2]), "+v"(init[0][1][3]),
@@ -598,11 +643,10 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
       s16x4 lo_[LB], hi_[LB];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, u = F / (2 * DBO), bb = (F / 2) % DBO, X = F % 2;
-        const unsigned a = X ? aq : ado;
-        ds_tr64<u * 16 * ROWB>(lo_[F % LB], a + trq[bb][0]);
-        ds_tr64<u * 16 * ROWB>(hi_[F % LB], a + trq[bb][1]);
+        ds_tr64<BQ + u * 16 * ROWB>(lo_[F % LB], (X ? tq[bb][0] : tdo[bb][0]) + bq);
+        ds_tr64<BQ + u * 16 * ROWB>(hi_[F % LB], (X ? tq[bb][1] : tdo[bb][1]) + bq);
       };
-      static_for<LB>(issue);
+      static_for<(LB < NB ? LB : NB)>(issue);
       static_for<NB>([&](auto fc) {
         constexpr int F = decltype(fc)::value, u = F / (2 * DBO), bb = (F / 2) % DBO, X = F % 2;
         constexpr int last = (F + LB - 1 < NB - 1) ? F + LB - 1 : NB - 1;
@@ -636,7 +680,7 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
 
   // Tiles [it0, it_s) and [it_e, nqt) may hide scores (the causal diagonal,
   // the ragged end); tiles in between need no mask for any wave.
-  const int it_s = CAUSAL ? min(it0 + 2, nqt) : 0;
+  const int it_s = it_s0;
   int it_e = kb0 + kBKV <= N ? N / kBQ : 0;
   it_e = max(it_e, it_s);
 
@@ -650,9 +694,18 @@ void bwd_dkdv_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T
   for (int rr = 0; rr < hc; ++rr) {
     int v = rr * span;
     int it = it0;
-    for (; it < it_s; ++it, ++v) iteration(v, it, std::true_type{});
-    for (; it < it_e; ++it, ++v) iteration(v, it, std::false_type{});
-    for (; it < nqt; ++it, ++v) iteration(v, it, std::true_type{});
+    for (; it < it_s; ++it, ++v) iteration(v, it, std::true_type{}, ring(v));
+    // Unmasked tiles: up to buffer 0 with the buffer a run-time value, then
+    // the loop unrolled by the ring period (the buffers compile-time), then
+    // the rest.
+    for (; kAbs && it < it_e && ring(v) != 0; ++it, ++v) iteration(v, it, std::false_type{}, ring(v));
+    for (; kAbs && it + RING <= it_e; it += RING, v += RING) {
+      iteration(v, it, std::false_type{}, ic<0>{});
+      iteration(v + 1, it + 1, std::false_type{}, ic<1>{});
+      if constexpr (RING > 2) iteration(v + 2, it + 2, std::false_type{}, ic<(RING > 2 ? 2 : 0)>{});
+    }
+    for (; it < it_e; ++it, ++v) iteration(v, it, std::false_type{}, ring(v));
+    for (; it < nqt; ++it, ++v) iteration(v, it, std::true_type{}, ring(v));
   }
 
   mfma_drain();
@@ -851,6 +904,22 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
       }
   }
   const unsigned sbase = lds_addr(smem);
+  // Absolute LDS addresses in ring buffer 0: K and V row fragments of
+  // 16-wide d step t, the K^T transposing reads; the ring buffer (when
+  // known at compile time) and the 16-key step enter as immediates.  (At
+  // d = 256, one wave per SIMD, the 32 row-fragment addresses would not fit
+  // beside the Q, dO and dQ registers: they are formed per read.)
+  constexpr bool kAbs = D <= 128;
+  unsigned rk[kAbs ? DT : 1], rv[kAbs ? DT : 1], tk[DB][2];
+#pragma unroll
+  for (int t = 0; t < (kAbs ? DT : 0); ++t) {
+    rk[t] = sbase + Ly::OFF_K + (rf_lane[0] ^ (unsigned)(t << 5));
+    rv[t] = sbase + Ly::OFF_V + (rf_lane[0] ^ (unsigned)(t << 5));
+  }
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) tk[b][hi] = sbase + Ly::OFF_K + trk[b][hi];
 
   f32x16 dqT[DB];
 #pragma unroll
@@ -881,16 +950,26 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
     dw[kb][2 * g + 1] = pack2<T>(ds[2], ds[3]);
   };
 
-  auto iteration = [&](int j, auto mask_c) {
-    const int b = ring(j);
+  // bc: the ring buffer of tile j, as an int or as integral_constant (then
+  // every buffer offset is an instruction immediate).
+  auto iteration = [&](int j, auto mask_c, auto bc) {
+    constexpr bool CT = !std::is_integral_v<decltype(bc)>;
+    int b;
+    if constexpr (CT)
+      b = decltype(bc)::value;
+    else
+      b = bc;
     // The copies of tile j + 2 ride on phase A's MFMAs, one every
     // kDmaStride; past the last tile they repeat it into the buffer of tile
     // j - 1 (consumed, never read again).
     const int jn = min(j + 2, nkt - 1);
-    const int nb = ring(j + 2);
+    const int nb = CT ? (b + 2) % kRing : ring(j + 2);
     constexpr int kDmaStride = NA / kDmaPerWave;
-    const unsigned ak = sbase + Ly::OFF_K + b * Ly::KTILE;
-    const unsigned av = sbase + Ly::OFF_V + b * Ly::KTILE;
+    constexpr int BK = [] {
+      if constexpr (CT) return decltype(bc)::value * Ly::KTILE;
+      else return 0;
+    }();
+    const unsigned bk = CT ? 0u : (unsigned)(b * Ly::KTILE);
     {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -902,9 +981,13 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
       vec8<T> fa[LA];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, kb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
-        ds_b128<0>(fa[F % LA], (X ? av : ak) + (rf_lane[kb] ^ (unsigned)(t << 5)));
+        if constexpr (kAbs)
+          ds_b128<BK + kb * 32 * ROWB>(fa[F % LA], (X ? rv[t] : rk[t]) + bk);
+        else
+          ds_b128<0>(fa[F % LA], sbase + (X ? Ly::OFF_V : Ly::OFF_K) + (unsigned)(b * Ly::KTILE) +
+                                     (rf_lane[kb] ^ (unsigned)(t << 5)));
       };
-      static_for<LA>(issue);
+      static_for<(LA < NA ? LA : NA)>(issue);
       static_for<NA>([&](auto fc) {
         constexpr int F = decltype(fc)::value, kb = F / (2 * DT), t = (F / 2) % DT, X = F % 2;
         constexpr int last = (F + LA - 1 < NA - 1) ? F + LA - 1 : NA - 1;
@@ -925,10 +1008,10 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
       s16x4 lo_[LC], hi_[LC];
       auto issue = [&](auto fc) {
         constexpr int F = decltype(fc)::value, u = F / DB, bb = F % DB;
-        ds_tr64<u * 16 * ROWB>(lo_[F % LC], ak + trk[bb][0]);
-        ds_tr64<u * 16 * ROWB>(hi_[F % LC], ak + trk[bb][1]);
+        ds_tr64<BK + u * 16 * ROWB>(lo_[F % LC], tk[bb][0] + bk);
+        ds_tr64<BK + u * 16 * ROWB>(hi_[F % LC], tk[bb][1] + bk);
       };
-      static_for<LC>(issue);
+      static_for<(LC < NC ? LC : NC)>(issue);
       static_for<NC>([&](auto fc) {
         constexpr int F = decltype(fc)::value, u = F / DB, bb = F % DB;
         constexpr int last = (F + LC - 1 < NC - 1) ? F + LC - 1 : NC - 1;
@@ -969,9 +1052,16 @@ void bwd_dq_kernel(const T* __restrict__ Qg, const T* __restrict__ Kg, const T* 
   } else {
     dma_barrier<0>();
   }
+  // Unmasked tiles in a loop unrolled by the ring period (tile 0 is in
+  // buffer 0, so the buffers are compile-time there), then the rest.
   int j = 0;
-  for (; j < j_e; ++j) iteration(j, std::false_type{});
-  for (; j < nkt; ++j) iteration(j, std::true_type{});
+  for (; kAbs && j + kRing <= j_e; j += kRing) {
+    iteration(j, std::false_type{}, ic<0>{});
+    iteration(j + 1, std::false_type{}, ic<1>{});
+    iteration(j + 2, std::false_type{}, ic<2>{});
+  }
+  for (; j < j_e; ++j) iteration(j, std::false_type{}, ring(j));
+  for (; j < nkt; ++j) iteration(j, std::true_type{}, ring(j));
 
   // ---- dQ = scale * (dQ^T)^T: lane writes query qi, d = 32 b + 8 g + 4 half + {0..3}.
   if (qi < N) {

@@ -1284,7 +1284,7 @@ void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
           read_k<o>(fh[F % kLead], base + k_abs[2 * (F / 2) + 1]);
         }
       };
-      static_for<kLead>(issue);
+      static_for<(kLead < NK ? kLead : NK)>(issue);
       static_for<NK>([&](auto fc) {
         constexpr int F = decltype(fc)::value;
         constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
@@ -1315,7 +1315,7 @@ void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
       else
         read_k<(F % 2) * 32 * LD * 2>(fr[F % kLead], base + k_abs[F / 2]);
     };
-    static_for<kLead>(issue);
+    static_for<(kLead < NK ? kLead : NK)>(issue);
     static_for<NK>([&](auto fc) {
       constexpr int F = decltype(fc)::value;
       constexpr int last = (F + kLead - 1 < NK - 1) ? F + kLead - 1 : NK - 1;
@@ -1382,7 +1382,7 @@ void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
         read_v<u * 16 * LD * 2, (u * 16 + 8) * LD * 2>(lo[F % kLead], hi[F % kLead], base + v_abs[b]);
       }
     };
-    static_for<kLead>(issue);
+    static_for<(kLead < NV ? kLead : NV)>(issue);
     static_for<NV>([&](auto fc) {
       constexpr int F = decltype(fc)::value;
       constexpr int u = F / DB, b = F % DB;

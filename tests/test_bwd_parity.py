@@ -166,6 +166,25 @@ def test_bwd_head_dims_long(fa, d):
     run_bwd(fa, 9100 + d, 2, 4, 2048, d, True, heads=synthetic.sample_heads(9100 + d, 2, 4, 3))
 
 
+def test_bwd_d32_large_grid_repeatable(fa):
+    """B2 H16 N4096 d32 causal (1024 dQ workgroups, three per CU): 2 seeded
+    heads against the oracle, and three runs bitwise equal.  The dQ kernel
+    once issued more transposing LDS reads than its d = 32 loop consumed;
+    their unused destination registers, still being written by the reads
+    in flight, could be handed to live values, which corrupted dQ from run
+    to run on this grid only."""
+    import torch
+
+    dq, dk, dv = run_bwd(fa, 9150, 2, 16, 4096, 32, True, heads=synthetic.sample_heads(9150, 2, 16, 2))
+    st = {t: synthetic.full_storage(9150, t, 2, 16, 4096, 32, "bf16") for t in ("q", "k", "v", "do")}
+    q, k, v, do = (to_device(st[t]) for t in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    for _ in range(3):
+        dq2, dk2, dv2 = fa.bwd(q, k, v, o, lse, do, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dq2, dq) and torch.equal(dk2, dk) and torch.equal(dv2, dv)
+
+
 def test_bwd_d256_sampled_heads(fa):
     """B2 H8 N4096 d256 causal: 2 seeded heads, every row of dQ, dK, dV."""
     run_bwd(fa, 9400, 2, 8, 4096, 256, True, heads=synthetic.sample_heads(9400, 2, 8, 2))
