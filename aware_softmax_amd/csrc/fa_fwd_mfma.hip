@@ -957,18 +957,20 @@ __device__ __forceinline__ int swz_v(int r) {
 
 // A ring slot holds one key tile per wave group (G tiles of kBK rows, the
 // keys of one interval, contiguous in HBM and copied as one G kBK-row tile).
-// F8 (e4m3 inputs, d = 128): the K slots hold the tile's bytes (128-byte
-// rows: the d = 64 geometry and swizzle); V is copied as bytes into a
-// staging ring (128-byte rows, unswizzled) and widened to bf16 into the V
-// ring (the d = 128 geometry) by the whole workgroup in the interval
-// before its P.V.  Sizes in elements of the 16-bit type.
+// F8 (e4m3 inputs, d = 64 or 128): the K slots hold the tile's bytes in
+// 128-byte rows (the bf16 d = 64 geometry and swizzle; at d = 64 the last
+// four chunks of a row are never read and their copies fetch nothing); V
+// is copied as bytes into a staging ring of 128-byte rows (unswizzled) and
+// widened to bf16 into the V ring (the bf16 geometry of d) by the
+// workgroup in the interval before its P.V.  Sizes in elements of the
+// 16-bit type.
 template <int D, int G, bool F8 = false>
 struct Layout {
-  static constexpr int CPR = F8 ? D / 16 : D / 8;  // 16-byte chunks of a copied row
+  static constexpr int CPR = F8 ? 8 : D / 8;  // 16-byte chunks of a copied row
   static constexpr int TILE = kBK * D;  // one group's tile
   static constexpr int SLOT = G * TILE;
-  static constexpr int KSLOT = F8 ? SLOT / 2 : SLOT;
-  static constexpr int STSLOT = F8 ? SLOT / 2 : 0;
+  static constexpr int KSLOT = F8 ? kBK * 64 : SLOT;
+  static constexpr int STSLOT = F8 ? kBK * 64 : 0;
   static constexpr int K0 = 0;
   static constexpr int V0 = kRingK * KSLOT;
   static constexpr int ST0 = V0 + kRingV * SLOT;
@@ -978,7 +980,7 @@ struct Layout {
   static constexpr int INSTR_PER_WAVE = INSTR_PER_TILE / kWaves;
   static_assert(INSTR_PER_TILE % kWaves == 0, "DMA instructions split evenly over waves");
   static_assert(D == 64 || D == 128, "row swizzles exist for 128- and 256-byte rows");
-  static_assert(!F8 || (D == 128 && G == 1), "e4m3 inputs: d = 128, one wave group");
+  static_assert(!F8 || ((D == 64 || D == 128) && G == 1), "e4m3 inputs: d = 64 or 128, one wave group");
   static_assert(TOTAL * 2 <= 160 * 1024, "fits the 160 KiB LDS");
 };
 
@@ -1018,7 +1020,7 @@ void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
   // Copied rows: bytes per row in HBM, and the row length (in elements of
   // T) of the K tile in LDS, whose swizzle it takes.
   constexpr int HROWB = F8 ? D : D * 2;
-  constexpr int KLD = F8 ? D / 2 : LD;
+  constexpr int KLD = F8 ? 64 : LD;
   constexpr int BQ = block_q<G>();
   static_assert(!PERSIST || G == 1, "persistent launches run one wave group");
   constexpr int DT = D / 16;
@@ -1340,14 +1342,21 @@ void fwd_kernel(const std::conditional_t<F8, uint8_t, T>* __restrict__ Qg,
   // two 16-byte bf16 chunks into V slot t % 4 (exact: every e4m3 value is
   // a bf16 value).  Read and write are split so that the read's latency
   // can ride on MFMAs.
+  // (At d = 64 a tile is 4 KiB: threads 0..255, waves 0-3, do it.)
   char* const sm = (char*)smem;
-  const int w_row = tid >> 3, w_c = tid & 7;
-  const unsigned w_src = Ly::ST0 * 2 + tid * 16;
+  constexpr int WCPR = D / 16;  // 16-byte chunks of an e4m3 row
+  constexpr bool kWideAll = kBK * WCPR == kThreads;
+  const bool w_on = kWideAll || tid < kBK * WCPR;
+  const int w_row = tid / WCPR, w_c = tid % WCPR;
+  const unsigned w_src = Ly::ST0 * 2 + w_row * 128 + w_c * 16;
   const unsigned w_dst0 = Ly::V0 * 2 + w_row * LD * 2 + (((2 * w_c) ^ swz_v<LD>(w_row)) * 16);
   const unsigned w_dst1 = Ly::V0 * 2 + w_row * LD * 2 + (((2 * w_c + 1) ^ swz_v<LD>(w_row)) * 16);
   u32x4 w_in{};
-  auto widen_read = [&](int slot) { w_in = *(const u32x4*)(sm + w_src + slot * (Ly::STSLOT * 2)); };
+  auto widen_read = [&](int slot) {
+    if (w_on) w_in = *(const u32x4*)(sm + w_src + slot * (Ly::STSLOT * 2));
+  };
   auto widen_write = [&](int slot) {
+    if (!w_on) return;
     unsigned w[8];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -1728,7 +1737,7 @@ hipError_t launch_f8(const FwdParams& p, hipStream_t stream) {
   const float c_signed = p.scale * p.q_descale * p.k_descale * 1.44269504088896340736f;
   const int negate = c_signed < 0.f ? 1 : 0;
   const float c = negate ? -c_signed : c_signed;
-  if constexpr (D == 128) {
+  if constexpr (D == 128 || D == 64) {
     // The two-waves-per-SIMD kernel (e4m3 Q.K, V widened in LDS) unless
     // its 256-row blocks would leave CUs idle; persistent as in launch().
     const int nqb2 = (p.N + duo::kBQ - 1) / duo::kBQ;

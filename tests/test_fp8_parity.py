@@ -81,19 +81,21 @@ def test_fp8_throughput_shape_sampled(fa):
     run_case(fa, 9800, 8, 32, 32, 8192, 128, True, heads=synthetic.sample_heads(9800, 8, 32, 3), rows=rows)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("variant", ["plain", "grouped", "negative_scale", "zero_scale", "descales"])
-def test_fp8_two_waves_per_simd(fa, causal, variant):
-    """B4 H16 N4096 d128 (1024 blocks of 256 rows): the two-waves-per-SIMD
+def test_fp8_two_waves_per_simd(fa, d, causal, variant):
+    """B4 H16 N4096 (1024 blocks of 256 rows): the two-waves-per-SIMD
     kernel, persistent, with e4m3 Q.K and V widened to bf16 in LDS; 3
     seeded heads x 256 rows plus edge rows, with grouped key/value heads
     (Hkv 4), scales -0.2 and 0, or distinct factors per tensor."""
     cid = 9760 + causal + 2 * ["plain", "grouped", "negative_scale", "zero_scale", "descales"].index(variant)
+    cid += 20 * (d == 64)
     hkv = 4 if variant == "grouped" else 16
     scale = {"negative_scale": -0.2, "zero_scale": 0.0}.get(variant)
     descales = (1 / 16, 1 / 64, 1 / 8) if variant == "descales" else (DS, DS, DS)
     rows = synthetic.sample_rows(cid, 4096, 256)
-    run_case(fa, cid, 4, 16, hkv, 4096, 128, causal, scale=scale, heads=synthetic.sample_heads(cid, 4, 16, 3),
+    run_case(fa, cid, 4, 16, hkv, 4096, d, causal, scale=scale, heads=synthetic.sample_heads(cid, 4, 16, 3),
              rows=rows, descales=descales)
 
 
