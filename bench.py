@@ -44,6 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 256 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "aware_softmax_amd", "csrc", "fa_fwd_mfma.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_B8H32N8192d128_counters.txt")
@@ -282,6 +283,47 @@ def time_gqa(fa, steps=10, warmup=2):
                                       workspace=ws))
             out[f"{label} bwd"] = {"ms": round(ms, 4), "TFLOP/s": round(2.5 * f / (ms * 1e-3) / 1e12, 2)}
         del q, k, v, do, o, lse
+        torch.cuda.empty_cache()
+    return out
+
+
+def time_f32(fa, steps=10, warmup=2):
+    """float32 legs (the VALU kernel): the single-head workload B1 H1 N256
+    d64 non-causal, graph-timed (a launch-latency case), and B2 H16 N4096
+    d64 non-causal for throughput, against the fp32 vector peak."""
+    import torch
+
+    import synthetic
+
+    out = {}
+    dev = torch.device("cuda:0")
+    for (B, H, N, d, graph) in ((1, 1, 256, 64, True), (2, 16, 4096, 64, False)):
+        q, k, v = (torch.from_numpy(synthetic.full_storage(1, t, B, H, N, d, "f32", threads=16)).to(dev)
+                   for t in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+        call = lambda: fa.fwd(q, k, v, causal=False, scale=scale, out=o, lse=lse)
+        f = attention_flops(B, H, N, d, False)
+        prewarm(call)
+        if graph:
+            ms = graph_ms(call, 100)
+        else:
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                call()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / steps
+        tf = f / (ms * 1e-3) / 1e12
+        out[f"non-causal fp32 fwd B{B} H{H} N{N} d{d}"] = {
+            "ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_of_fp32_peak": round(tf / PEAK_FP32_TFLOPS, 4),
+            "timing": "HIP graph of 100 launches" if graph else "events around 10 launches"}
+        del q, k, v, o, lse
         torch.cuda.empty_cache()
     return out
 
@@ -942,6 +984,7 @@ def main():
             torch.cuda.empty_cache()
         extra.update(time_gqa(fa))
         extra.update(time_f16(fa))
+        extra.update(time_f32(fa))
         extra.update(time_fp8(fa))
         extra.update(time_varlen(fa))
         gqa8 = synthetic.DecodeWorkload(8, "decode bf16 B8 H64 Hkv8 N32768 d128", 8, 64, 8, 32768, 128)
