@@ -30,15 +30,17 @@
 //     (the gfx950 transposing LDS read), so V is stored in LDS as it sits in
 //     HBM;
 //   * exp is the hardware exp2 with scale*log2(e) folded into one FMA.
-// Two kernels:
-//   * d = 32, 96, 256: 4 waves, 128 query rows per workgroup, K/V tiles
-//     staged through registers into padded, double-buffered LDS rows;
-//   * d = 128 and 64 ("duo"): 8 waves (two per SIMD), 256 query rows (128
-//     with two wave groups over the key tiles on small grids, d = 64), K/V
-//     tiles copied HBM -> LDS by LDS-DMA into XOR-swizzled rings, every
-//     MFMA followed by one (d = 128) or two (d = 64) slots of softmax VALU
-//     work; steady tiles skip the row max (fixed reference max with an
-//     overflow check, see below).
+// Two kernels (and an e4m3 variant of each):
+//   * d = 256, and d = 96 on grids of fewer 256-row blocks than CUs: 4
+//     waves, 128 query rows per workgroup, K/V tiles staged through
+//     registers into padded, double-buffered LDS rows;
+//   * d = 32, 64, 96, 128 ("duo"): 8 waves (two per SIMD), 256 query rows
+//     (128 with two wave groups over the key tiles on small grids, d = 32
+//     and 64), K/V tiles copied HBM -> LDS by LDS-DMA into XOR-swizzled
+//     rings (d = 32 and 96 in the LDS rows of d = 64 and 128), the 32
+//     softmax slots of an interval spread one to four per MFMA; steady
+//     tiles skip the row max (fixed reference max with an overflow check,
+//     see below).
 #include <math.h>
 #include <stdlib.h>
 
