@@ -7,9 +7,13 @@
 // (m, l, unnormalised O) per row, one division by l at the end.  It exists
 // for full-precision callers: every product and sum is an fp32 VALU FMA
 // (no reduced-precision matrix path), so results stay within a few fp32
-// ulps of the exact attention.  Four lanes share a query row: each scores
-// 16 of the tile's 64 keys and owns a quarter of the output columns; the
-// probabilities of a row are exchanged through LDS.
+// ulps of the exact attention.  LPR lanes share a query row: each scores
+// 64 / LPR of the tile's 64 keys and owns 1 / LPR of the output columns;
+// the probabilities of a row are exchanged through LDS; a workgroup is 256
+// threads, 256 / LPR query rows.  LPR = 4 (64-row blocks) on large grids;
+// on grids too small to fill the chip the time is one workgroup's chain of
+// dependent FMAs and LDS reads, and LPR = 16 (16-row blocks; 8 and 32 rows
+// at d = 32 and 96) cuts it by four.
 #include <math.h>
 
 #include "fa_internal.h"
@@ -18,31 +22,36 @@
 namespace fa {
 namespace {
 
-constexpr int kBQ = 64;
+constexpr int kBQ = 64;  // query rows per workgroup on large grids (LPR = 4)
 constexpr int kBK = 64;
-constexpr int kThreads = 256;  // 4 lanes per query row
-constexpr int kKeysPerLane = kBK / 4;
+constexpr int kThreads = 256;
+// Grids of at most this many 64-row blocks run more lanes per row.
+constexpr int kSmallGrid = 256;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int LPR>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restrict__ Qg,
                                                           const float* __restrict__ Kg,
                                                           const float* __restrict__ Vg,
                                                           float* __restrict__ Og,
                                                           float* __restrict__ Lg, int BH, int N,
                                                           int nqb, float c, int group) {
+  constexpr int THREADS = kThreads;
+  constexpr int BQ = kThreads / LPR;  // query rows per workgroup
+  constexpr int KPL = kBK / LPR;  // keys per lane
   constexpr int KP = D + 4;       // padded K row (floats)
   constexpr int PP = kBK + 1;     // padded P row
-  constexpr int DQ = D / 4;       // output columns per lane
+  constexpr int DQ = D / LPR;     // output columns per lane
+  static_assert(DQ % 4 == 0, "whole float4 column groups per lane");
   __shared__ __attribute__((aligned(16))) float Kl[kBK * KP];
   __shared__ __attribute__((aligned(16))) float Vl[kBK * D];
-  __shared__ float Pl[kBQ * PP];
+  __shared__ float Pl[BQ * PP];
 
   const int tid = threadIdx.x;
-  const int row = tid >> 2;
-  const int sub = tid & 3;
+  const int row = tid / LPR;
+  const int sub = tid % LPR;
   int bh, qb;
   map_block(blockIdx.x, BH * nqb, nqb, CAUSAL ? Order::HeavyLast : Order::Plain, &bh, &qb);
-  const int q0 = qb * kBQ;
+  const int q0 = qb * BQ;
   const int qi = q0 + row;
   const size_t head = (size_t)bh * (size_t)N * D;
   const float* Qh = Qg + head;
@@ -68,12 +77,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
   float l_part = 0.f;
 
   int nkt = (N + kBK - 1) / kBK;
-  if (CAUSAL) nkt = min(nkt, (q0 + kBQ - 1) / kBK + 1);
+  if (CAUSAL) nkt = min(nkt, (q0 + BQ - 1) / kBK + 1);
 
   for (int j = 0; j < nkt; ++j) {
     const int kt0 = j * kBK;
     __syncthreads();  // previous tile fully consumed
-    for (int ci = tid; ci < kBK * D / 4; ci += kThreads) {
+    for (int ci = tid; ci < kBK * D / 4; ci += THREADS) {
       const int r = ci / (D / 4);
       const int x = (ci % (D / 4)) * 4;
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
@@ -86,11 +95,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     }
     __syncthreads();
 
-    float s[kKeysPerLane];
+    float s[KPL];
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-      const int key = sub + 4 * i;
+    for (int i = 0; i < KPL; ++i) {
+      const int key = sub + LPR * i;
       const float* kr = Kl + key * KP;
       float acc = 0.f;
 #pragma unroll
@@ -107,18 +116,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
       s[i] = t;
       mx = fmaxf(mx, t);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
+#pragma unroll
+    for (int x = 1; x < LPR; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
       const float p = exp2f(s[i] - m_use);  // masked: 2^-inf = 0
       psum += p;
-      Pl[row * PP + sub + 4 * i] = p;
+      Pl[row * PP + sub + LPR * i] = p;
     }
     l_part = alpha * l_part + psum;
 #pragma unroll
@@ -138,8 +147,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 1);
-  l_tot += __shfl_xor(l_tot, 2);
+  float l_tot = l_part;
+#pragma unroll
+  for (int x = 1; x < LPR; x <<= 1) l_tot += __shfl_xor(l_tot, x);
   if (qi < N) {
     float* orow = Og + head + (size_t)qi * D + sub * DQ;
 #pragma unroll
@@ -152,8 +162,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
-  const int nqb = (p.N + kBQ - 1) / kBQ;
   const float c = p.scale * 1.44269504088896340736f;
+  // small grids: 16 lanes per row (8 at d = 32 and 96, whose columns
+  // split into float4 groups only eight ways)
+  constexpr int kSmallLpr = D % 64 == 0 ? 16 : 8;
+  const bool small = (int64_t)p.BH * ((p.N + kBQ - 1) / kBQ) <= kSmallGrid;
+  const int bq = small ? kThreads / kSmallLpr : kBQ;
+  const int nqb = (p.N + bq - 1) / bq;
   dim3 grid(p.BH * nqb), block(kThreads);
   const float* q = (const float*)p.q;
   const float* k = (const float*)p.k;
@@ -163,7 +178,8 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   int bh = p.BH, n = p.N;
   int group = p.group;
   void* args[] = {&q, &k, &v, &o, &lse, &bh, &n, (void*)&nqb, (void*)&c, &group};
-  return hipLaunchKernel((const void*)fwd_f32_kernel<D, CAUSAL>, grid, block, args, 0, stream);
+  const void* fn = small ? (const void*)fwd_f32_kernel<D, CAUSAL, kSmallLpr> : (const void*)fwd_f32_kernel<D, CAUSAL, 4>;
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace

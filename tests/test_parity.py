@@ -256,6 +256,17 @@ def test_ragged_fp32(fa, n, d, causal):
     assert_close(run_case(fa, cid, 1, 2, n, d, "f32", causal), "f32")
 
 
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_large_grid(fa, d, causal):
+    """B2 H16 N1000 fp32 (512 blocks of 64 rows, above the small-grid limit
+    of the fp32 kernel, so four lanes per row; the ragged cases above run
+    its small-grid form with 8 or 16 lanes per row); 3 seeded heads."""
+    cid = 3500 + d + causal
+    assert_close(run_case(fa, cid, 2, 16, 1000, d, "f32", causal, heads=synthetic.sample_heads(cid, 2, 16, 3)),
+                 "f32")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [-0.2, 0.9, 3.0])
 def test_other_scales(fa, dtype, scale):
