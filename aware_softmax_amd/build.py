@@ -34,6 +34,9 @@ SOURCES = ["fa_api.hip", "fa_fwd_mfma.hip", "fa_fwd_f32.hip", "fa_bwd_mfma.hip",
 SOURCE_FLAGS = {
     "fa_fwd_mfma.hip": ["-fno-honor-nans"],
     "fa_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    # fp32 matrix-core forward: accumulators in VGPRs, where the softmax
+    # reads them (no accumulator-register copies per tile).
+    "fa_fwd_f32.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = "gfx950"
 

@@ -44,7 +44,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
-PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 256 FLOP/clk x 2.4 GHz
+PEAK_FP32_TFLOPS = 157.3  # MI355X fp32 (matrix and vector alike): 256 CU x 256 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "aware_softmax_amd", "csrc", "fa_fwd_mfma.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_B8H32N8192d128_counters.txt")
@@ -288,9 +288,10 @@ def time_gqa(fa, steps=10, warmup=2):
 
 
 def time_f32(fa, steps=10, warmup=2):
-    """float32 legs (the VALU kernel): the single-head workload B1 H1 N256
-    d64 non-causal, graph-timed (a launch-latency case), and B2 H16 N4096
-    d64 non-causal for throughput, against the fp32 vector peak."""
+    """float32 legs: the single-head workload B1 H1 N256 d64 non-causal
+    (the small-grid VALU kernel), graph-timed (a launch-latency case), and
+    B2 H16 N4096 d64 non-causal (the fp32 matrix-core kernel) for
+    throughput, against the fp32 peak."""
     import torch
 
     import synthetic
