@@ -170,7 +170,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 // the softmax and the matrix unit reuses each operand 32 times (the VALU
 // kernel reads one LDS value per FMA and is bound by that).
 //   * 4 waves, 128 query rows (32 per wave), 64-key tiles of K and V in
-//     double-buffered LDS, loaded through registers one tile ahead;
+//     one LDS buffer, loaded into registers one tile ahead and stored
+//     between two barriers; the small LDS footprint lets two workgroups
+//     share a CU (two waves per SIMD);
 //   * S^T = K Q^T (keys x the wave's queries) in two 32-key halves: MFMA
 //     step s takes, in lane half h, dimension (D/2) h + s of the key row
 //     (A) and of the lane's query row (B), so a lane reads four steps of
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 typedef float f32x16m __attribute__((ext_vector_type(16)));
 
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1))) void fwd_f32_mfma_kernel(const float* __restrict__ Qg,
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void fwd_f32_mfma_kernel(const float* __restrict__ Qg,
                                                           const float* __restrict__ Kg,
                                                           const float* __restrict__ Vg, float* __restrict__ Og,
                                                           float* __restrict__ Lg, int BH, int N, int nqb, float c,
@@ -197,8 +199,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   constexpr int HALF = D / 2;
   constexpr int DB = D / 32;
   constexpr int LPT = kBK * D / 4 / 256;  // float4 loads per thread and tensor
-  __shared__ __attribute__((aligned(16))) float Ks[2][kBK * KS];
-  __shared__ __attribute__((aligned(16))) float Vs[2][kBK * VS];
+  __shared__ __attribute__((aligned(16))) float Ks[1][kBK * KS];  // one buffer: 2 workgroups per CU
+  __shared__ __attribute__((aligned(16))) float Vs[1][kBK * VS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,7 +274,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
   }
   __syncthreads();
   for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
+    const int buf = 0;
     if (j + 1 < nkt) gload(j + 1);
     if (j < wave_nt) {
       const int kt0 = j * kBK;
@@ -344,7 +346,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
                                                           0, 0);
         }
     }
-    if (j + 1 < nkt) lstore(buf ^ 1);
+    if (j + 1 < nkt) {
+      __syncthreads();  // every wave is done with tile j
+      lstore(0);
+    }
     __syncthreads();
   }
 
