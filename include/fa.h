@@ -166,11 +166,11 @@ const char* fa_status_string(fa_status_t status);
  * fa_fwd_tile -- the tile configuration fa_fwd uses for (d, dtype):
  * query rows per workgroup, keys per streamed tile and wavefronts per
  * workgroup, as launched on large grids (16-bit: 256 rows and 8 waves for
- * d = 32 to 128, 128 rows and 8 waves at d = 256; fp32: 64 rows, 4
+ * d = 32 to 128, 128 rows and 8 waves at d = 256; fp32: 128 rows, 4
  * waves).  On small grids (at most 1024 workgroups of 128 rows) d <= 96
  * runs two wave groups splitting the keys of each 128-row block (8 waves;
  * at d = 96 only where 256-row blocks would leave compute units idle), and
- * fp32 grids of at most 256 blocks run 16- or 32-row blocks.
+ * fp32 grids of at most 256 blocks of 64 rows run 16- or 32-row blocks.
  * Host-only; makes no HIP call.  Returns FA_OK or
  * FA_ERR_NULL / FA_ERR_DTYPE / FA_ERR_UNSUPPORTED_HEADDIM.
  */
