@@ -187,8 +187,16 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(const float* __restri
 //     on distinct banks.
 typedef float f32x16m __attribute__((ext_vector_type(16)));
 
+// Waves per SIMD: two (four at d = 32, whose registers allow it: +6 % on B2
+// H16 N4096; three at d = 64 lost 5 %).
+template <int D>
+constexpr int f32_mfma_waves() {
+  return D <= 32 ? 4 : 2;
+}
+
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2))) void fwd_f32_mfma_kernel(const float* __restrict__ Qg,
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(f32_mfma_waves<D>(), f32_mfma_waves<D>()))) void fwd_f32_mfma_kernel(const float* __restrict__ Qg,
                                                           const float* __restrict__ Kg,
                                                           const float* __restrict__ Vg, float* __restrict__ Og,
                                                           float* __restrict__ Lg, int BH, int N, int nqb, float c,
