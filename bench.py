@@ -387,7 +387,7 @@ def time_f16(fa, steps=10, warmup=2):
     return out
 
 
-def time_fp8(fa, steps=10, warmup=3):
+def time_fp8(fa, steps=10, warmup=3, shapes=((8, 32, 8192, 128), (2, 16, 4096, 128))):
     """fa_fwd_fp8 (e4m3 inputs, bf16 output) on B8 H32 N8192 d128 and
     B2 H16 N4096 d128 causal; FLOPs counted as for the bf16 forward."""
     import numpy as np
@@ -396,7 +396,7 @@ def time_fp8(fa, steps=10, warmup=3):
     import synthetic
 
     out = {}
-    for (B, H, N, d) in ((8, 32, 8192, 128), (2, 16, 4096, 128)):
+    for (B, H, N, d) in shapes:
         w = synthetic.Workload(3, "", B, H, N, d, "e4m3", True)
         q, k, v = (torch.from_numpy(synthetic.full_storage(w.config_id, t, B, H, N, d, "e4m3", threads=16)).cuda()
                    for t in ("q", "k", "v"))
@@ -535,8 +535,8 @@ def time_default_legs(fa):
     leg, outside its timed region): causal bf16 forward on B1 H16 N2048 d64,
     B8 H32 N8192 d64, B1 H16 N32768 d128 (batch-1 long context) and B2 H16
     N4096 d128, the
-    backward of the last and of B2 H8 N4096 d256, and split-K decode on B8
-    H32 N32768 d128.  Inputs are the seeded workloads of the parity tests
+    backward of the last and of B2 H8 N4096 d256, split-K decode on B8
+    H32 N32768 d128, and the e4m3 forward on B8 H32 N8192 d128.  Inputs are the seeded workloads of the parity tests
     (the d256 one drawn the same way); each leg frees its tensors."""
     import dataclasses
 
@@ -586,6 +586,9 @@ def time_default_legs(fa):
     legs[f"{dw.name} split-K"] = time_decode(fa, dw, dq_, dk_, dv_, 0, 50, 200)
     del dq_, dk_, dv_
     torch.cuda.empty_cache()
+    # the e4m3 forward on the headline shape (its B2 H16 N4096 leg and the
+    # fp32 legs run under --extra)
+    legs.update(time_fp8(fa, shapes=((8, 32, 8192, 128),)))
     return legs
 
 
